@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""FP32 GEMM throughput on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config c4_4096] [--algo auto]
+
+A step is one call of the C ABI (``sgemm_f32``) over the whole workload, inputs
+already resident in HBM.  The default workload is 4096x4096x4096, C = A*B,
+alpha=1, beta=0, A and B uniform[-1,1) from seed 3.  W untimed warm-up calls,
+then exactly K timed calls bracketed by device synchronisation; the JSON line
+on stdout carries the throughput, the dominant kernel's roofline position
+(its own average duration measured with events on the launch stream) and the
+FP64 CPU oracle's rate on a bounded sample of the same workload.
+
+Other modes:
+  --copy-calibration   run a plain device copy of known size (for scaling the
+                       FETCH_SIZE / WRITE_SIZE counters) and exit.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP32_MFMA_PEAK_TFLOPS = 157.3   # 256 CU x 256 FLOP/clk x 2.4 GHz
+FP32_VALU_PEAK_TFLOPS = 78.6    # non-packed vector FMA
+HBM_PEAK_GBS = 8000.0
+METRIC = "FP32 GEMM TFLOP/s at 4096³ (and % of MI355X FP32 peak), 1 GPU"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mfma_c4_4096.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "fp32_gemm_08_amd", "csrc", f) for f in ("k_mfma.hip", "sgemm_internal.h")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source (else None)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE, encoding="utf-8"):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(nbytes=1 << 30, reps=5):
+    import torch
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {reps} copies of {nbytes} bytes ({nbytes // 1024} KiB read and written each)")
+
+
+def cpu_baseline(case, D_gpu_host, target_s):
+    """Time the FP64 oracle on a bounded sample of the same workload (whole
+    output rows), and check those rows of the GPU result against it."""
+    import numpy as np
+
+    import oracle
+    M, N, K = case.M, case.N, case.K
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(12345)
+    # calibrate with one row per thread
+    rows = np.sort(rng.choice(M, size=min(M, threads), replace=False))
+    t0 = time.perf_counter()
+    oracle.gemm_rows(M, N, K, case.alpha, case.A, case.B, case.trans_b, case.beta, case.C, rows=rows,
+                     nthreads=threads)
+    t_cal = time.perf_counter() - t0
+    per_row = t_cal / len(rows) * threads  # single-row cost on one thread
+    n_rows = int(max(threads, min(M, round(target_s * threads / max(per_row, 1e-9)))))
+    n_rows = max(threads, (n_rows // threads) * threads)
+    n_rows = min(n_rows, M)
+    rows = np.sort(rng.choice(M, size=n_rows, replace=False))
+    t0 = time.perf_counter()
+    D, S, used = oracle.gemm_rows(M, N, K, case.alpha, case.A, case.B, case.trans_b, case.beta, case.C,
+                                  rows=rows, nthreads=threads)
+    t = time.perf_counter() - t0
+    chk = oracle.check(D_gpu_host[rows, :N], D, S, K)
+    flops = 2.0 * n_rows * N * K
+    return {
+        "value": flops / t / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(used),
+        "kind": "oracle",
+        "sample": f"{n_rows} of {M} output rows (all {N} columns, K={K}) of the same product, "
+                  f"FP64 triple loop with the |a*b| sum, {t:.1f} s",
+        "seconds": t,
+        "sample_parity": {"ok": bool(chk["ok"]), "max_rho": chk["max_rho"], "rows": int(n_rows)},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c4_4096")
+    ap.add_argument("--algo", default="auto")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the GEMM shards by output rows; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import fp32_gemm_08_amd as lib
+    from fp32_gemm_08_amd.inputs import CONFIGS, make_config
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    log(f"bench: config={args.config} algo={args.algo} steps={args.steps} warmup={args.warmup}")
+    case = make_config(args.config)
+    M, N, K = case.M, case.N, case.K
+    dA = torch.from_numpy(case.A).to(dev)
+    dB = torch.from_numpy(case.B).to(dev)
+    dC = torch.from_numpy(case.C.copy()).to(dev) if case.C is not None else \
+        torch.zeros((M, case.ldc), dtype=torch.float32, device=dev)
+    C0 = dC.clone() if case.C is not None else None
+    algo = lib.ALGO[args.algo]
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    pa, pb, pc = dA.data_ptr(), dB.data_ptr(), dC.data_ptr()
+    st, kid, tm, tn, kname = lib.sgemm_f32_plan(algo, M, N, K, case.alpha, pa, case.lda, pb, case.ldb,
+                                                int(case.trans_b), case.beta, pc, case.ldc)
+    if st != 0:
+        raise SystemExit(f"plan failed: {lib.sgemm_f32_status_string(st)}")
+
+    def step():
+        s = lib.sgemm_f32_algo(algo, M, N, K, case.alpha, pa, case.lda, pb, case.ldb, int(case.trans_b),
+                               case.beta, pc, case.ldc, sp)
+        if s != 0:
+            raise RuntimeError(lib.sgemm_f32_status_string(s))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K_steps = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K_steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K_steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = [a.elapsed_time(b) * 1e-3 for a, b in ev]
+    span = ev[0][0].elapsed_time(ev[-1][1]) * 1e-3
+    flop = 2.0 * M * N * K
+    value = K_steps * flop / wall / 1e12
+    kern_avg = sum(durs) / len(durs)
+    achieved = flop / kern_avg / 1e12
+    mfma = kid in (40, 41, 42)
+    peak = FP32_MFMA_PEAK_TFLOPS if mfma else FP32_VALU_PEAK_TFLOPS
+    log(f"kernel {kname}: avg {kern_avg * 1e3:.4f} ms, min {min(durs) * 1e3:.4f} ms, "
+        f"event span {span * 1e3:.3f} ms, wall {wall * 1e3:.3f} ms")
+
+    # output for the sample check (beta != 0 workloads accumulate across steps:
+    # rerun once from the original C for the check)
+    if C0 is not None:
+        dC.copy_(C0)
+        step()
+        torch.cuda.synchronize()
+    D_host = dC.cpu().numpy()
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / K_steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "strong",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "pct_of_peak": round(100.0 * value / FP32_MFMA_PEAK_TFLOPS, 2),
+        "config": {
+            "workload": f"sgemm {M}x{N}x{K} row-major, D=alpha*A*{'B^T' if case.trans_b else 'B'}+beta*C, "
+                        f"alpha={case.alpha:g}, beta={case.beta:g}, {case.meta['dist']} inputs, "
+                        f"seed {case.meta['seed']}",
+            "name": args.config, "M": M, "N": N, "K": K, "trans_b": case.trans_b,
+            "lda": case.lda, "ldb": case.ldb, "ldc": case.ldc,
+            "algo": args.algo, "kernel": kname, "workgroups": tm * tn,
+        },
+        "roofline": {
+            "bound": "mfma" if mfma else "alu",
+            "achieved": round(achieved, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": None,
+            "kernel_avg_ms": round(kern_avg * 1e3, 4),
+            "algorithmic_flop_per_launch": flop,
+        },
+        "cpu_baseline": None,
+    }
+    traffic = read_traffic() if (args.config == "c4_4096" and kid == 40) else None
+    out["roofline"]["traffic"] = traffic
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on a sample of rows for ~{args.cpu_seconds:.0f} s")
+        out["cpu_baseline"] = cpu_baseline(case, D_host, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

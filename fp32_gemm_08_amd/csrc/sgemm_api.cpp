@@ -1,0 +1,240 @@
+// C-ABI entry points: argument validation, quick returns, kernel choice, launch.
+// Validation and planning touch no HIP API, so every error below the device
+// check is reported identically with or without a GPU.
+#include "sgemm_f32.h"
+#include "sgemm_internal.h"
+
+#include <atomic>
+#include <cstdio>
+#include <cstring>
+#include <limits>
+
+namespace sgemm {
+namespace {
+
+constexpr int64_t kMaxDim = std::numeric_limits<int32_t>::max();
+constexpr int kMaxDevices = 64;
+
+struct Plan {
+    int status = SGEMM_OK;
+    int kid = KID_NONE;
+    bool transB = false;
+    bool vec = false;
+    int64_t tiles_m = 0, tiles_n = 0;
+};
+
+// Bytes spanned by a rows x cols row-major matrix with leading dimension ld,
+// or -1 if that does not fit comfortably in int64.
+int64_t span_bytes(int64_t rows, int64_t cols, int64_t ld)
+{
+    if (rows <= 0 || cols <= 0)
+        return 0;
+    const int64_t lim = std::numeric_limits<int64_t>::max() / 8;
+    if (ld > lim / rows)
+        return -1;
+    return ((rows - 1) * ld + cols) * (int64_t)sizeof(float);
+}
+
+bool overlaps(const void *p, int64_t pb, const void *q, int64_t qb)
+{
+    if (pb <= 0 || qb <= 0)
+        return false;
+    const uintptr_t p0 = reinterpret_cast<uintptr_t>(p), q0 = reinterpret_cast<uintptr_t>(q);
+    return p0 < q0 + (uintptr_t)qb && q0 < p0 + (uintptr_t)pb;
+}
+
+bool aligned16(const void *p, int64_t ld) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0 && (ld & 3) == 0; }
+
+// Largest MFMA tile that still gives every CU a workgroup; the smallest tile otherwise.
+int choose_mfma(int64_t M, int64_t N)
+{
+    const int kids[3] = {KID_MFMA_L, KID_MFMA_M, KID_MFMA_S};
+    for (int kid : kids) {
+        const TileShape t = tile_shape(kid);
+        if (ceil_div(M, t.bm) * ceil_div(N, t.bn) >= 256)
+            return kid;
+    }
+    return KID_MFMA_S;
+}
+
+Plan make_plan(int algo, int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
+               const float *B, int64_t ldb, int transB, float beta, const float *C, int64_t ldc)
+{
+    Plan p;
+    auto fail = [&](int s) {
+        p.status = s;
+        p.kid = KID_NONE;
+        return p;
+    };
+    if (algo < SGEMM_ALGO_AUTO || algo > SGEMM_ALGO_LDS_TILED_NOPAD)
+        return fail(SGEMM_ERR_INVALID_VALUE);
+    if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+        return fail(SGEMM_ERR_INVALID_VALUE);
+    if (transB != 0 && transB != 1)
+        return fail(SGEMM_ERR_INVALID_VALUE);
+    p.transB = transB == 1;
+    const int64_t b_rows = p.transB ? N : K, b_cols = p.transB ? K : N;
+    if (lda < (K > 1 ? K : 1) || ldb < (b_cols > 1 ? b_cols : 1) || ldc < (N > 1 ? N : 1))
+        return fail(SGEMM_ERR_INVALID_VALUE);
+    const int64_t a_bytes = span_bytes(M, K, lda);
+    const int64_t b_bytes = span_bytes(b_rows, b_cols, ldb);
+    const int64_t c_bytes = span_bytes(M, N, ldc);
+    if (a_bytes < 0 || b_bytes < 0 || c_bytes < 0)
+        return fail(SGEMM_ERR_INVALID_VALUE);
+    if (M == 0 || N == 0)
+        return p;  // nothing to do
+    if (C == nullptr)
+        return fail(SGEMM_ERR_INVALID_VALUE);
+    const bool product = alpha != 0.0f && K > 0;
+    if (!product) {
+        if (beta == 1.0f)
+            return p;  // C is already the result
+        p.kid = KID_SCALE;
+        p.tiles_m = M;
+        p.tiles_n = ceil_div(N, 256);
+        return p;
+    }
+    if (A == nullptr || B == nullptr)
+        return fail(SGEMM_ERR_INVALID_VALUE);
+    if (overlaps(C, c_bytes, A, a_bytes) || overlaps(C, c_bytes, B, b_bytes))
+        return fail(SGEMM_ERR_ALIAS);
+    p.vec = aligned16(A, lda) && aligned16(B, ldb);
+    switch (algo) {
+    case SGEMM_ALGO_NAIVE: p.kid = KID_NAIVE; break;
+    case SGEMM_ALGO_LDS_TILED: p.kid = KID_TILED_PAD; break;
+    case SGEMM_ALGO_LDS_TILED_NOPAD: p.kid = KID_TILED_NOPAD; break;
+    case SGEMM_ALGO_REGBLOCK: p.kid = KID_REGBLOCK; break;
+    case SGEMM_ALGO_MFMA:
+    case SGEMM_ALGO_AUTO: p.kid = choose_mfma(M, N); break;
+    }
+    const TileShape t = tile_shape(p.kid);
+    p.tiles_m = ceil_div(M, t.bm);
+    p.tiles_n = ceil_div(N, t.bn);
+    if (p.tiles_m * p.tiles_n > (int64_t)std::numeric_limits<int32_t>::max())
+        return fail(SGEMM_ERR_INVALID_VALUE);
+    return p;
+}
+
+const char *kernel_label(int kid)
+{
+    switch (kid) {
+    case KID_NONE: return "none";
+    case KID_SCALE: return "scale";
+    case KID_NAIVE: return "naive";
+    case KID_TILED_PAD: return "lds_tiled_16x16_pad1";
+    case KID_TILED_NOPAD: return "lds_tiled_16x16_pad0";
+    case KID_REGBLOCK: return "regblock_128x128x8_t8x8";
+    case KID_MFMA_L: return "mfma_128x256x16_w2x2";
+    case KID_MFMA_M: return "mfma_128x128x16_w2x2";
+    case KID_MFMA_S: return "mfma_64x64x32_w2x2";
+    default: return "unknown";
+    }
+}
+
+// 0 = unknown, 1 = gfx950, 2 = other architecture.
+std::atomic<int> g_arch[kMaxDevices];
+
+int check_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return SGEMM_ERR_NO_DEVICE;
+    if (dev >= kMaxDevices)
+        return SGEMM_ERR_UNSUPPORTED_ARCH;
+    int st = g_arch[dev].load(std::memory_order_acquire);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return SGEMM_ERR_NO_DEVICE;
+        st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_arch[dev].store(st, std::memory_order_release);
+    }
+    return st == 1 ? SGEMM_OK : SGEMM_ERR_UNSUPPORTED_ARCH;
+}
+
+int run(int algo, int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
+        const float *B, int64_t ldb, int transB, float beta, float *C, int64_t ldc, void *stream)
+{
+    const Plan p = make_plan(algo, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc);
+    if (p.status != SGEMM_OK || p.kid == KID_NONE)
+        return p.status;
+    const int dev_status = check_device();
+    if (dev_status != SGEMM_OK)
+        return dev_status;
+    GemmArgs a;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.lda = lda;
+    a.ldb = ldb;
+    a.ldc = ldc;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.alpha = alpha;
+    a.beta = beta;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    (void)hipGetLastError();  // report this launch's status, not an older one
+    hipError_t e;
+    switch (p.kid) {
+    case KID_SCALE: e = launch_scale(a, s); break;
+    case KID_NAIVE: e = launch_naive(a, p.transB, s); break;
+    case KID_TILED_PAD: e = launch_tiled(a, p.transB, true, s); break;
+    case KID_TILED_NOPAD: e = launch_tiled(a, p.transB, false, s); break;
+    case KID_REGBLOCK: e = launch_regblock(a, p.transB, p.vec, s); break;
+    default: e = launch_mfma(a, p.kid, p.transB, p.vec, s); break;
+    }
+    return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
+}
+
+}  // namespace
+}  // namespace sgemm
+
+extern "C" {
+
+int sgemm_f32(int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda, const float *B,
+              int64_t ldb, int transB, float beta, float *C, int64_t ldc, void *stream)
+{
+    return sgemm::run(SGEMM_ALGO_AUTO, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, stream);
+}
+
+int sgemm_f32_algo(int algo, int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
+                   const float *B, int64_t ldb, int transB, float beta, float *C, int64_t ldc, void *stream)
+{
+    return sgemm::run(algo, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, stream);
+}
+
+int sgemm_f32_plan(int algo, int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
+                   const float *B, int64_t ldb, int transB, float beta, const float *C, int64_t ldc,
+                   int *kernel_id, int64_t *tiles_m, int64_t *tiles_n, char *name, int name_len)
+{
+    const sgemm::Plan p = sgemm::make_plan(algo, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc);
+    if (kernel_id)
+        *kernel_id = p.kid;
+    if (tiles_m)
+        *tiles_m = p.kid == sgemm::KID_NONE ? 0 : p.tiles_m;
+    if (tiles_n)
+        *tiles_n = p.kid == sgemm::KID_NONE ? 0 : p.tiles_n;
+    if (name && name_len > 0) {
+        std::snprintf(name, (size_t)name_len, "%s transB=%d vec=%d", sgemm::kernel_label(p.kid),
+                      p.transB ? 1 : 0, p.vec ? 1 : 0);
+    }
+    return p.status;
+}
+
+const char *sgemm_f32_status_string(int status)
+{
+    switch (status) {
+    case SGEMM_OK: return "SGEMM_OK";
+    case SGEMM_ERR_INVALID_VALUE: return "SGEMM_ERR_INVALID_VALUE: invalid argument";
+    case SGEMM_ERR_ALIAS: return "SGEMM_ERR_ALIAS: C overlaps A or B";
+    case SGEMM_ERR_NO_DEVICE: return "SGEMM_ERR_NO_DEVICE: no HIP device is current";
+    case SGEMM_ERR_UNSUPPORTED_ARCH: return "SGEMM_ERR_UNSUPPORTED_ARCH: device is not gfx950";
+    case SGEMM_ERR_LAUNCH: return "SGEMM_ERR_LAUNCH: kernel launch failed";
+    default: return "SGEMM: unknown status";
+    }
+}
+
+const char *sgemm_f32_version(void) { return "sgemm_f32 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,49 @@
+// Internal declarations shared by the host dispatcher and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sgemm {
+
+// Problem description handed to every kernel by value (kernel arguments).
+// Dimensions are validated to fit in int32; offsets are formed in int64.
+struct GemmArgs {
+    const float *A;
+    const float *B;
+    float *C;
+    int64_t lda, ldb, ldc;
+    int M, N, K;
+    float alpha, beta;
+};
+
+// Kernel identifiers reported by the planning query.
+enum KernelId : int {
+    KID_NONE = 0,
+    KID_SCALE = 1,          // C <- beta*C (alpha == 0 or K == 0)
+    KID_NAIVE = 10,
+    KID_TILED_PAD = 20,
+    KID_TILED_NOPAD = 21,
+    KID_REGBLOCK = 30,
+    KID_MFMA_L = 40,        // 128 x 256 macro tile
+    KID_MFMA_M = 41,        // 128 x 128
+    KID_MFMA_S = 42,        // 64 x 64
+};
+
+// Tile geometry of each kernel (rows x cols of C per workgroup).
+struct TileShape {
+    int bm, bn;
+};
+TileShape tile_shape(int kid);
+
+// Launchers: enqueue one kernel on `stream`, return hipGetLastError().
+hipError_t launch_scale(const GemmArgs &a, hipStream_t stream);
+hipError_t launch_naive(const GemmArgs &a, bool transB, hipStream_t stream);
+hipError_t launch_tiled(const GemmArgs &a, bool transB, bool pad, hipStream_t stream);
+hipError_t launch_regblock(const GemmArgs &a, bool transB, bool vec, hipStream_t stream);
+hipError_t launch_mfma(const GemmArgs &a, int kid, bool transB, bool vec, hipStream_t stream);
+
+// Number of workgroup tiles along one dimension.
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace sgemm

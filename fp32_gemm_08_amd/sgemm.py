@@ -1,0 +1,139 @@
+"""ctypes binding for libsgemm_f32.so (argument marshalling only).
+
+The entry points keep the C names and arguments of ``include/sgemm_f32.h``;
+pointers are plain integers (device addresses) and ``stream`` is a hipStream_t
+as an integer (0 = null stream).  ``gemm`` is a convenience wrapper over torch
+tensors that derives the leading dimensions and the current stream; torch is
+used for device memory and streams only, every FLOP runs in the HIP kernels.
+
+There is no fallback: if the library is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsgemm_f32.so")
+
+SGEMM_OK = 0
+SGEMM_ERR_INVALID_VALUE = 1
+SGEMM_ERR_ALIAS = 2
+SGEMM_ERR_NO_DEVICE = 3
+SGEMM_ERR_UNSUPPORTED_ARCH = 4
+SGEMM_ERR_LAUNCH = 5
+
+ALGO = {"auto": 0, "naive": 1, "lds_tiled": 2, "regblock": 3, "mfma": 4, "lds_tiled_nopad": 5}
+
+# Symbols declared in include/sgemm_f32.h.
+EXPORTS = ("sgemm_f32", "sgemm_f32_algo", "sgemm_f32_plan", "sgemm_f32_status_string",
+           "sgemm_f32_version")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class SgemmError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def load():
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m fp32_gemm_08_amd.build` "
+                               "(or __graft_entry__.build()) first")
+        lib = ctypes.CDLL(LIB_PATH)
+        i64, f32, vp, ci = ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_int
+        gemm_args = [i64, i64, i64, f32, vp, i64, vp, i64, ci, f32, vp, i64, vp]
+        lib.sgemm_f32.restype = ci
+        lib.sgemm_f32.argtypes = gemm_args
+        lib.sgemm_f32_algo.restype = ci
+        lib.sgemm_f32_algo.argtypes = [ci] + gemm_args
+        lib.sgemm_f32_plan.restype = ci
+        lib.sgemm_f32_plan.argtypes = [ci, i64, i64, i64, f32, vp, i64, vp, i64, ci, f32, vp, i64,
+                                       ctypes.POINTER(ci), ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                       ctypes.c_char_p, ci]
+        lib.sgemm_f32_status_string.restype = ctypes.c_char_p
+        lib.sgemm_f32_status_string.argtypes = [ci]
+        lib.sgemm_f32_version.restype = ctypes.c_char_p
+        lib.sgemm_f32_version.argtypes = []
+        _lib = lib
+        return lib
+
+
+def sgemm_f32(M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, stream=0) -> int:
+    """C <- alpha*A*op(B) + beta*C (AUTO algorithm).  Returns the status code."""
+    return load().sgemm_f32(M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, stream)
+
+
+def sgemm_f32_algo(algo, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, stream=0) -> int:
+    """Same operation with an explicit algorithm id.  Returns the status code."""
+    return load().sgemm_f32_algo(algo, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, stream)
+
+
+def sgemm_f32_plan(algo, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc):
+    """Host-only planning query: (status, kernel_id, tiles_m, tiles_n, name)."""
+    kid = ctypes.c_int(0)
+    tm = ctypes.c_int64(0)
+    tn = ctypes.c_int64(0)
+    buf = ctypes.create_string_buffer(128)
+    st = load().sgemm_f32_plan(algo, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc,
+                               ctypes.byref(kid), ctypes.byref(tm), ctypes.byref(tn), buf, 128)
+    return st, kid.value, tm.value, tn.value, buf.value.decode()
+
+
+def sgemm_f32_status_string(status: int) -> str:
+    return load().sgemm_f32_status_string(status).decode()
+
+
+def sgemm_f32_version() -> str:
+    return load().sgemm_f32_version().decode()
+
+
+def _check(status):
+    if status != SGEMM_OK:
+        raise SgemmError(status, sgemm_f32_status_string(status))
+
+
+def _algo_id(algo):
+    if isinstance(algo, str):
+        return ALGO[algo]
+    return int(algo)
+
+
+def gemm(A, B, C, alpha=1.0, beta=0.0, trans_b=False, algo="auto", stream=None):
+    """C <- alpha*A*op(B) + beta*C on torch float32 CUDA tensors, in place; returns C.
+
+    A is (M, K), B is (K, N) or, with trans_b, (N, K); C is (M, N).  Each may be a
+    row-strided view (last-dimension stride 1); its row stride is the leading
+    dimension.  Runs on ``stream`` (a torch stream) or torch's current stream.
+    """
+    import torch  # plumbing only: device memory and streams
+
+    for name, t in (("A", A), ("B", B), ("C", C)):
+        if t.dtype != torch.float32 or not t.is_cuda or t.dim() != 2:
+            raise TypeError(f"{name} must be a 2-D float32 device tensor")
+        if t.shape[1] > 1 and t.stride(1) != 1:
+            raise ValueError(f"{name} must have unit stride along its last dimension")
+        if t.shape[0] > 1 and t.stride(0) < t.shape[1]:
+            raise ValueError(f"{name} rows overlap (row stride below the row length)")
+    M, K = A.shape
+    N = B.shape[0] if trans_b else B.shape[1]
+    if (B.shape[1] if trans_b else B.shape[0]) != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)} "
+                         f"(trans_b={trans_b}), C {tuple(C.shape)}")
+    def ld(t):
+        return max(t.stride(0) if t.shape[0] > 1 else t.shape[1], t.shape[1], 1)
+
+    s = (stream if stream is not None else torch.cuda.current_stream(C.device)).cuda_stream
+    with torch.cuda.device(C.device):
+        st = sgemm_f32_algo(_algo_id(algo), M, N, K, float(alpha), A.data_ptr(), ld(A), B.data_ptr(), ld(B),
+                            int(bool(trans_b)), float(beta), C.data_ptr(), ld(C), s)
+    _check(st)
+    return C

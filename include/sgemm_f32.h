@@ -1,0 +1,141 @@
+/*
+ * sgemm_f32 — FP32 GEMM for AMD Instinct MI355X (gfx950).
+ *
+ *     C  <-  alpha * A * op(B) + beta * C          row-major, FP32, op(B) in {B, B^T}
+ *
+ * The operation is the one defined on the pages this library follows:
+ *   - "CUDA矩阵乘法性能优化实战：从朴素内核到寄存器分块与Nsight剖析", section 1.1:
+ *     C(MxN) = A(MxK) x B(KxN), every C[i][j] a sum of K multiply-adds; section 2.1
+ *     gives the row-major element addressing A[row*K+k], B[k*N+col], C[row*N+col].
+ *   - Baidu Cloud article comparing the naive and 2-D block-tiled CUDA matmul,
+ *     paragraph on the naive mapping: the general form D = alpha*A*B^T + beta*C, in
+ *     which C[i][j] is row i of A dotted with row j of B.
+ * The result D is written in place into C (one C buffer in the interface).
+ *
+ * Layout (row-major, leading dimensions in elements):
+ *   A      M x K,  element (i,k) at A[i*lda + k],  lda >= max(1, K)
+ *   B      transB == 0:  K x N,  op(B)(k,j) = B[k*ldb + j],  ldb >= max(1, N)
+ *          transB == 1:  N x K,  op(B)(k,j) = B[j*ldb + k],  ldb >= max(1, K)
+ *   C      M x N,  element (i,j) at C[i*ldc + j],  ldc >= max(1, N)
+ *
+ * Ownership: A, B and C are DEVICE pointers owned by the caller.  The library
+ * never allocates, frees, copies or synchronises, and uses no workspace.
+ *
+ * Asynchrony: a call validates its arguments on the host, enqueues its kernel on
+ * `stream` (a hipStream_t; NULL means the null stream) and returns.  Faults inside
+ * a kernel surface at the caller's next synchronisation.
+ *
+ * Quick returns and special values (BLAS conventions; the pages are silent):
+ *   - M == 0 or N == 0: nothing is touched, SGEMM_OK.
+ *   - alpha == 0 or K == 0: C <- beta*C and A, B are not read
+ *     (beta == 1: nothing is touched; beta == 0: C <- 0 without reading C).
+ *   - beta == 0: C is not read, so NaN/Inf already in C do not propagate.
+ *
+ * Accuracy: every element satisfies
+ *     |D - D_exact| <= 4*K*2^-24 * sum_k |a(i,k)*b(k,j)| + 1e-6
+ * against the exact result, for |alpha| <= 4 and moderate beta*C; the summation
+ * order is unspecified and may differ between algorithms.
+ *
+ * Errors are returned before any HIP call where possible, so they are testable
+ * without a GPU:
+ *   SGEMM_ERR_INVALID_VALUE   negative or too large (> 2^31-1) dimension, a leading
+ *                             dimension below its minimum, transB not 0/1, a NULL
+ *                             pointer for an operand that would be read or written,
+ *                             or an unknown algorithm id;
+ *   SGEMM_ERR_ALIAS           C's byte range overlaps A's or B's (the kernels rely on
+ *                             the no-alias premise of __restrict__, section 5.3 of the
+ *                             first page); A and B may overlap each other;
+ *   SGEMM_ERR_NO_DEVICE       no HIP device is current;
+ *   SGEMM_ERR_UNSUPPORTED_ARCH the current device is not gfx950 (the code objects
+ *                             hold gfx950 code only; compare the "no kernel image"
+ *                             case of section 6.2 of the first page);
+ *   SGEMM_ERR_LAUNCH          the launch was rejected (hipGetLastError after it).
+ *
+ * Thread safety: calls are reentrant; the only shared state is a per-device
+ * architecture cache filled once.
+ */
+#ifndef SGEMM_F32_H
+#define SGEMM_F32_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SGEMM_OK = 0,
+    SGEMM_ERR_INVALID_VALUE = 1,
+    SGEMM_ERR_ALIAS = 2,
+    SGEMM_ERR_NO_DEVICE = 3,
+    SGEMM_ERR_UNSUPPORTED_ARCH = 4,
+    SGEMM_ERR_LAUNCH = 5
+} sgemm_status;
+
+/*
+ * Algorithms.  Every stage stays available for comparison; all compute the same
+ * operation under the same contract.
+ *   NAIVE            one work-item per output element, operands read from global
+ *                    memory (first page, section 2.1).
+ *   LDS_TILED        16x16 output tile per workgroup, A and B tiles staged through
+ *                    LDS with a +1 padded row (first page, sections 3.2-3.3; second
+ *                    page, section 4.1), zero-filled outside the matrices.
+ *   LDS_TILED_NOPAD  the same kernel without the padding column (second page,
+ *                    section 3.1); kept to measure LDS bank conflicts against it.
+ *   REGBLOCK         128x128 macro tile, 8x8 outputs per work-item held in
+ *                    registers (first page, section 5.2), 128-bit global loads
+ *                    (section 5.3) and double-buffered LDS staging (second page,
+ *                    section 3.2).  Vector FP32 FMA.
+ *   MFMA             CDNA matrix-core path: v_mfma_f32_32x32x2_f32, FP32 inputs and
+ *                    FP32 accumulation, multi-level tiling (second page, section 7.3).
+ *   AUTO             MFMA with a tile chosen from the problem shape.
+ */
+typedef enum {
+    SGEMM_ALGO_AUTO = 0,
+    SGEMM_ALGO_NAIVE = 1,
+    SGEMM_ALGO_LDS_TILED = 2,
+    SGEMM_ALGO_REGBLOCK = 3,
+    SGEMM_ALGO_MFMA = 4,
+    SGEMM_ALGO_LDS_TILED_NOPAD = 5
+} sgemm_algo;
+
+/*
+ * C <- alpha*A*op(B) + beta*C with the AUTO algorithm.
+ * Arguments as described above; `stream` is a hipStream_t (NULL: null stream).
+ * Returns an sgemm_status.
+ */
+int sgemm_f32(int64_t M, int64_t N, int64_t K, float alpha,
+              const float *A, int64_t lda, const float *B, int64_t ldb, int transB,
+              float beta, float *C, int64_t ldc, void *stream);
+
+/* The same operation with an explicit algorithm (an sgemm_algo value). */
+int sgemm_f32_algo(int algo, int64_t M, int64_t N, int64_t K, float alpha,
+                   const float *A, int64_t lda, const float *B, int64_t ldb, int transB,
+                   float beta, float *C, int64_t ldc, void *stream);
+
+/*
+ * Host-only planning query, no HIP call: validates the arguments exactly as
+ * sgemm_f32_algo would (pointers may be any non-NULL values; only their
+ * numeric ranges are compared for aliasing) and reports what would run.
+ *   *kernel_id   receives the launched kernel's id (0 when nothing would launch);
+ *   *tiles_m, *tiles_n receive the workgroup grid (0 when nothing would launch);
+ *   name/name_len receive a NUL-terminated kernel description (may be NULL/0).
+ * Returns the sgemm_status the call would return before touching the device.
+ */
+int sgemm_f32_plan(int algo, int64_t M, int64_t N, int64_t K, float alpha,
+                   const float *A, int64_t lda, const float *B, int64_t ldb, int transB,
+                   float beta, const float *C, int64_t ldc,
+                   int *kernel_id, int64_t *tiles_m, int64_t *tiles_n,
+                   char *name, int name_len);
+
+/* Static, NUL-terminated text for a status code (unknown codes included). */
+const char *sgemm_f32_status_string(int status);
+
+/* Static, NUL-terminated library version string. */
+const char *sgemm_f32_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGEMM_F32_H */

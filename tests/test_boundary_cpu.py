@@ -1,0 +1,177 @@
+"""C-ABI boundary tests that need no GPU.
+
+The library loads without a device; argument validation, quick returns and the
+planning query run on the host before any HIP call, so every status they
+produce is checked here.  No compute call is made.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp32_gemm_08_amd as lib
+from fp32_gemm_08_amd import sgemm as binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sgemm_f32.h")
+
+OK, INVALID, ALIAS = 0, 1, 2
+KID_NONE, KID_SCALE, KID_NAIVE, KID_TILED, KID_TILED_NOPAD, KID_REG = 0, 1, 10, 20, 21, 30
+KID_L, KID_M, KID_S = 40, 41, 42
+
+# Fake, well-separated "device" addresses: planning only compares ranges.
+PA, PB, PC = 1 << 32, 1 << 40, 1 << 44
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    if not os.path.exists(lib.LIB_PATH):
+        pytest.skip("libsgemm_f32.so not built")
+
+
+def header_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sgemm_f32\w*)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    declared = header_functions()
+    assert declared == sorted(binding.EXPORTS)
+    so = ctypes.CDLL(lib.LIB_PATH)
+    for name in declared:
+        assert hasattr(so, name), name
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in lib.sgemm_f32_version()
+    for code in range(6):
+        assert lib.sgemm_f32_status_string(code).startswith("SGEMM_")
+    assert "unknown" in lib.sgemm_f32_status_string(99)
+
+
+def plan(algo=0, M=64, N=64, K=64, alpha=1.0, A=PA, lda=None, B=PB, ldb=None, transB=0, beta=0.0,
+         C=PC, ldc=None):
+    lda = K if lda is None else lda
+    ldb = (K if transB else N) if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    return lib.sgemm_f32_plan(algo, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc)
+
+
+def call(algo=0, M=64, N=64, K=64, alpha=1.0, A=PA, lda=None, B=PB, ldb=None, transB=0, beta=0.0,
+         C=PC, ldc=None):
+    lda = K if lda is None else lda
+    ldb = (K if transB else N) if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    return lib.sgemm_f32_algo(algo, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, 0)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(M=-1), dict(N=-1), dict(K=-1), dict(M=1 << 31), dict(K=1 << 31),
+    dict(transB=2), dict(transB=-1),
+    dict(lda=63), dict(ldb=63), dict(ldc=63), dict(transB=1, ldb=63),
+    dict(A=0), dict(B=0), dict(C=0), dict(algo=6), dict(algo=-1),
+    dict(M=2, K=2, lda=1 << 61),
+])
+def test_invalid_arguments(kw):
+    assert plan(**kw)[0] == INVALID
+    assert call(**kw) == INVALID
+
+
+def test_ld_minimum_is_one_for_empty_rows():
+    # K == 0: lda may be 1; N == 0: ldb/ldc may be 1
+    assert plan(K=0, lda=1, beta=1.0)[0] == OK
+    assert plan(N=0, ldb=1, ldc=1)[0] == OK
+    assert plan(K=0, lda=0)[0] == INVALID
+
+
+@pytest.mark.parametrize("transB", [0, 1])
+def test_alias_detection(transB):
+    M = N = K = 64
+    a_bytes = ((M - 1) * K + K) * 4
+    # C starts inside A
+    assert plan(C=PA + a_bytes - 4, transB=transB)[0] == ALIAS
+    # C ends inside A
+    assert plan(A=PC + 64 * 64 * 4 - 4, transB=transB)[0] == ALIAS
+    # C overlaps B
+    assert plan(B=PC + 128, transB=transB)[0] == ALIAS
+    # adjacent but not overlapping
+    assert plan(C=PA + a_bytes, transB=transB)[0] == OK
+    # A and B may alias each other (both are only read)
+    assert plan(A=PB, transB=transB)[0] == OK
+    assert call(C=PA + 4, transB=transB) == ALIAS
+
+
+def test_quick_returns_touch_nothing():
+    # M == 0 or N == 0: OK, nothing launches, NULL pointers allowed
+    for kw in (dict(M=0, A=0, C=0), dict(N=0, B=0, C=0, ldb=1, ldc=1)):
+        st, kid, tm, tn, _ = plan(**kw)
+        assert (st, kid, tm, tn) == (OK, KID_NONE, 0, 0)
+        assert call(**kw) == OK
+    # alpha == 0 or K == 0 with beta == 1: C is already the result
+    for kw in (dict(alpha=0.0, beta=1.0, A=0, B=0), dict(K=0, lda=1, beta=1.0, A=0, B=0)):
+        st, kid, _, _, _ = plan(**kw)
+        assert (st, kid) == (OK, KID_NONE)
+        assert call(**kw) == OK
+
+
+def test_product_free_cases_scale_c():
+    # alpha == 0 or K == 0 with beta != 1: only C <- beta*C runs, A and B may be NULL
+    for kw in (dict(alpha=0.0, beta=0.0, A=0, B=0), dict(K=0, lda=1, beta=-0.5, A=0, B=0),
+               dict(alpha=0.0, beta=2.0, A=PC + 8)):
+        st, kid, tm, tn, name = plan(**kw)
+        assert (st, kid) == (OK, KID_SCALE), name
+        assert (tm, tn) == (64, 1)
+
+
+@pytest.mark.parametrize("algo,kid", [(1, KID_NAIVE), (2, KID_TILED), (3, KID_REG), (5, KID_TILED_NOPAD)])
+def test_explicit_algorithms(algo, kid):
+    st, k, tm, tn, name = plan(algo=algo, M=1000, N=1017, K=999)
+    assert (st, k) == (OK, kid)
+    if kid == KID_NAIVE:
+        assert (tm, tn) == (250, 16)
+    elif kid in (KID_TILED, KID_TILED_NOPAD):
+        assert (tm, tn) == (63, 64)
+    else:
+        assert (tm, tn) == (8, 8)
+
+
+@pytest.mark.parametrize("shape,kid,tiles", [
+    ((4096, 4096, 4096), KID_L, (32, 16)),
+    ((8192, 8192, 8192), KID_L, (64, 32)),
+    ((16384, 4096, 1024), KID_L, (128, 16)),
+    ((2048, 2048, 2048), KID_M, (16, 16)),
+    ((1024, 1024, 1024), KID_S, (16, 16)),
+    ((1000, 1017, 999), KID_S, (16, 16)),
+    ((512, 512, 512), KID_S, (8, 8)),
+    ((128, 128, 128), KID_S, (2, 2)),
+    ((1, 1, 1), KID_S, (1, 1)),
+])
+def test_auto_tile_choice(shape, kid, tiles):
+    M, N, K = shape
+    for algo in (0, 4):
+        st, k, tm, tn, name = plan(algo=algo, M=M, N=N, K=K)
+        assert (st, k, (tm, tn)) == (OK, kid, tiles), name
+
+
+def test_vector_path_needs_alignment():
+    assert "vec=1" in plan(M=256, N=256, K=256)[4]
+    assert "vec=0" in plan(M=256, N=256, K=255, lda=255)[4]          # lda % 4 != 0
+    assert "vec=0" in plan(M=256, N=256, K=256, A=PA + 4)[4]         # A not 16-byte aligned
+    assert "vec=0" in plan(M=256, N=256, K=256, transB=1, ldb=257)[4]
+    assert "transB=1" in plan(transB=1)[4]
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        binding.sgemm_f32(1, 1, 1, 1.0, 0, 1, 0, 1, 0, 0.0, 0, 1, 0)
+
+
+def test_gemm_wrapper_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    a = torch.zeros(4, 4)
+    with pytest.raises(TypeError):
+        lib.gemm(a, a, a.clone())

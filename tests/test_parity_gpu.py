@@ -1,0 +1,266 @@
+"""GPU parity: every algorithm against the FP64 oracle, through the C ABI.
+
+Bar: |D_gpu - D| <= 4*K*2^-24*S + 1e-6 elementwise (S = sum_k |a*b|), finite;
+bit-exact where the inputs make every summation order exact (small integers).
+Full compares at sizes the oracle finishes in seconds; the large workloads
+(4096^3, 2048^3, 8192^3, 16384x4096x1024) compare sampled rows, which the
+oracle computes one by one, in the same launch configuration the benchmark
+times.
+"""
+import numpy as np
+import pytest
+
+import fp32_gemm_08_amd as lib
+from fp32_gemm_08_amd.inputs import CONFIGS, make_case, make_config
+
+from gpu_helpers import ALGOS, oracle_rows, run_case, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    assert lib.sgemm_f32_version()  # the HIP library must load: no fallback exists
+
+
+_cases = {}
+_oracle = {}
+
+
+def cached_config(name):
+    if name not in _cases:
+        _cases[name] = make_config(name)
+    return _cases[name]
+
+
+def cached_oracle(o, name, rows=None):
+    key = (name, None if rows is None else tuple(rows))
+    if key not in _oracle:
+        _oracle[key] = oracle_rows(o, cached_config(name), rows)
+    return _oracle[key]
+
+
+def assert_parity(Dg, D, S, K, what):
+    r = lib_check(Dg, D, S, K)
+    say(f"{what}: max_abs={r['max_abs']:.3e} max_rho={r['max_rho']:.3f} fails={r['n_fail']}")
+    assert r["ok"], f"{what}: {r}"
+    return r
+
+
+def lib_check(Dg, D, S, K):
+    import oracle
+    return oracle.check(Dg, D, S, K)
+
+
+SMALL = ["c1_128", "c2_1024", "c3_ragged_bt", "c5_512"]
+LARGE = ["c4_4096", "c5_2048", "c5_8192", "c5_tall"]
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("name", SMALL)
+def test_config_full(oracle_lib, name, algo):
+    case = cached_config(name)
+    st, Dg = run_case(case, algo)
+    assert st == 0, lib.sgemm_f32_status_string(st)
+    D, S = cached_oracle(oracle_lib, name)
+    assert_parity(Dg[:, :case.N], D, S, case.K, f"{name}/{algo}")
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("name", LARGE)
+def test_config_sampled(oracle_lib, name, algo):
+    case = cached_config(name)
+    st, Dg = run_case(case, algo, guard=False)
+    assert st == 0, lib.sgemm_f32_status_string(st)
+    rows = sample_rows(case.M, n=16, seed=sum(name.encode()))
+    D, S = cached_oracle(oracle_lib, name, rows)
+    assert_parity(Dg[rows, :case.N], D, S, case.K, f"{name}/{algo} rows")
+
+
+INT_SHAPES = [(128, 128, 128, 0), (1000, 1017, 999, 1), (1000, 1017, 999, 0), (257, 383, 129, 1),
+              (64, 64, 4096, 0), (1, 1, 1, 0), (33, 1, 7, 1), (1, 700, 33, 0)]
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("shape", INT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_small_integers_bit_exact(oracle_lib, shape, algo):
+    """Entries in {-2..2}: every partial sum is an exact integer, so every
+    summation order gives the same FP32 result; alpha=1.5, beta=-0.5 stay exact."""
+    M, N, K, t = shape
+    case = make_case(M, N, K, trans_b=t, alpha=1.5, beta=-0.5, dist="int2", seed=M + N + K)
+    st, Dg = run_case(case, algo)
+    assert st == 0
+    D, _ = oracle_rows(oracle_lib, case)
+    assert np.array_equal(Dg[:, :N], D.astype(np.float32)), f"{shape}/{algo} not bit-exact"
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_integers_bit_exact_at_4096(oracle_lib, algo):
+    case = make_case(4096, 4096, 4096, dist="int2", alpha=1.5, beta=-0.5, seed=77)
+    st, Dg = run_case(case, algo, guard=False)
+    assert st == 0
+    rows = sample_rows(4096, n=8, seed=3)
+    D, _ = oracle_rows(oracle_lib, case, rows)
+    assert np.array_equal(Dg[rows], D.astype(np.float32))
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_beta_zero_ignores_nan_in_c(oracle_lib, algo):
+    case = make_case(300, 260, 129, dist="uniform", seed=5)
+    st, Dg = run_case(case, algo, c_fill=np.nan)
+    assert st == 0 and np.all(np.isfinite(Dg))
+    D, S = oracle_rows(oracle_lib, case)
+    assert_parity(Dg, D, S, 129, f"nan-c/{algo}")
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("t", [0, 1])
+def test_padded_leading_dims_and_guards(oracle_lib, algo, t):
+    """lda/ldb/ldc above the row length; the padding of A and B holds NaN (a
+    stray read poisons the result) and the padding of C holds a canary that
+    must survive."""
+    case = make_case(261, 197, 143, trans_b=t, alpha=-1.25, beta=0.75, dist="normal", seed=11,
+                     lda=160, ldb=(143 if t else 197) + 9, ldc=200)
+    st, Dg = run_case(case, algo, ldc_pad=3)
+    assert st == 0
+    D, S = oracle_rows(oracle_lib, case)
+    assert_parity(Dg[:, :197], D, S, 143, f"padded/{algo}/t{t}")
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_misaligned_base_pointers(oracle_lib, algo):
+    case = make_case(130, 132, 68, dist="uniform", seed=13)
+    st, Dg = run_case(case, algo, a_offset=1, b_offset=3)
+    assert st == 0
+    D, S = oracle_rows(oracle_lib, case)
+    assert_parity(Dg[:, :132], D, S, 68, f"misaligned/{algo}")
+
+
+def _sweep_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        M, N, K = (int(x) for x in rng.integers(1, 701, 3))
+        t = int(rng.integers(0, 2))
+        alpha = float(rng.choice([1.0, -0.5, 1.5, 2.0]))
+        beta = float(rng.choice([0.0, 1.0, -0.5]))
+        out.append((M, N, K, t, alpha, beta, 1000 + i))
+    return out
+
+
+@pytest.mark.parametrize("algo", ["mfma", "regblock", "lds_tiled", "naive"])
+def test_random_ragged_sweep(oracle_lib, algo):
+    """Seeded sweep of ragged shapes in [1, 700]^3, both op(B), random alpha/beta."""
+    for (M, N, K, t, alpha, beta, seed) in _sweep_cases(24 if algo == "mfma" else 8, 42):
+        case = make_case(M, N, K, trans_b=t, alpha=alpha, beta=beta, dist="uniform", seed=seed)
+        st, Dg = run_case(case, algo)
+        assert st == 0
+        D, S = oracle_rows(oracle_lib, case)
+        assert_parity(Dg[:, :N], D, S, K, f"sweep {M}x{N}x{K} t{t}/{algo}")
+
+
+@pytest.mark.parametrize("algo", ["mfma", "regblock", "lds_tiled", "naive"])
+def test_degenerate_shapes(oracle_lib, algo):
+    for (M, N, K, t) in [(1, 1, 1, 0), (1, 1, 1, 1), (1, 513, 1, 0), (513, 1, 2, 1), (31, 33, 1, 0),
+                         (64, 64, 8, 1), (65, 65, 9, 0), (7, 5, 4099, 1)]:
+        case = make_case(M, N, K, trans_b=t, alpha=1.5, beta=-0.5, dist="uniform", seed=M * 7 + K)
+        st, Dg = run_case(case, algo)
+        assert st == 0
+        D, S = oracle_rows(oracle_lib, case)
+        assert_parity(Dg[:, :N], D, S, K, f"degenerate {M}x{N}x{K} t{t}/{algo}")
+
+
+def test_product_free_paths(oracle_lib):
+    """alpha == 0 or K == 0: C <- beta*C; beta == 1 leaves C untouched bitwise;
+    beta == 0 zeroes C without reading it (NaN in C)."""
+    base = make_case(77, 91, 0, beta=-0.5, dist="uniform", seed=3, with_c=True)
+    st, Dg = run_case(base, "auto")
+    assert st == 0
+    assert np.array_equal(Dg[:, :91], (np.float32(-0.5) * base.C[:, :91]))
+    a0 = make_case(77, 91, 33, alpha=0.0, beta=1.0, dist="uniform", seed=4, with_c=True)
+    st, Dg = run_case(a0, "auto")
+    assert st == 0 and np.array_equal(Dg[:, :91].view(np.uint32), a0.C[:, :91].view(np.uint32))
+    z = make_case(77, 91, 33, alpha=0.0, beta=0.0, dist="uniform", seed=4)
+    st, Dg = run_case(z, "auto", c_fill=np.nan)
+    assert st == 0 and np.all(Dg[:, :91] == 0)
+
+
+def test_empty_shapes_touch_nothing():
+    for (M, N, K) in [(0, 5, 3), (5, 0, 3)]:
+        case = make_case(M, N, K, dist="uniform", seed=1, ldc=max(1, N))
+        st, Dg = run_case(case, "auto", c_fill=1.0)
+        assert st == 0
+        assert np.all(Dg[:, :N] == 1.0)
+
+
+@pytest.mark.parametrize("algo", ["mfma", "regblock"])
+def test_deterministic_reruns(algo):
+    case = make_case(1000, 1017, 999, trans_b=True, alpha=1.5, beta=-0.5, dist="uniform", seed=2)
+    _, D0 = run_case(case, algo)
+    for _ in range(3):
+        _, D1 = run_case(case, algo)
+        assert np.array_equal(D0.view(np.uint32), D1.view(np.uint32))
+
+
+def test_transposed_storage_agrees(oracle_lib):
+    """op(B) = B^T on a materialised B^T agrees with op(B) = B (both within the bound)."""
+    case0 = make_case(300, 280, 260, dist="normal", seed=8)
+    case1 = make_case(300, 280, 260, dist="normal", seed=8)
+    case1.B = np.ascontiguousarray(case0.B.T)
+    case1.trans_b = True
+    _, D0 = run_case(case0, "mfma")
+    _, D1 = run_case(case1, "mfma")
+    D, S = oracle_rows(oracle_lib, case0)
+    assert_parity(D0, D, S, 260, "transB=0")
+    assert_parity(D1, D, S, 260, "transB=1")
+
+
+def test_beta_one_accumulates(oracle_lib):
+    """Applying beta=1 twice equals alpha=2 from C=0 (within the bound)."""
+    torch = pytest.importorskip("torch")
+    case = make_case(256, 256, 256, dist="normal", seed=10)
+    dev = torch.device("cuda", 0)
+    A = torch.from_numpy(case.A).to(dev)
+    B = torch.from_numpy(case.B).to(dev)
+    C = torch.zeros(256, 256, device=dev)
+    lib.gemm(A, B, C, alpha=1.0, beta=1.0)
+    lib.gemm(A, B, C, alpha=1.0, beta=1.0)
+    C2 = torch.zeros(256, 256, device=dev)
+    lib.gemm(A, B, C2, alpha=2.0, beta=0.0)
+    D, S, _ = __import__("oracle").gemm_rows(256, 256, 256, 2.0, case.A, case.B, False, 0.0, None)
+    assert_parity(C.cpu().numpy(), D, S, 2 * 256, "beta twice")
+    assert_parity(C2.cpu().numpy(), D, S, 256, "alpha 2")
+
+
+def test_nondefault_stream_and_wrapper(oracle_lib):
+    torch = pytest.importorskip("torch")
+    dev = torch.device("cuda", 0)
+    case = make_case(384, 320, 200, trans_b=True, alpha=0.5, beta=2.0, dist="uniform", seed=6)
+    s = torch.cuda.Stream(device=dev)
+    A = torch.from_numpy(case.A).to(dev)
+    B = torch.from_numpy(case.B).to(dev)
+    C = torch.from_numpy(case.C.copy()).to(dev)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        lib.gemm(A, B, C, alpha=0.5, beta=2.0, trans_b=True)
+    s.synchronize()
+    D, S = oracle_rows(oracle_lib, case)
+    assert_parity(C.cpu().numpy(), D, S, 200, "stream")
+    # a row-strided view: the leading dimension comes from the stride
+    big = torch.from_numpy(np.pad(case.A, ((0, 0), (0, 8)))).to(dev)
+    Cv = torch.from_numpy(case.C.copy()).to(dev)
+    lib.gemm(big[:, :200], B, Cv, alpha=0.5, beta=2.0, trans_b=True)
+    torch.cuda.synchronize()
+    assert_parity(Cv.cpu().numpy(), D, S, 200, "strided view")
+
+
+def test_alias_is_rejected_on_device():
+    torch = pytest.importorskip("torch")
+    dev = torch.device("cuda", 0)
+    X = torch.zeros(64, 64, device=dev)
+    with pytest.raises(lib.SgemmError) as e:
+        lib.gemm(X, X, X)
+    assert e.value.status == 2
