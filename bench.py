@@ -6,7 +6,9 @@
 A step is one call of the C ABI (``sgemm_f32``) over the whole workload, inputs
 already resident in HBM.  The default workload is 4096x4096x4096, C = A*B,
 alpha=1, beta=0, A and B uniform[-1,1) from seed 3.  W untimed warm-up calls,
-then exactly K timed calls bracketed by device synchronisation; the JSON line
+then exactly K timed calls bracketed by device synchronisation (the defaults,
+200 and 100, let the engine clock settle first: the first ~30 calls of a cold
+GPU run measurably slower); the JSON line
 on stdout carries the throughput, the dominant kernel's roofline position
 (its own average duration measured with events on the launch stream) and the
 FP64 CPU oracle's rate on a bounded sample of the same workload.
@@ -25,8 +27,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-FP32_MFMA_PEAK_TFLOPS = 157.3   # 256 CU x 256 FLOP/clk x 2.4 GHz
-FP32_VALU_PEAK_TFLOPS = 78.6    # non-packed vector FMA
+FP32_MFMA_PEAK_TFLOPS = 157.3   # matrix cores: 256 CU x 256 FLOP/clk x 2.4 GHz
+FP32_VALU_PEAK_TFLOPS = 157.3   # vector ALU, same published figure (256 CU x 4 SIMD x 64 FLOP/clk x 2.4 GHz)
 HBM_PEAK_GBS = 8000.0
 METRIC = "FP32 GEMM TFLOP/s at 4096³ (and % of MI355X FP32 peak), 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mfma_c4_4096.txt")
@@ -112,28 +114,85 @@ def cpu_baseline(case, D_gpu_host, target_s):
     }
 
 
+def sweep(algos=("naive", "lds_tiled", "lds_tiled_nopad", "regblock", "mfma")):
+    """Every algorithm on every workload: median kernel time over a few calls."""
+    import torch
+
+    import fp32_gemm_08_amd as lib
+    from fp32_gemm_08_amd.inputs import CONFIGS, make_config
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream(dev)
+    rows = []
+    print("| workload | algorithm | kernel | median ms | TFLOP/s | % of 157.3 |")
+    print("|---|---|---|---|---|---|")
+    for name in CONFIGS:
+        case = make_config(name)
+        M, N, K = case.M, case.N, case.K
+        dA = torch.from_numpy(case.A).to(dev)
+        dB = torch.from_numpy(case.B).to(dev)
+        dC = torch.zeros((M, case.ldc), dtype=torch.float32, device=dev)
+        if case.C is not None:
+            dC.copy_(torch.from_numpy(case.C))
+        flop = 2.0 * M * N * K
+        for algo in algos:
+            a = lib.ALGO[algo]
+            st, kid, tm, tn, kname = lib.sgemm_f32_plan(a, M, N, K, case.alpha, dA.data_ptr(), case.lda,
+                                                        dB.data_ptr(), case.ldb, int(case.trans_b), case.beta,
+                                                        dC.data_ptr(), case.ldc)
+            est = flop / 2e12 if algo in ("naive", "lds_tiled", "lds_tiled_nopad") else flop / 50e12
+            reps = int(max(3, min(20, 2.0 / max(est, 1e-6))))
+            times = []
+            for i in range(reps + 1):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                s = lib.sgemm_f32_algo(a, M, N, K, case.alpha, dA.data_ptr(), case.lda, dB.data_ptr(), case.ldb,
+                                       int(case.trans_b), case.beta, dC.data_ptr(), case.ldc, stream.cuda_stream)
+                e1.record(stream)
+                if s != 0:
+                    raise RuntimeError(lib.sgemm_f32_status_string(s))
+                torch.cuda.synchronize()
+                if i:
+                    times.append(e0.elapsed_time(e1) * 1e-3)
+            times.sort()
+            med = times[len(times) // 2]
+            tf = flop / med / 1e12
+            print(f"| {name} {M}x{N}x{K}{' B^T' if case.trans_b else ''} | {algo} | {kname.split()[0]} | "
+                  f"{med * 1e3:.4f} | {tf:.2f} | {100 * tf / FP32_MFMA_PEAK_TFLOPS:.1f} |", flush=True)
+            rows.append(dict(workload=name, algo=algo, kernel=kname, ms=med * 1e3, tflops=tf))
+        del dA, dB, dC
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed calls first; the clock needs ~0.1 s of load to reach its steady state")
     ap.add_argument("--config", default="c4_4096")
     ap.add_argument("--algo", default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every algorithm on every workload and print a table (no JSON line)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the GEMM shards by output rows; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: there is no multi-GPU path (the GEMM would shard by "
+              "rows of C with B replicated on every GPU). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.sweep:
+        sweep()
         return
 
     import fp32_gemm_08_amd as lib
@@ -170,26 +229,30 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    # Timed region: exactly K back-to-back calls on one stream, events at its two
+    # ends only (an event between launches inserts a gap of its own).  The
+    # kernel's average duration is the event span over K; the throughput uses the
+    # host wall clock between the two device synchronisations.
     K_steps = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K_steps)]
+    e_start = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(K_steps):
-        ev[i][0].record(stream)
+    e_start.record(stream)
+    for _ in range(K_steps):
         step()
-        ev[i][1].record(stream)
+    e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    durs = [a.elapsed_time(b) * 1e-3 for a, b in ev]
-    span = ev[0][0].elapsed_time(ev[-1][1]) * 1e-3
+    span = e_start.elapsed_time(e_end) * 1e-3
     flop = 2.0 * M * N * K
     value = K_steps * flop / wall / 1e12
-    kern_avg = sum(durs) / len(durs)
+    kern_avg = span / K_steps
     achieved = flop / kern_avg / 1e12
     mfma = kid in (40, 41, 42)
     peak = FP32_MFMA_PEAK_TFLOPS if mfma else FP32_VALU_PEAK_TFLOPS
-    log(f"kernel {kname}: avg {kern_avg * 1e3:.4f} ms, min {min(durs) * 1e3:.4f} ms, "
-        f"event span {span * 1e3:.3f} ms, wall {wall * 1e3:.3f} ms")
+    log(f"kernel {kname}: avg {kern_avg * 1e3:.4f} ms over {K_steps} calls "
+        f"(event span {span * 1e3:.3f} ms, wall {wall * 1e3:.3f} ms)")
 
     # output for the sample check (beta != 0 workloads accumulate across steps:
     # rerun once from the original C for the check)

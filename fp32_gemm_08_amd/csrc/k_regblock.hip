@@ -11,8 +11,9 @@
 // The A tile is stored k-major (As[k][m]) so a work-item fetches its 8 rows of A
 // for one k as two 128-bit LDS reads.  Rows and columns are split 4 + 4 (m, m+64
 // and n, n+64), so within a wavefront the A reads touch 4 broadcast addresses and
-// the 16 distinct B fragments form one contiguous 256-byte run.  Peak for this
-// stage is the non-packed vector FP32 rate (half the matrix-core rate on MI355X).
+// the 16 distinct B fragments form one contiguous 256-byte run.  The FMAs are
+// plain v_fmac_f32 (packed FP32 is kept out of the build); the stage's ceiling is
+// the vector FP32 rate.
 #include "sgemm_internal.h"
 
 namespace sgemm {

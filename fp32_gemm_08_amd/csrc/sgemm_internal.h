@@ -25,9 +25,9 @@ enum KernelId : int {
     KID_TILED_PAD = 20,
     KID_TILED_NOPAD = 21,
     KID_REGBLOCK = 30,
-    KID_MFMA_L = 40,        // 128 x 256 macro tile
-    KID_MFMA_M = 41,        // 128 x 128
-    KID_MFMA_S = 42,        // 64 x 64
+    KID_MFMA_L = 40,        // 256 x 256 macro tile, 8 wavefronts
+    KID_MFMA_M = 41,        // 128 x 128, 4 wavefronts
+    KID_MFMA_S = 42,        // 64 x 64, 4 wavefronts
 };
 
 // Tile geometry of each kernel (rows x cols of C per workgroup).

@@ -85,7 +85,7 @@ typedef enum {
  *   REGBLOCK         128x128 macro tile, 8x8 outputs per work-item held in
  *                    registers (first page, section 5.2), 128-bit global loads
  *                    (section 5.3) and double-buffered LDS staging (second page,
- *                    section 3.2).  Vector FP32 FMA.
+ *                    section 3.2).  Vector FP32 FMA (v_fmac_f32).
  *   MFMA             CDNA matrix-core path: v_mfma_f32_32x32x2_f32, FP32 inputs and
  *                    FP32 accumulation, multi-level tiling (second page, section 7.3).
  *   AUTO             MFMA with a tile chosen from the problem shape.

@@ -138,9 +138,9 @@ def test_explicit_algorithms(algo, kid):
 
 
 @pytest.mark.parametrize("shape,kid,tiles", [
-    ((4096, 4096, 4096), KID_L, (32, 16)),
-    ((8192, 8192, 8192), KID_L, (64, 32)),
-    ((16384, 4096, 1024), KID_L, (128, 16)),
+    ((4096, 4096, 4096), KID_L, (16, 16)),
+    ((8192, 8192, 8192), KID_L, (32, 32)),
+    ((16384, 4096, 1024), KID_L, (64, 16)),
     ((2048, 2048, 2048), KID_M, (16, 16)),
     ((1024, 1024, 1024), KID_S, (16, 16)),
     ((1000, 1017, 999), KID_S, (16, 16)),
