@@ -21,26 +21,28 @@
 //     epilogue writes IL consecutive columns per lane.
 //   * op(B) = B^T is staged k-contiguous like A (rows of B are already k-major),
 //     so it needs neither a transpose nor an interleave.
-//   * LDS rows of A (and of B^T) are padded by 4 floats: the 16-byte rows read by
-//     consecutive lanes then start on distinct banks (the +1 padding idea of
+//   * k-contiguous LDS tiles (A, B^T) are unpadded, with the 16-byte chunks of
+//     each row permuted by an XOR of row bits: the 32 rows a half-wavefront reads
+//     at one k then fall on distinct banks, and a whole 1 KB block of LDS can be
+//     filled by one direct global->LDS load (the +1 padding of
 //     "CUDA矩阵乘法性能优化实战：从朴素内核到寄存器分块与Nsight剖析", section 3.3,
-//     at 128-bit granularity).
+//     cannot be expressed inside such a block; the permutation does its job).
 //   * Workgroups are dispatched round-robin over the 8 XCDs; tiles are remapped
 //     so each XCD gets a contiguous run, grouped 8 tile-rows at a time, so tiles
 //     that share rows of A and columns of B run on the same L2.
 //
-// Software pipeline (one barrier per k-tile).  The global loads of tile t+1 are
-// in registers when iteration t starts; iteration t
-//   1. stores them to the other LDS buffer (free: every wavefront finished
-//      reading it before the previous barrier) and issues the global loads of
-//      tile t+2, so global latency has a whole tile of MFMA work to hide under;
-//   2. runs the MFMAs of k-groups 0..G-2, reading each next group's fragments
-//      from LDS while the current group's MFMAs execute;
-//   3. waits for its LDS traffic, passes the barrier, reads group 0 of tile t+1,
-//      and only then issues the MFMAs of the last group, which cover the barrier
-//      and the next tile's first LDS reads.
-// Interior workgroups (the tile inside M x N, a full k-tile) load without masks;
-// edge workgroups and the K tail load element-wise with zero fill.
+// Two staging paths fill the same LDS layout:
+//   * direct (interior tiles, 16-byte aligned operands): global_load_lds_dwordx4
+//     writes each 1 KB LDS block straight from memory, no registers involved.
+//     Tile t+1 is issued at the start of iteration t into the free buffer and must
+//     land before the iteration's barrier.  A partial last k-tile (K % BK != 0) is
+//     staged through registers with zero fill and multiplied first.
+//   * registers (edge tiles, unaligned operands): masked loads into registers,
+//     one tile ahead: iteration t stores tile t+1 to the free buffer and issues
+//     the loads of tile t+2.
+// In both, each k-group's fragments are read while the previous group's MFMAs
+// run, and the one barrier per tile sits before the last group's MFMAs, which
+// cover it and the next tile's first LDS reads.
 #include "sgemm_internal.h"
 
 namespace sgemm {
@@ -48,6 +50,7 @@ namespace sgemm {
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 template <int W> struct vec_of;
 template <> struct vec_of<1> { typedef float type; };
@@ -106,24 +109,54 @@ template <int BM_, int BN_, int BK_, int WGM_, int WGN_, int OCC_, bool TRANS_B>
 struct Geo {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_, OCC = OCC_;
     static constexpr int NT = 64 * WGM * WGN;          // work-items per workgroup
+    static constexpr int NW = WGM * WGN;               // wavefronts per workgroup
     static constexpr int WM = BM / WGM, WN = BN / WGN; // wavefront tile
     static constexpr int FM = WM / 32, FN = WN / 32;   // 32x32 blocks per wavefront
     static constexpr int IL = TRANS_B ? 1 : (FN >= 4 ? 4 : FN);
     static constexpr int NG = FN / IL;                 // interleaved column groups
     static constexpr int G = BK / 8;                   // k-groups per tile
-    static constexpr int SA = BK + 4;                  // A row stride in LDS (floats)
-    static constexpr int SB = TRANS_B ? BK + 4 : BN;   // B^T row stride / B row stride
-    static constexpr int A_SZ = BM * SA;
-    static constexpr int B_SZ = TRANS_B ? BN * SB : BK * SB;
+    static constexpr int CPR = BK / 4;                 // 16-byte chunks per k-row
+    static constexpr int A_SZ = BM * BK;               // floats per LDS stage
+    static constexpr int B_SZ = BK * BN;
     static constexpr int STAGE = A_SZ + B_SZ;
-    static constexpr int KC = BK / 4;                  // 4-float chunks per k-row
-    static constexpr int CA = BM * KC / NT;            // A chunks per work-item
-    static constexpr int CB = (TRANS_B ? BN * KC : BK * (BN / 4)) / NT;
-    static_assert(WM % 32 == 0 && WN % 32 == 0 && BK % 8 == 0, "tile shape");
-    static_assert(BM * KC % NT == 0 && (TRANS_B ? BN * KC : BK * (BN / 4)) % NT == 0, "staging split");
+    static constexpr int CA = BM * CPR / NT;           // register path: A chunks per work-item
+    static constexpr int CB = BK * BN / 4 / NT;        //                B chunks per work-item
+    static constexpr int A_BLK_W = A_SZ / 256 / NW;    // direct path: 1 KB blocks per wavefront
+    static constexpr int B_BLK_W = B_SZ / 256 / NW;
+    static_assert(WM % 32 == 0 && WN % 32 == 0, "tile shape");
+    static_assert(BK == 16 || BK == 32, "the chunk permutation covers 4 or 8 chunks per row");
+    static_assert(BM * CPR % NT == 0 && (BK * BN / 4) % NT == 0, "register staging split");
+    static_assert(A_SZ % (256 * NW) == 0 && B_SZ % (256 * NW) == 0, "direct staging split");
+    static_assert(TRANS_B || 256 % BN == 0, "op(B)=B rows must tile a 1 KB block");
     static_assert(2 * STAGE * 4 <= 160 * 1024, "LDS budget");
-    static_assert(G >= 2 && G % 2 == 0, "the fragment ping-pong needs an even number of k-groups");
+    static_assert(G % 2 == 0, "the fragment ping-pong needs an even number of k-groups");
 };
+
+// Physical 16-byte chunk of logical chunk c in row r of a k-contiguous tile.
+// Rows r..r+7 get 8 distinct permutations (CPR=8), and any 16 rows split into
+// pairs (r mod 2 or r mod 4) that differ too, so 8- and 16-lane read phases
+// both touch every bank once.
+template <int CPR>
+__device__ __forceinline__ int swz(int r)
+{
+    if constexpr (CPR == 4)
+        return ((r >> 1) ^ (r >> 2)) & 3;
+    else
+        return (r ^ (r >> 3)) & 7;
+}
+
+// Float offset of logical chunk c of row r in a k-contiguous tile.
+template <int CPR>
+__device__ __forceinline__ int koff(int r, int c)
+{
+    return r * (4 * CPR) + 4 * (c ^ swz<CPR>(r));
+}
+
+// Keeps the instruction scheduler from moving anything across this point.  The
+// fragment reads of the next k-group are issued before the current group's
+// MFMAs on purpose (their latency hides under ~32 MFMAs); left alone, the
+// scheduler sinks them next to their first use to save registers.
+__device__ __forceinline__ void pin_order() { __builtin_amdgcn_sched_barrier(0); }
 
 // Fragments of one k-group: FM A operands (4 k-steps each) and the B operands.
 template <class Gm, bool TRANS_B>
@@ -138,30 +171,34 @@ template <class Gm, bool TRANS_B>
 __device__ __forceinline__ void read_frags(Frags<Gm, TRANS_B> &f, const float *As, const float *Bs, int g,
                                            int wm, int wn, int l32, int hi)
 {
-    const int kq = 8 * g + 4 * hi;  // this half-wavefront's first k of the group
+    constexpr int CPR = Gm::CPR;
+    const int c = 2 * g + hi;  // logical chunk: k = 8g + 4*hi .. +3
 #pragma unroll
     for (int fm = 0; fm < Gm::FM; ++fm)
-        f.a[fm] = *reinterpret_cast<const f32x4 *>(&As[(wm * Gm::WM + 32 * fm + l32) * Gm::SA + kq]);
+        f.a[fm] = *reinterpret_cast<const f32x4 *>(&As[koff<CPR>(wm * Gm::WM + 32 * fm + l32, c)]);
     if constexpr (TRANS_B) {
 #pragma unroll
         for (int fn = 0; fn < Gm::FN; ++fn)
-            f.bt[fn] = *reinterpret_cast<const f32x4 *>(&Bs[(wn * Gm::WN + 32 * fn + l32) * Gm::SB + kq]);
+            f.bt[fn] = *reinterpret_cast<const f32x4 *>(&Bs[koff<CPR>(wn * Gm::WN + 32 * fn + l32, c)]);
     } else {
         typedef typename vec_of<Gm::IL>::type bvec;
+        const int k = 8 * g + 4 * hi;
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int gr = 0; gr < Gm::NG; ++gr)
                 f.b[s][gr] = *reinterpret_cast<const bvec *>(
-                    &Bs[(kq + s) * Gm::SB + wn * Gm::WN + gr * 32 * Gm::IL + Gm::IL * l32]);
+                    &Bs[(k + s) * Gm::BN + wn * Gm::WN + gr * 32 * Gm::IL + Gm::IL * l32]);
     }
 }
 
+// MFMA steps s0 .. s1-1 of one k-group (8 consecutive k values, 4 steps).
 template <class Gm, bool TRANS_B>
-__device__ __forceinline__ void mfma_group(f32x16 (&acc)[Gm::FM][Gm::FN], const Frags<Gm, TRANS_B> &f)
+__device__ __forceinline__ void mfma_steps(f32x16 (&acc)[Gm::FM][Gm::FN], const Frags<Gm, TRANS_B> &f, int s0,
+                                           int s1)
 {
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int s = s0; s < s1; ++s)
 #pragma unroll
         for (int fm = 0; fm < Gm::FM; ++fm) {
             if constexpr (TRANS_B) {
@@ -179,126 +216,152 @@ __device__ __forceinline__ void mfma_group(f32x16 (&acc)[Gm::FM][Gm::FN], const 
         }
 }
 
-// The k-loop and epilogue for one workgroup tile.  FULL: the tile lies inside
-// M x N, so only the K tail needs masks.
-template <class Gm, bool TRANS_B, bool VEC, bool FULL>
-__device__ __forceinline__ void gemm_tile(const GemmArgs &a, float *smem, int m0, int n0)
+template <class Gm, bool TRANS_B>
+__device__ __forceinline__ void mfma_group(f32x16 (&acc)[Gm::FM][Gm::FN], const Frags<Gm, TRANS_B> &f)
 {
-    constexpr int NT = Gm::NT, KC = Gm::KC, CA = Gm::CA, CB = Gm::CB, BK = Gm::BK, G = Gm::G;
-    constexpr int BN4 = Gm::BN / 4;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int l32 = lane & 31, hi = lane >> 5;
-    const int wm = wave / Gm::WGN, wn = wave % Gm::WGN;
+    mfma_steps<Gm, TRANS_B>(acc, f, 0, 4);
+}
 
-    // Per work-item staging coordinates and global base pointers (k = 0).
+// Register staging of one k-tile: masked (or, for interior tiles and full
+// k-tiles, plain) loads of the tile into registers, then stores in LDS layout.
+template <class Gm, bool TRANS_B, bool VEC>
+struct RegStage {
+    static constexpr int CA = Gm::CA, CB = Gm::CB, CPR = Gm::CPR, BN4 = Gm::BN / 4;
     const float *pa[CA];
     const float *pb[CB];
-    int ra_row[CA], ra_col[CA], rb_row[CB], rb_col[CB];
-#pragma unroll
-    for (int i = 0; i < CA; ++i) {
-        const int q = tid + i * NT;
-        ra_row[i] = q / KC;
-        ra_col[i] = 4 * (q % KC);
-        pa[i] = a.A + (int64_t)(m0 + ra_row[i]) * a.lda + ra_col[i];
-    }
-#pragma unroll
-    for (int i = 0; i < CB; ++i) {
-        const int q = tid + i * NT;
-        if constexpr (TRANS_B) {
-            rb_row[i] = q / KC;           // n within the tile
-            rb_col[i] = 4 * (q % KC);     // k within the tile
-            pb[i] = a.B + (int64_t)(n0 + rb_row[i]) * a.ldb + rb_col[i];
-        } else {
-            rb_row[i] = q / BN4;          // k within the tile
-            rb_col[i] = 4 * (q % BN4);    // n within the tile
-            pb[i] = a.B + (int64_t)rb_row[i] * a.ldb + n0 + rb_col[i];
-        }
-    }
-    const int64_t b_kstep = TRANS_B ? (int64_t)BK : (int64_t)BK * a.ldb;
-
+    int ra_row[CA], ra_c[CA], rb_row[CB], rb_c[CB];
     f32x4 ra[CA], rb[CB];
-    auto gload = [&](int kt) {
-        const int k0 = kt * BK;
-        if (FULL && k0 + BK <= a.K) {
+    int64_t b_kstep;
+
+    __device__ __forceinline__ void init(const GemmArgs &a, int m0, int n0)
+    {
+        const int tid = threadIdx.x;
 #pragma unroll
-            for (int i = 0; i < CA; ++i)
-                ra[i] = load4<VEC, false>(pa[i] + (int64_t)kt * BK, true, 0, 0);
+        for (int i = 0; i < CA; ++i) {
+            const int q = tid + i * Gm::NT;
+            ra_row[i] = q / CPR;
+            ra_c[i] = q % CPR;
+            pa[i] = a.A + (int64_t)(m0 + ra_row[i]) * a.lda + 4 * ra_c[i];
+        }
 #pragma unroll
-            for (int i = 0; i < CB; ++i)
-                rb[i] = load4<VEC, false>(pb[i] + (int64_t)kt * b_kstep, true, 0, 0);
-        } else {
-#pragma unroll
-            for (int i = 0; i < CA; ++i)
-                ra[i] = load4<VEC, true>(pa[i] + (int64_t)kt * BK, m0 + ra_row[i] < a.M, k0 + ra_col[i], a.K);
-#pragma unroll
-            for (int i = 0; i < CB; ++i) {
-                if constexpr (TRANS_B)
-                    rb[i] = load4<VEC, true>(pb[i] + (int64_t)kt * b_kstep, n0 + rb_row[i] < a.N,
-                                             k0 + rb_col[i], a.K);
-                else
-                    rb[i] = load4<VEC, true>(pb[i] + (int64_t)kt * b_kstep, k0 + rb_row[i] < a.K,
-                                             n0 + rb_col[i], a.N);
+        for (int i = 0; i < CB; ++i) {
+            const int q = tid + i * Gm::NT;
+            if constexpr (TRANS_B) {
+                rb_row[i] = q / CPR;          // n within the tile
+                rb_c[i] = q % CPR;            // k chunk
+                pb[i] = a.B + (int64_t)(n0 + rb_row[i]) * a.ldb + 4 * rb_c[i];
+            } else {
+                rb_row[i] = q / BN4;          // k within the tile
+                rb_c[i] = q % BN4;            // n chunk
+                pb[i] = a.B + (int64_t)rb_row[i] * a.ldb + n0 + 4 * rb_c[i];
             }
         }
-    };
-    auto sstore = [&](int buf) {
-        float *As = smem + buf * Gm::STAGE;
-        float *Bs = As + Gm::A_SZ;
-#pragma unroll
-        for (int i = 0; i < CA; ++i)
-            *reinterpret_cast<f32x4 *>(&As[ra_row[i] * Gm::SA + ra_col[i]]) = ra[i];
-#pragma unroll
-        for (int i = 0; i < CB; ++i)
-            *reinterpret_cast<f32x4 *>(&Bs[rb_row[i] * Gm::SB + rb_col[i]]) = rb[i];
-    };
-
-    f32x16 acc[Gm::FM][Gm::FN];
-#pragma unroll
-    for (int i = 0; i < Gm::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < Gm::FN; ++j)
-            acc[i][j] = f32x16{0};
-
-    const int nk = (a.K + BK - 1) / BK;
-    Frags<Gm, TRANS_B> f[2];
-
-    // Prologue: tile 0 into LDS buffer 0, tile 1 in flight, group 0 fragments.
-    gload(0);
-    sstore(0);
-    if (nk > 1)
-        gload(1);
-    __syncthreads();
-    read_frags<Gm, TRANS_B>(f[0], smem, smem + Gm::A_SZ, 0, wm, wn, l32, hi);
-
-    for (int t = 0; t < nk; ++t) {
-        const float *As = smem + (t & 1) * Gm::STAGE;
-        const float *Bs = As + Gm::A_SZ;
-        // 1. tile t+1 (in registers) to the free buffer; tile t+2 in flight
-        if (t + 1 < nk) {
-            sstore((t + 1) & 1);
-            if (t + 2 < nk)
-                gload(t + 2);
-        }
-        // 2. groups 0..G-2, next group's fragments read under the MFMAs
-#pragma unroll
-        for (int g = 0; g < G - 1; ++g) {
-            read_frags<Gm, TRANS_B>(f[(g + 1) & 1], As, Bs, g + 1, wm, wn, l32, hi);
-            mfma_group<Gm, TRANS_B>(acc, f[g & 1]);
-        }
-        // 3. barrier and the next tile's first fragments under the last group
-        if (t + 1 < nk) {
-            __syncthreads();
-            const float *An = smem + ((t + 1) & 1) * Gm::STAGE;
-            read_frags<Gm, TRANS_B>(f[G & 1], An, An + Gm::A_SZ, 0, wm, wn, l32, hi);
-        }
-        mfma_group<Gm, TRANS_B>(acc, f[(G - 1) & 1]);
+        b_kstep = TRANS_B ? (int64_t)Gm::BK : (int64_t)Gm::BK * a.ldb;
     }
 
-    // Epilogue.  Accumulator register r of a 32x32 block holds row
-    // 8*(r/4) + 4*hi + (r%4) and column l32 of that block.
+    // MASKED=false: the tile lies inside M x N and k-tile kt is full.
+    template <bool MASKED>
+    __device__ __forceinline__ void load(const GemmArgs &a, int m0, int n0, int kt)
+    {
+        const int k0 = kt * Gm::BK;
+#pragma unroll
+        for (int i = 0; i < CA; ++i)
+            ra[i] = load4<VEC, MASKED>(pa[i] + (int64_t)k0, m0 + ra_row[i] < a.M, k0 + 4 * ra_c[i], a.K);
+#pragma unroll
+        for (int i = 0; i < CB; ++i) {
+            if constexpr (TRANS_B)
+                rb[i] = load4<VEC, MASKED>(pb[i] + (int64_t)kt * b_kstep, n0 + rb_row[i] < a.N,
+                                           k0 + 4 * rb_c[i], a.K);
+            else
+                rb[i] = load4<VEC, MASKED>(pb[i] + (int64_t)kt * b_kstep, k0 + rb_row[i] < a.K,
+                                           n0 + 4 * rb_c[i], a.N);
+        }
+    }
+
+    __device__ __forceinline__ void store(float *As, float *Bs) const
+    {
+#pragma unroll
+        for (int i = 0; i < CA; ++i)
+            *reinterpret_cast<f32x4 *>(&As[koff<CPR>(ra_row[i], ra_c[i])]) = ra[i];
+#pragma unroll
+        for (int i = 0; i < CB; ++i) {
+            if constexpr (TRANS_B)
+                *reinterpret_cast<f32x4 *>(&Bs[koff<CPR>(rb_row[i], rb_c[i])]) = rb[i];
+            else
+                *reinterpret_cast<f32x4 *>(&Bs[rb_row[i] * Gm::BN + 4 * rb_c[i]]) = rb[i];
+        }
+    }
+};
+
+// Direct staging of full k-tiles: each wavefront fills A_BLK_W + B_BLK_W 1 KB
+// LDS blocks with global_load_lds_dwordx4 (lane L writes bytes 16L..16L+15 of a
+// block).  Per-lane sources are 32-bit float offsets from the tile's first
+// element, valid because the host allows this path only when a tile's extent
+// fits (rows x leading dimension < 2^31).
+template <class Gm, bool TRANS_B>
+struct DirectStage {
+    static constexpr int CPR = Gm::CPR, RPB = 256 / Gm::BK;  // k-rows of A per block
+    uint32_t a_off[Gm::A_BLK_W], b_off[Gm::B_BLK_W];
+    int a_blk0, b_blk0;
+    const float *a_base;
+    const float *b_base;
+    int64_t b_kstep;
+
+    __device__ __forceinline__ void init(const GemmArgs &a, int m0, int n0)
+    {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        a_blk0 = wave * Gm::A_BLK_W;
+        b_blk0 = wave * Gm::B_BLK_W;
+#pragma unroll
+        for (int j = 0; j < Gm::A_BLK_W; ++j) {
+            const int r = (a_blk0 + j) * RPB + lane / CPR;
+            const int c = (lane % CPR) ^ swz<CPR>(r);
+            a_off[j] = (uint32_t)(r * a.lda + 4 * c);
+        }
+#pragma unroll
+        for (int j = 0; j < Gm::B_BLK_W; ++j) {
+            if constexpr (TRANS_B) {
+                const int r = (b_blk0 + j) * RPB + lane / CPR;   // n within the tile
+                const int c = (lane % CPR) ^ swz<CPR>(r);
+                b_off[j] = (uint32_t)(r * a.ldb + 4 * c);
+            } else {
+                const int e = (b_blk0 + j) * 256 + 4 * lane;     // float index in the [BK][BN] tile
+                b_off[j] = (uint32_t)((e / Gm::BN) * a.ldb + e % Gm::BN);
+            }
+        }
+        a_base = a.A + (int64_t)m0 * a.lda;
+        b_base = TRANS_B ? a.B + (int64_t)n0 * a.ldb : a.B + n0;
+        b_kstep = TRANS_B ? (int64_t)Gm::BK : (int64_t)Gm::BK * a.ldb;
+    }
+
+    static constexpr int NLOAD = Gm::A_BLK_W + Gm::B_BLK_W;  // loads per wavefront per k-tile
+
+    // Loads j0 .. j1-1 of k-tile kt (A blocks first, then B blocks).
+    __device__ __forceinline__ void issue(int kt, float *As, float *Bs, int j0 = 0, int j1 = NLOAD) const
+    {
+        const float *ak = a_base + (int64_t)kt * Gm::BK;
+        const float *bk = b_base + (int64_t)kt * b_kstep;
+#pragma unroll
+        for (int j = 0; j < Gm::A_BLK_W; ++j)
+            if (j >= j0 && j < j1)
+                __builtin_amdgcn_global_load_lds(ak + a_off[j], (lds_void *)(As + (a_blk0 + j) * 256), 16, 0, 0);
+#pragma unroll
+        for (int j = 0; j < Gm::B_BLK_W; ++j)
+            if (Gm::A_BLK_W + j >= j0 && Gm::A_BLK_W + j < j1)
+                __builtin_amdgcn_global_load_lds(bk + b_off[j], (lds_void *)(Bs + (b_blk0 + j) * 256), 16, 0, 0);
+    }
+};
+
+template <class Gm, bool TRANS_B, bool FULL>
+__device__ __forceinline__ void epilogue(const GemmArgs &a, const f32x16 (&acc)[Gm::FM][Gm::FN], int m0, int n0)
+{
+    // Accumulator register r of a 32x32 block holds row 8*(r/4) + 4*hi + (r%4)
+    // and column l32 of that block.
     typedef typename vec_of<Gm::IL>::type bvec;
     constexpr int IL = Gm::IL;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+    const int wm = wave / Gm::WGN, wn = wave % Gm::WGN;
     const uintptr_t cbase = reinterpret_cast<uintptr_t>(a.C);
     const bool cvec = IL > 1 && (cbase % (4 * IL)) == 0 && (a.ldc % IL) == 0;
 #pragma unroll
@@ -358,19 +421,165 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, float *smem, int m0
     }
 }
 
-template <class Gm, bool TRANS_B, bool VEC>
-__global__ __launch_bounds__(Gm::NT) __attribute__((amdgpu_waves_per_eu(Gm::OCC)))
+// Register-staged k-loop.  FULL: the tile lies inside M x N (only the K tail
+// needs masks).
+template <class Gm, bool TRANS_B, bool VEC, bool FULL>
+__device__ __forceinline__ void gemm_tile_regs(const GemmArgs &a, float *smem, int m0, int n0)
+{
+    constexpr int G = Gm::G;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+    const int wm = wave / Gm::WGN, wn = wave % Gm::WGN;
+
+    RegStage<Gm, TRANS_B, VEC> st;
+    st.init(a, m0, n0);
+    auto gload = [&](int kt) {
+        if (FULL && (kt + 1) * Gm::BK <= a.K)
+            st.template load<false>(a, m0, n0, kt);
+        else
+            st.template load<true>(a, m0, n0, kt);
+    };
+
+    f32x16 acc[Gm::FM][Gm::FN];
+#pragma unroll
+    for (int i = 0; i < Gm::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < Gm::FN; ++j)
+            acc[i][j] = f32x16{0};
+
+    const int nk = (a.K + Gm::BK - 1) / Gm::BK;
+    Frags<Gm, TRANS_B> f[2];
+    gload(0);
+    st.store(smem, smem + Gm::A_SZ);
+    if (nk > 1)
+        gload(1);
+    __syncthreads();
+    read_frags<Gm, TRANS_B>(f[0], smem, smem + Gm::A_SZ, 0, wm, wn, l32, hi);
+
+    for (int t = 0; t < nk; ++t) {
+        const float *As = smem + (t & 1) * Gm::STAGE;
+        const float *Bs = As + Gm::A_SZ;
+        float *An = smem + ((t + 1) & 1) * Gm::STAGE;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            // First MFMA step on fragments read a whole group earlier, before any
+            // new LDS traffic, so the wait in front of it never covers fresh reads.
+            mfma_steps<Gm, TRANS_B>(acc, f[g & 1], 0, 1);
+            pin_order();
+            if (g == 0 && t + 1 < nk) {
+                st.store(An, An + Gm::A_SZ);   // tile t+1 into the free buffer
+                if (t + 2 < nk)
+                    gload(t + 2);
+            }
+            if (g + 1 < G) {
+                read_frags<Gm, TRANS_B>(f[(g + 1) & 1], As, Bs, g + 1, wm, wn, l32, hi);
+            } else if (t + 1 < nk) {
+                __syncthreads();
+                read_frags<Gm, TRANS_B>(f[G & 1], An, An + Gm::A_SZ, 0, wm, wn, l32, hi);
+            }
+            pin_order();
+            mfma_steps<Gm, TRANS_B>(acc, f[g & 1], 1, 4);
+        }
+    }
+    epilogue<Gm, TRANS_B, FULL>(a, acc, m0, n0);
+}
+
+// Direct-staged k-loop for interior tiles with 16-byte aligned operands.
+template <class Gm, bool TRANS_B>
+__device__ __forceinline__ void gemm_tile_direct(const GemmArgs &a, float *smem, int m0, int n0)
+{
+    constexpr int G = Gm::G;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+    const int wm = wave / Gm::WGN, wn = wave % Gm::WGN;
+    float *buf0 = smem, *buf1 = smem + Gm::STAGE;
+
+    f32x16 acc[Gm::FM][Gm::FN];
+#pragma unroll
+    for (int i = 0; i < Gm::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < Gm::FN; ++j)
+            acc[i][j] = f32x16{0};
+
+    const int nf = a.K / Gm::BK;  // full k-tiles
+    Frags<Gm, TRANS_B> f[2];
+
+    DirectStage<Gm, TRANS_B> ds;
+    ds.init(a, m0, n0);
+    if (nf > 0)
+        ds.issue(0, buf0, buf0 + Gm::A_SZ);
+
+    // Partial last k-tile first (the order of the k sum is free): registers with
+    // zero fill, through buffer 1, while tile 0 lands in buffer 0.
+    if (nf * Gm::BK < a.K) {
+        RegStage<Gm, TRANS_B, true> st;
+        st.init(a, m0, n0);
+        st.template load<true>(a, m0, n0, nf);
+        st.store(buf1, buf1 + Gm::A_SZ);
+        __syncthreads();
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            read_frags<Gm, TRANS_B>(f[0], buf1, buf1 + Gm::A_SZ, g, wm, wn, l32, hi);
+            mfma_group<Gm, TRANS_B>(acc, f[0]);
+        }
+    }
+    if (nf > 0) {
+        __syncthreads();  // tile 0 has landed (and buffer 1 is free again)
+        read_frags<Gm, TRANS_B>(f[0], buf0, buf0 + Gm::A_SZ, 0, wm, wn, l32, hi);
+        for (int t = 0; t < nf; ++t) {
+            const float *As = (t & 1) ? buf1 : buf0;
+            const float *Bs = As + Gm::A_SZ;
+            float *An = (t & 1) ? buf0 : buf1;
+            // All loads of tile t+1 go out first: measured against spreading them
+            // over the MFMA steps, issuing them together at the top is faster.
+            if (t + 1 < nf) {
+                ds.issue(t + 1, An, An + Gm::A_SZ);
+                pin_order();
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                mfma_steps<Gm, TRANS_B>(acc, f[g & 1], 0, 1);
+                pin_order();
+                if (g + 1 < G) {
+                    read_frags<Gm, TRANS_B>(f[(g + 1) & 1], As, Bs, g + 1, wm, wn, l32, hi);
+                } else if (t + 1 < nf) {
+                    __syncthreads();  // this wavefront's direct loads, then everyone's
+                    read_frags<Gm, TRANS_B>(f[G & 1], An, An + Gm::A_SZ, 0, wm, wn, l32, hi);
+                }
+                pin_order();
+                mfma_steps<Gm, TRANS_B>(acc, f[g & 1], 1, 4);
+            }
+        }
+    }
+    epilogue<Gm, TRANS_B, true>(a, acc, m0, n0);
+}
+
+// GD: geometry of the direct path; GR: geometry of the register path (same
+// workgroup tile and wavefront layout, possibly a shorter k-tile so the register
+// staging fits next to the accumulators).
+template <class GD, class GR, bool TRANS_B, bool VEC>
+__global__ __launch_bounds__(GD::NT) __attribute__((amdgpu_waves_per_eu(GD::OCC)))
 void sgemm_mfma_kernel(GemmArgs a)
 {
-    __shared__ __attribute__((aligned(16))) float smem[2 * Gm::STAGE];
-    const int nbm = (a.M + Gm::BM - 1) / Gm::BM, nbn = (a.N + Gm::BN - 1) / Gm::BN;
+    static_assert(GD::BM == GR::BM && GD::BN == GR::BN && GD::NT == GR::NT && GD::WGN == GR::WGN,
+                  "both paths share the workgroup tile");
+    constexpr int SMEM = 2 * (GD::STAGE > GR::STAGE ? GD::STAGE : GR::STAGE);
+    __shared__ __attribute__((aligned(1024))) float smem[SMEM];
+    const int nbm = (a.M + GD::BM - 1) / GD::BM, nbn = (a.N + GD::BN - 1) / GD::BN;
     int tile_m, tile_n;
     map_tile(blockIdx.x, nbm, nbn, tile_m, tile_n);
-    const int m0 = tile_m * Gm::BM, n0 = tile_n * Gm::BN;
-    if (m0 + Gm::BM <= a.M && n0 + Gm::BN <= a.N)
-        gemm_tile<Gm, TRANS_B, VEC, true>(a, smem, m0, n0);
+    const int m0 = tile_m * GD::BM, n0 = tile_n * GD::BN;
+    const bool full = m0 + GD::BM <= a.M && n0 + GD::BN <= a.N;
+    if constexpr (VEC) {
+        if (full && (a.flags & GEMM_FLAG_DIRECT)) {
+            gemm_tile_direct<GD, TRANS_B>(a, smem, m0, n0);
+            return;
+        }
+    }
+    if (full)
+        gemm_tile_regs<GR, TRANS_B, VEC, true>(a, smem, m0, n0);
     else
-        gemm_tile<Gm, TRANS_B, VEC, false>(a, smem, m0, n0);
+        gemm_tile_regs<GR, TRANS_B, VEC, false>(a, smem, m0, n0);
 }
 
 TileShape tile_shape(int kid)
@@ -387,23 +596,25 @@ TileShape tile_shape(int kid)
     }
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, int OCC>
+template <int BM, int BN, int BKD, int BKR, int WGM, int WGN, int OCC>
 static void launch_cfg(const GemmArgs &a, bool transB, bool vec, hipStream_t stream)
 {
     const int64_t blocks = ceil_div(a.M, BM) * ceil_div(a.N, BN);
     const dim3 grid((unsigned)blocks), block(64 * WGM * WGN);
-    typedef Geo<BM, BN, BK, WGM, WGN, OCC, true> GT;
-    typedef Geo<BM, BN, BK, WGM, WGN, OCC, false> GN;
+    typedef Geo<BM, BN, BKD, WGM, WGN, OCC, true> GDT;
+    typedef Geo<BM, BN, BKR, WGM, WGN, OCC, true> GRT;
+    typedef Geo<BM, BN, BKD, WGM, WGN, OCC, false> GDN;
+    typedef Geo<BM, BN, BKR, WGM, WGN, OCC, false> GRN;
     if (transB) {
         if (vec)
-            sgemm_mfma_kernel<GT, true, true><<<grid, block, 0, stream>>>(a);
+            sgemm_mfma_kernel<GDT, GRT, true, true><<<grid, block, 0, stream>>>(a);
         else
-            sgemm_mfma_kernel<GT, true, false><<<grid, block, 0, stream>>>(a);
+            sgemm_mfma_kernel<GDT, GRT, true, false><<<grid, block, 0, stream>>>(a);
     } else {
         if (vec)
-            sgemm_mfma_kernel<GN, false, true><<<grid, block, 0, stream>>>(a);
+            sgemm_mfma_kernel<GDN, GRN, false, true><<<grid, block, 0, stream>>>(a);
         else
-            sgemm_mfma_kernel<GN, false, false><<<grid, block, 0, stream>>>(a);
+            sgemm_mfma_kernel<GDN, GRN, false, false><<<grid, block, 0, stream>>>(a);
     }
 }
 
@@ -411,9 +622,9 @@ hipError_t launch_mfma(const GemmArgs &a, int kid, bool transB, bool vec, hipStr
 {
     switch (kid) {
 #ifndef SGEMM_MFMA_EXPERIMENT
-    case KID_MFMA_L: launch_cfg<256, 256, 16, 4, 2, 2>(a, transB, vec, stream); break;
-    case KID_MFMA_M: launch_cfg<128, 128, 32, 2, 2, 2>(a, transB, vec, stream); break;
-    case KID_MFMA_S: launch_cfg<64, 64, 32, 2, 2, 4>(a, transB, vec, stream); break;
+    case KID_MFMA_L: launch_cfg<256, 256, 32, 16, 4, 2, 2>(a, transB, vec, stream); break;
+    case KID_MFMA_M: launch_cfg<128, 128, 32, 32, 2, 2, 2>(a, transB, vec, stream); break;
+    case KID_MFMA_S: launch_cfg<64, 64, 32, 32, 2, 2, 4>(a, transB, vec, stream); break;
 #else
     SGEMM_MFMA_EXPERIMENT
 #endif

@@ -124,7 +124,7 @@ const char *kernel_label(int kid)
     case KID_TILED_PAD: return "lds_tiled_16x16_pad1";
     case KID_TILED_NOPAD: return "lds_tiled_16x16_pad0";
     case KID_REGBLOCK: return "regblock_128x128x8_t8x8";
-    case KID_MFMA_L: return "mfma_256x256x16_w4x2";
+    case KID_MFMA_L: return "mfma_256x256x32_w4x2";
     case KID_MFMA_M: return "mfma_128x128x32_w2x2";
     case KID_MFMA_S: return "mfma_64x64x32_w2x2";
     default: return "unknown";
@@ -173,6 +173,8 @@ int run(int algo, int64_t M, int64_t N, int64_t K, float alpha, const float *A, 
     a.K = (int)K;
     a.alpha = alpha;
     a.beta = beta;
+    const int64_t off_limit = ((int64_t)1 << 31) / 256;
+    a.flags = (lda < off_limit && ldb < off_limit) ? GEMM_FLAG_DIRECT : 0;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     (void)hipGetLastError();  // report this launch's status, not an older one
     hipError_t e;

@@ -15,7 +15,13 @@ struct GemmArgs {
     int64_t lda, ldb, ldc;
     int M, N, K;
     float alpha, beta;
+    int flags;  // GEMM_FLAG_* bits
 };
+
+// The MFMA kernel may stage interior tiles with direct global->LDS loads, whose
+// per-lane source offsets are 32-bit: set when 256 rows of A (and of B) span
+// fewer than 2^31 elements.
+constexpr int GEMM_FLAG_DIRECT = 1;
 
 // Kernel identifiers reported by the planning query.
 enum KernelId : int {
