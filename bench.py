@@ -115,16 +115,23 @@ def cpu_baseline(case, D_gpu_host, target_s):
 
 
 def sweep(algos=("naive", "lds_tiled", "lds_tiled_nopad", "regblock", "mfma")):
-    """Every algorithm on every workload: median kernel time over a few calls."""
+    """Every algorithm on every workload: average kernel time over back-to-back
+    calls (after a warm-up that brings the engine clock to its steady state)."""
     import torch
 
     import fp32_gemm_08_amd as lib
     from fp32_gemm_08_amd.inputs import CONFIGS, make_config
     dev = torch.device("cuda", 0)
     stream = torch.cuda.current_stream(dev)
+    w = torch.rand(4096, 4096, device=dev)
+    wc = torch.empty_like(w)
+    for _ in range(300):
+        lib.gemm(w, w, wc, algo="mfma")
+    torch.cuda.synchronize()
+    del w, wc
     rows = []
-    print("| workload | algorithm | kernel | median ms | TFLOP/s | % of 157.3 |")
-    print("|---|---|---|---|---|---|")
+    print("| workload | algorithm | kernel | calls | avg ms | TFLOP/s | % of 157.3 |")
+    print("|---|---|---|---|---|---|---|")
     for name in CONFIGS:
         case = make_config(name)
         M, N, K = case.M, case.N, case.K
@@ -139,27 +146,30 @@ def sweep(algos=("naive", "lds_tiled", "lds_tiled_nopad", "regblock", "mfma")):
             st, kid, tm, tn, kname = lib.sgemm_f32_plan(a, M, N, K, case.alpha, dA.data_ptr(), case.lda,
                                                         dB.data_ptr(), case.ldb, int(case.trans_b), case.beta,
                                                         dC.data_ptr(), case.ldc)
-            est = flop / 2e12 if algo in ("naive", "lds_tiled", "lds_tiled_nopad") else flop / 50e12
-            reps = int(max(3, min(20, 2.0 / max(est, 1e-6))))
-            times = []
-            for i in range(reps + 1):
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
+            rate = 3e12 if algo in ("naive", "lds_tiled", "lds_tiled_nopad") else 60e12
+            reps = int(max(3, min(200, 0.2 / max(flop / rate, 1e-7))))
+
+            def call():
                 s = lib.sgemm_f32_algo(a, M, N, K, case.alpha, dA.data_ptr(), case.lda, dB.data_ptr(), case.ldb,
                                        int(case.trans_b), case.beta, dC.data_ptr(), case.ldc, stream.cuda_stream)
-                e1.record(stream)
                 if s != 0:
                     raise RuntimeError(lib.sgemm_f32_status_string(s))
-                torch.cuda.synchronize()
-                if i:
-                    times.append(e0.elapsed_time(e1) * 1e-3)
-            times.sort()
-            med = times[len(times) // 2]
-            tf = flop / med / 1e12
-            print(f"| {name} {M}x{N}x{K}{' B^T' if case.trans_b else ''} | {algo} | {kname.split()[0]} | "
-                  f"{med * 1e3:.4f} | {tf:.2f} | {100 * tf / FP32_MFMA_PEAK_TFLOPS:.1f} |", flush=True)
-            rows.append(dict(workload=name, algo=algo, kernel=kname, ms=med * 1e3, tflops=tf))
+
+            for _ in range(max(2, reps // 4)):
+                call()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            avg = e0.elapsed_time(e1) * 1e-3 / reps
+            tf = flop / avg / 1e12
+            print(f"| {name} {M}x{N}x{K}{' B^T' if case.trans_b else ''} | {algo} | {kname.split()[0]} | {reps} | "
+                  f"{avg * 1e3:.4f} | {tf:.2f} | {100 * tf / FP32_MFMA_PEAK_TFLOPS:.1f} |", flush=True)
+            rows.append(dict(workload=name, algo=algo, kernel=kname, ms=avg * 1e3, tflops=tf))
         del dA, dB, dC
         torch.cuda.empty_cache()
     return rows

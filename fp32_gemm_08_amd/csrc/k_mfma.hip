@@ -109,32 +109,60 @@ __device__ __forceinline__ f32x4 load4(const float *p, bool ok, int first, int l
     return v;
 }
 
-// Compile-time geometry of one MFMA kernel configuration.
-template <int BM_, int BN_, int BK_, int WGM_, int WGN_, int OCC_, bool TRANS_B>
+// Compile-time geometry of one MFMA kernel configuration.  KS > 1 splits the
+// k-range of one output tile over KS groups of wavefronts ("k-slices"): an LDS
+// stage then holds KS consecutive BK-deep k-tiles, slice s multiplies the s-th
+// into its own accumulators, and the slices are added in LDS at the end.
+template <int BM_, int BN_, int BK_, int WGM_, int WGN_, int OCC_, bool TRANS_B, int KS_ = 1>
 struct Geo {
-    static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_, OCC = OCC_;
-    static constexpr int NT = 64 * WGM * WGN;          // work-items per workgroup
-    static constexpr int NW = WGM * WGN;               // wavefronts per workgroup
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_, OCC = OCC_, KS = KS_;
+    static constexpr int NWO = WGM * WGN;              // wavefronts per k-slice (one output tile)
+    static constexpr int NW = NWO * KS;                // wavefronts per workgroup
+    static constexpr int NT = 64 * NW;                 // work-items per workgroup
+    static constexpr int KT = KS * BK;                 // k values per LDS stage
     static constexpr int WM = BM / WGM, WN = BN / WGN; // wavefront tile
     static constexpr int FM = WM / 32, FN = WN / 32;   // 32x32 blocks per wavefront
     static constexpr int IL = TRANS_B ? 1 : (FN >= 4 ? 4 : FN);
     static constexpr int NG = FN / IL;                 // interleaved column groups
-    static constexpr int G = BK / 8;                   // k-groups per tile
+    static constexpr int G = BK / 8;                   // k-groups per slice tile
     static constexpr int CPR = BK / 4;                 // 16-byte chunks per k-row
-    static constexpr int A_SZ = BM * BK;               // floats per LDS stage
-    static constexpr int B_SZ = BK * BN;
-    static constexpr int STAGE = A_SZ + B_SZ;
-    static constexpr int CA = BM * CPR / NT;           // register path: A chunks per work-item
-    static constexpr int CB = BK * BN / 4 / NT;        //                B chunks per work-item
-    static constexpr int A_BLK_W = A_SZ / 256 / NW;    // direct path: 1 KB blocks per wavefront
-    static constexpr int B_BLK_W = B_SZ / 256 / NW;
+    static constexpr int A_SZ = BM * BK;               // floats of A per slice tile
+    static constexpr int B_SZ = BK * BN;               // floats of op(B) per slice tile
+    static constexpr int SLICE = A_SZ + B_SZ;
+    static constexpr int STAGE = KS * SLICE;           // floats per LDS stage
+    static constexpr int CA = KS * BM * CPR / NT;      // register path: A chunks per work-item
+    static constexpr int CB = KS * BK * BN / 4 / NT;   //                B chunks per work-item
+    static constexpr int A_BLK = A_SZ / 256, B_BLK = B_SZ / 256;  // 1 KB blocks per slice tile
+    static constexpr int A_BLK_W = KS * A_BLK / NW;    // direct path: blocks per wavefront
+    static constexpr int B_BLK_W = KS * B_BLK / NW;
+    static constexpr int ACC = FM * FN * 16;           // accumulators per lane
+    static constexpr int RED = (KS - 1) * NWO * ACC * 64;  // floats for the k-slice reduction
+    static constexpr int SMEM = (2 * STAGE > RED) ? 2 * STAGE : RED;
     static_assert(WM % 32 == 0 && WN % 32 == 0, "tile shape");
     static_assert(BK == 16 || BK == 32, "the chunk permutation covers 4 or 8 chunks per row");
-    static_assert(BM * CPR % NT == 0 && (BK * BN / 4) % NT == 0, "register staging split");
-    static_assert(A_SZ % (256 * NW) == 0 && B_SZ % (256 * NW) == 0, "direct staging split");
+    static_assert((KS * BM * CPR) % NT == 0 && (KS * BK * BN / 4) % NT == 0, "register staging split");
+    static_assert(A_SZ % 256 == 0 && B_SZ % 256 == 0, "whole 1 KB blocks");
+    static_assert((KS * A_BLK) % NW == 0 && (KS * B_BLK) % NW == 0, "direct staging split");
     static_assert(TRANS_B || 256 % BN == 0, "op(B)=B rows must tile a 1 KB block");
-    static_assert(2 * STAGE * 4 <= 160 * 1024, "LDS budget");
+    static_assert(SMEM * 4 <= 160 * 1024, "LDS budget");
     static_assert(G % 2 == 0, "the fragment ping-pong needs an even number of k-groups");
+};
+
+// What one wavefront does: its k-slice and its place in the output tile.
+template <class Gm>
+struct Role {
+    int lane, l32, hi, slice, wo, wm, wn;
+    __device__ __forceinline__ Role()
+    {
+        const int wave = wave_id();
+        lane = threadIdx.x & 63;
+        l32 = lane & 31;
+        hi = lane >> 5;
+        slice = wave / Gm::NWO;
+        wo = wave % Gm::NWO;
+        wm = wo / Gm::WGN;
+        wn = wo % Gm::WGN;
+    }
 };
 
 // Physical 16-byte chunk of logical chunk c in row r of a k-contiguous tile.
@@ -227,16 +255,16 @@ __device__ __forceinline__ void mfma_group(f32x16 (&acc)[Gm::FM][Gm::FN], const 
     mfma_steps<Gm, TRANS_B>(acc, f, 0, 4);
 }
 
-// Register staging of one k-tile: masked (or, for interior tiles and full
-// k-tiles, plain) loads of the tile into registers, then stores in LDS layout.
+// Register staging of one LDS stage (KS k-tiles): masked (or, for interior
+// tiles and full stages, plain) loads into registers, then stores in LDS layout.
 template <class Gm, bool TRANS_B, bool VEC>
 struct RegStage {
     static constexpr int CA = Gm::CA, CB = Gm::CB, CPR = Gm::CPR, BN4 = Gm::BN / 4;
     const float *pa[CA];
     const float *pb[CB];
-    int ra_row[CA], ra_c[CA], rb_row[CB], rb_c[CB];
+    int ra_row[CA], ra_k[CA], ra_lds[CA];   // row in tile, k within the stage, LDS offset
+    int rb_row[CB], rb_k[CB], rb_lds[CB];   // (B: n row / k row, k / n offset, LDS offset)
     f32x4 ra[CA], rb[CB];
-    int64_t b_kstep;
 
     __device__ __forceinline__ void init(const GemmArgs &a, int m0, int n0)
     {
@@ -244,70 +272,72 @@ struct RegStage {
 #pragma unroll
         for (int i = 0; i < CA; ++i) {
             const int q = tid + i * Gm::NT;
-            ra_row[i] = q / CPR;
-            ra_c[i] = q % CPR;
-            pa[i] = a.A + (int64_t)(m0 + ra_row[i]) * a.lda + 4 * ra_c[i];
+            const int sl = q / (Gm::BM * CPR), q2 = q % (Gm::BM * CPR);
+            const int c = q2 % CPR;
+            ra_row[i] = q2 / CPR;
+            ra_k[i] = sl * Gm::BK + 4 * c;
+            ra_lds[i] = sl * Gm::SLICE + koff<CPR>(ra_row[i], c);
+            pa[i] = a.A + (int64_t)(m0 + ra_row[i]) * a.lda + ra_k[i];
         }
 #pragma unroll
         for (int i = 0; i < CB; ++i) {
             const int q = tid + i * Gm::NT;
             if constexpr (TRANS_B) {
-                rb_row[i] = q / CPR;          // n within the tile
-                rb_c[i] = q % CPR;            // k chunk
-                pb[i] = a.B + (int64_t)(n0 + rb_row[i]) * a.ldb + 4 * rb_c[i];
+                const int sl = q / (Gm::BN * CPR), q2 = q % (Gm::BN * CPR);
+                const int c = q2 % CPR;
+                rb_row[i] = q2 / CPR;                        // n within the tile
+                rb_k[i] = sl * Gm::BK + 4 * c;               // k within the stage
+                rb_lds[i] = sl * Gm::SLICE + Gm::A_SZ + koff<CPR>(rb_row[i], c);
+                pb[i] = a.B + (int64_t)(n0 + rb_row[i]) * a.ldb + rb_k[i];
             } else {
-                rb_row[i] = q / BN4;          // k within the tile
-                rb_c[i] = q % BN4;            // n chunk
-                pb[i] = a.B + (int64_t)rb_row[i] * a.ldb + n0 + 4 * rb_c[i];
+                const int sl = q / (Gm::BK * BN4), q2 = q % (Gm::BK * BN4);
+                const int kr = q2 / BN4;
+                rb_row[i] = sl * Gm::BK + kr;                // k within the stage
+                rb_k[i] = 4 * (q2 % BN4);                    // n within the tile
+                rb_lds[i] = sl * Gm::SLICE + Gm::A_SZ + kr * Gm::BN + rb_k[i];
+                pb[i] = a.B + (int64_t)rb_row[i] * a.ldb + n0 + rb_k[i];
             }
         }
-        b_kstep = TRANS_B ? (int64_t)Gm::BK : (int64_t)Gm::BK * a.ldb;
     }
 
-    // MASKED=false: the tile lies inside M x N and k-tile kt is full.
+    // MASKED=false: the tile lies inside M x N and stage kt is full.
     template <bool MASKED>
     __device__ __forceinline__ void load(const GemmArgs &a, int m0, int n0, int kt)
     {
-        const int k0 = kt * Gm::BK;
+        const int k0 = kt * Gm::KT;
 #pragma unroll
         for (int i = 0; i < CA; ++i)
-            ra[i] = load4<VEC, MASKED>(pa[i] + (int64_t)k0, m0 + ra_row[i] < a.M, k0 + 4 * ra_c[i], a.K);
+            ra[i] = load4<VEC, MASKED>(pa[i] + (int64_t)k0, m0 + ra_row[i] < a.M, k0 + ra_k[i], a.K);
 #pragma unroll
         for (int i = 0; i < CB; ++i) {
             if constexpr (TRANS_B)
-                rb[i] = load4<VEC, MASKED>(pb[i] + (int64_t)kt * b_kstep, n0 + rb_row[i] < a.N,
-                                           k0 + 4 * rb_c[i], a.K);
+                rb[i] = load4<VEC, MASKED>(pb[i] + (int64_t)k0, n0 + rb_row[i] < a.N, k0 + rb_k[i], a.K);
             else
-                rb[i] = load4<VEC, MASKED>(pb[i] + (int64_t)kt * b_kstep, k0 + rb_row[i] < a.K,
-                                           n0 + 4 * rb_c[i], a.N);
+                rb[i] = load4<VEC, MASKED>(pb[i] + (int64_t)k0 * a.ldb, k0 + rb_row[i] < a.K, n0 + rb_k[i], a.N);
         }
     }
 
-    __device__ __forceinline__ void store(float *As, float *Bs) const
+    __device__ __forceinline__ void store(float *stage) const
     {
 #pragma unroll
         for (int i = 0; i < CA; ++i)
-            *reinterpret_cast<f32x4 *>(&As[koff<CPR>(ra_row[i], ra_c[i])]) = ra[i];
+            *reinterpret_cast<f32x4 *>(&stage[ra_lds[i]]) = ra[i];
 #pragma unroll
-        for (int i = 0; i < CB; ++i) {
-            if constexpr (TRANS_B)
-                *reinterpret_cast<f32x4 *>(&Bs[koff<CPR>(rb_row[i], rb_c[i])]) = rb[i];
-            else
-                *reinterpret_cast<f32x4 *>(&Bs[rb_row[i] * Gm::BN + 4 * rb_c[i]]) = rb[i];
-        }
+        for (int i = 0; i < CB; ++i)
+            *reinterpret_cast<f32x4 *>(&stage[rb_lds[i]]) = rb[i];
     }
 };
 
-// Direct staging of full k-tiles: each wavefront fills A_BLK_W + B_BLK_W 1 KB
+// Direct staging of full stages: each wavefront fills A_BLK_W + B_BLK_W 1 KB
 // LDS blocks with global_load_lds_dwordx4 (lane L writes bytes 16L..16L+15 of a
 // block).  Per-lane sources are 32-bit float offsets from the tile's first
 // element, valid because the host allows this path only when a tile's extent
 // fits (rows x leading dimension < 2^31).
 template <class Gm, bool TRANS_B>
 struct DirectStage {
-    static constexpr int CPR = Gm::CPR, RPB = 256 / Gm::BK;  // k-rows of A per block
+    static constexpr int CPR = Gm::CPR, RPB = 256 / Gm::BK;  // k-contiguous rows per block
     uint32_t a_off[Gm::A_BLK_W], b_off[Gm::B_BLK_W];
-    int a_blk0, b_blk0;
+    int a_lds[Gm::A_BLK_W], b_lds[Gm::B_BLK_W];   // LDS float offsets within a stage (wave-uniform)
     const float *a_base;
     const float *b_base;
     int64_t b_kstep;
@@ -315,58 +345,94 @@ struct DirectStage {
     __device__ __forceinline__ void init(const GemmArgs &a, int m0, int n0)
     {
         const int lane = threadIdx.x & 63, wave = wave_id();
-        a_blk0 = wave * Gm::A_BLK_W;
-        b_blk0 = wave * Gm::B_BLK_W;
 #pragma unroll
         for (int j = 0; j < Gm::A_BLK_W; ++j) {
-            const int r = (a_blk0 + j) * RPB + lane / CPR;
+            const int b = wave * Gm::A_BLK_W + j;
+            const int sl = b / Gm::A_BLK, lb = b % Gm::A_BLK;
+            const int r = lb * RPB + lane / CPR;
             const int c = (lane % CPR) ^ swz<CPR>(r);
-            a_off[j] = (uint32_t)(r * a.lda + 4 * c);
+            a_off[j] = (uint32_t)(r * a.lda + sl * Gm::BK + 4 * c);
+            a_lds[j] = sl * Gm::SLICE + lb * 256;
         }
 #pragma unroll
         for (int j = 0; j < Gm::B_BLK_W; ++j) {
+            const int b = wave * Gm::B_BLK_W + j;
+            const int sl = b / Gm::B_BLK, lb = b % Gm::B_BLK;
             if constexpr (TRANS_B) {
-                const int r = (b_blk0 + j) * RPB + lane / CPR;   // n within the tile
+                const int r = lb * RPB + lane / CPR;   // n within the tile
                 const int c = (lane % CPR) ^ swz<CPR>(r);
-                b_off[j] = (uint32_t)(r * a.ldb + 4 * c);
+                b_off[j] = (uint32_t)(r * a.ldb + sl * Gm::BK + 4 * c);
             } else {
-                const int e = (b_blk0 + j) * 256 + 4 * lane;     // float index in the [BK][BN] tile
-                b_off[j] = (uint32_t)((e / Gm::BN) * a.ldb + e % Gm::BN);
+                const int e = lb * 256 + 4 * lane;     // float index in the [BK][BN] slice tile
+                b_off[j] = (uint32_t)((sl * Gm::BK + e / Gm::BN) * a.ldb + e % Gm::BN);
             }
+            b_lds[j] = sl * Gm::SLICE + Gm::A_SZ + lb * 256;
         }
         a_base = a.A + (int64_t)m0 * a.lda;
         b_base = TRANS_B ? a.B + (int64_t)n0 * a.ldb : a.B + n0;
-        b_kstep = TRANS_B ? (int64_t)Gm::BK : (int64_t)Gm::BK * a.ldb;
+        b_kstep = TRANS_B ? (int64_t)Gm::KT : (int64_t)Gm::KT * a.ldb;
     }
 
-    static constexpr int NLOAD = Gm::A_BLK_W + Gm::B_BLK_W;  // loads per wavefront per k-tile
-
-    // Loads j0 .. j1-1 of k-tile kt (A blocks first, then B blocks).
-    __device__ __forceinline__ void issue(int kt, float *As, float *Bs, int j0 = 0, int j1 = NLOAD) const
+    __device__ __forceinline__ void issue(int kt, float *stage) const
     {
-        const float *ak = a_base + (int64_t)kt * Gm::BK;
+        const float *ak = a_base + (int64_t)kt * Gm::KT;
         const float *bk = b_base + (int64_t)kt * b_kstep;
 #pragma unroll
         for (int j = 0; j < Gm::A_BLK_W; ++j)
-            if (j >= j0 && j < j1)
-                __builtin_amdgcn_global_load_lds(ak + a_off[j], (lds_void *)(As + (a_blk0 + j) * 256), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(ak + a_off[j], (lds_void *)(stage + a_lds[j]), 16, 0, 0);
 #pragma unroll
         for (int j = 0; j < Gm::B_BLK_W; ++j)
-            if (Gm::A_BLK_W + j >= j0 && Gm::A_BLK_W + j < j1)
-                __builtin_amdgcn_global_load_lds(bk + b_off[j], (lds_void *)(Bs + (b_blk0 + j) * 256), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(bk + b_off[j], (lds_void *)(stage + b_lds[j]), 16, 0, 0);
     }
 };
 
+// KS > 1: k-slices 1..KS-1 leave their accumulators in LDS and slice 0 adds them
+// in slice order (a fixed order, so results are reproducible).  Called by every
+// wavefront; returns true for the wavefronts that write the output.
+template <class Gm>
+__device__ __forceinline__ bool reduce_slices(f32x16 (&acc)[Gm::FM][Gm::FN], float *smem, const Role<Gm> &ro)
+{
+    if constexpr (Gm::KS == 1) {
+        return true;
+    } else {
+        __syncthreads();  // every wavefront is done with the stage buffers
+        if (ro.slice > 0) {
+            float *dst = smem + ((ro.slice - 1) * Gm::NWO + ro.wo) * Gm::ACC * 64 + ro.lane;
+#pragma unroll
+            for (int fm = 0; fm < Gm::FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < Gm::FN; ++fn)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        dst[((fm * Gm::FN + fn) * 16 + r) * 64] = acc[fm][fn][r];
+        }
+        __syncthreads();
+        if (ro.slice > 0)
+            return false;
+#pragma unroll
+        for (int s = 1; s < Gm::KS; ++s) {
+            const float *src = smem + ((s - 1) * Gm::NWO + ro.wo) * Gm::ACC * 64 + ro.lane;
+#pragma unroll
+            for (int fm = 0; fm < Gm::FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < Gm::FN; ++fn)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        acc[fm][fn][r] += src[((fm * Gm::FN + fn) * 16 + r) * 64];
+        }
+        return true;
+    }
+}
+
 template <class Gm, bool TRANS_B, bool FULL>
-__device__ __forceinline__ void epilogue(const GemmArgs &a, const f32x16 (&acc)[Gm::FM][Gm::FN], int m0, int n0)
+__device__ __forceinline__ void epilogue(const GemmArgs &a, const f32x16 (&acc)[Gm::FM][Gm::FN], int m0, int n0,
+                                         const Role<Gm> &ro)
 {
     // Accumulator register r of a 32x32 block holds row 8*(r/4) + 4*hi + (r%4)
     // and column l32 of that block.
     typedef typename vec_of<Gm::IL>::type bvec;
     constexpr int IL = Gm::IL;
-    const int lane = threadIdx.x & 63, wave = wave_id();
-    const int l32 = lane & 31, hi = lane >> 5;
-    const int wm = wave / Gm::WGN, wn = wave % Gm::WGN;
+    const int l32 = ro.l32, hi = ro.hi, wm = ro.wm, wn = ro.wn;
     const uintptr_t cbase = reinterpret_cast<uintptr_t>(a.C);
     const bool cvec = IL > 1 && (cbase % (4 * IL)) == 0 && (a.ldc % IL) == 0;
 #pragma unroll
@@ -426,67 +492,84 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const f32x16 (&acc)[
     }
 }
 
+// One k-group of one stage: the first MFMA step runs on fragments read a whole
+// group earlier, before any new LDS traffic (so the wait in front of it never
+// covers fresh reads); then `next()` issues the next fragments (or the barrier
+// and the next stage's first fragments); then the other three steps.
+template <class Gm, bool TRANS_B, class Next>
+__device__ __forceinline__ void group_step(f32x16 (&acc)[Gm::FM][Gm::FN], const Frags<Gm, TRANS_B> &cur, Next next)
+{
+    mfma_steps<Gm, TRANS_B>(acc, cur, 0, 1);
+    pin_order();
+    next();
+    pin_order();
+    mfma_steps<Gm, TRANS_B>(acc, cur, 1, 4);
+}
+
+template <class Gm>
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[Gm::FM][Gm::FN])
+{
+#pragma unroll
+    for (int i = 0; i < Gm::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < Gm::FN; ++j)
+            acc[i][j] = f32x16{0};
+}
+
 // Register-staged k-loop.  FULL: the tile lies inside M x N (only the K tail
 // needs masks).
 template <class Gm, bool TRANS_B, bool VEC, bool FULL>
 __device__ __forceinline__ void gemm_tile_regs(const GemmArgs &a, float *smem, int m0, int n0)
 {
     constexpr int G = Gm::G;
-    const int lane = threadIdx.x & 63, wave = wave_id();
-    const int l32 = lane & 31, hi = lane >> 5;
-    const int wm = wave / Gm::WGN, wn = wave % Gm::WGN;
+    const Role<Gm> ro;
+    const int sl_off = ro.slice * Gm::SLICE;
 
     RegStage<Gm, TRANS_B, VEC> st;
     st.init(a, m0, n0);
     auto gload = [&](int kt) {
-        if (FULL && (kt + 1) * Gm::BK <= a.K)
+        if (FULL && (kt + 1) * Gm::KT <= a.K)
             st.template load<false>(a, m0, n0, kt);
         else
             st.template load<true>(a, m0, n0, kt);
     };
 
     f32x16 acc[Gm::FM][Gm::FN];
-#pragma unroll
-    for (int i = 0; i < Gm::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < Gm::FN; ++j)
-            acc[i][j] = f32x16{0};
+    zero_acc<Gm>(acc);
 
-    const int nk = (a.K + Gm::BK - 1) / Gm::BK;
+    const int nk = (a.K + Gm::KT - 1) / Gm::KT;
     Frags<Gm, TRANS_B> f[2];
     gload(0);
-    st.store(smem, smem + Gm::A_SZ);
+    st.store(smem);
     if (nk > 1)
         gload(1);
     __syncthreads();
-    read_frags<Gm, TRANS_B>(f[0], smem, smem + Gm::A_SZ, 0, wm, wn, l32, hi);
+    read_frags<Gm, TRANS_B>(f[0], smem + sl_off, smem + sl_off + Gm::A_SZ, 0, ro.wm, ro.wn, ro.l32, ro.hi);
 
     for (int t = 0; t < nk; ++t) {
-        const float *As = smem + (t & 1) * Gm::STAGE;
+        const float *As = smem + (t & 1) * Gm::STAGE + sl_off;
         const float *Bs = As + Gm::A_SZ;
-        float *An = smem + ((t + 1) & 1) * Gm::STAGE;
+        float *Sn = smem + ((t + 1) & 1) * Gm::STAGE;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            // First MFMA step on fragments read a whole group earlier, before any
-            // new LDS traffic, so the wait in front of it never covers fresh reads.
-            mfma_steps<Gm, TRANS_B>(acc, f[g & 1], 0, 1);
-            pin_order();
-            if (g == 0 && t + 1 < nk) {
-                st.store(An, An + Gm::A_SZ);   // tile t+1 into the free buffer
-                if (t + 2 < nk)
-                    gload(t + 2);
-            }
-            if (g + 1 < G) {
-                read_frags<Gm, TRANS_B>(f[(g + 1) & 1], As, Bs, g + 1, wm, wn, l32, hi);
-            } else if (t + 1 < nk) {
-                __syncthreads();
-                read_frags<Gm, TRANS_B>(f[G & 1], An, An + Gm::A_SZ, 0, wm, wn, l32, hi);
-            }
-            pin_order();
-            mfma_steps<Gm, TRANS_B>(acc, f[g & 1], 1, 4);
+            group_step<Gm, TRANS_B>(acc, f[g & 1], [&] {
+                if (g == 0 && t + 1 < nk) {
+                    st.store(Sn);   // stage t+1 into the free buffer
+                    if (t + 2 < nk)
+                        gload(t + 2);
+                }
+                if (g + 1 < G) {
+                    read_frags<Gm, TRANS_B>(f[(g + 1) & 1], As, Bs, g + 1, ro.wm, ro.wn, ro.l32, ro.hi);
+                } else if (t + 1 < nk) {
+                    __syncthreads();
+                    read_frags<Gm, TRANS_B>(f[G & 1], Sn + sl_off, Sn + sl_off + Gm::A_SZ, 0, ro.wm, ro.wn,
+                                            ro.l32, ro.hi);
+                }
+            });
         }
     }
-    epilogue<Gm, TRANS_B, FULL>(a, acc, m0, n0);
+    if (reduce_slices<Gm>(acc, smem, ro))
+        epilogue<Gm, TRANS_B, FULL>(a, acc, m0, n0, ro);
 }
 
 // Direct-staged k-loop for interior tiles with 16-byte aligned operands.
@@ -494,81 +577,77 @@ template <class Gm, bool TRANS_B>
 __device__ __forceinline__ void gemm_tile_direct(const GemmArgs &a, float *smem, int m0, int n0)
 {
     constexpr int G = Gm::G;
-    const int lane = threadIdx.x & 63, wave = wave_id();
-    const int l32 = lane & 31, hi = lane >> 5;
-    const int wm = wave / Gm::WGN, wn = wave % Gm::WGN;
+    const Role<Gm> ro;
+    const int sl_off = ro.slice * Gm::SLICE;
     float *buf0 = smem, *buf1 = smem + Gm::STAGE;
 
     f32x16 acc[Gm::FM][Gm::FN];
-#pragma unroll
-    for (int i = 0; i < Gm::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < Gm::FN; ++j)
-            acc[i][j] = f32x16{0};
+    zero_acc<Gm>(acc);
 
-    const int nf = a.K / Gm::BK;  // full k-tiles
+    const int nf = a.K / Gm::KT;  // full stages
     Frags<Gm, TRANS_B> f[2];
 
     DirectStage<Gm, TRANS_B> ds;
     ds.init(a, m0, n0);
     if (nf > 0)
-        ds.issue(0, buf0, buf0 + Gm::A_SZ);
+        ds.issue(0, buf0);
 
-    // Partial last k-tile first (the order of the k sum is free): registers with
-    // zero fill, through buffer 1, while tile 0 lands in buffer 0.
-    if (nf * Gm::BK < a.K) {
+    // Partial last stage first (the order of the k sum is free): registers with
+    // zero fill, through buffer 1, while stage 0 lands in buffer 0.
+    if (nf * Gm::KT < a.K) {
         RegStage<Gm, TRANS_B, true> st;
         st.init(a, m0, n0);
         st.template load<true>(a, m0, n0, nf);
-        st.store(buf1, buf1 + Gm::A_SZ);
+        st.store(buf1);
         __syncthreads();
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            read_frags<Gm, TRANS_B>(f[0], buf1, buf1 + Gm::A_SZ, g, wm, wn, l32, hi);
+            read_frags<Gm, TRANS_B>(f[0], buf1 + sl_off, buf1 + sl_off + Gm::A_SZ, g, ro.wm, ro.wn, ro.l32, ro.hi);
             mfma_group<Gm, TRANS_B>(acc, f[0]);
         }
     }
     if (nf > 0) {
-        __syncthreads();  // tile 0 has landed (and buffer 1 is free again)
-        read_frags<Gm, TRANS_B>(f[0], buf0, buf0 + Gm::A_SZ, 0, wm, wn, l32, hi);
+        __syncthreads();  // stage 0 has landed (and buffer 1 is free again)
+        read_frags<Gm, TRANS_B>(f[0], buf0 + sl_off, buf0 + sl_off + Gm::A_SZ, 0, ro.wm, ro.wn, ro.l32, ro.hi);
         for (int t = 0; t < nf; ++t) {
-            const float *As = (t & 1) ? buf1 : buf0;
+            const float *As = ((t & 1) ? buf1 : buf0) + sl_off;
             const float *Bs = As + Gm::A_SZ;
-            float *An = (t & 1) ? buf0 : buf1;
-            // All loads of tile t+1 go out first: measured against spreading them
+            float *Sn = (t & 1) ? buf0 : buf1;
+            // All loads of stage t+1 go out first: measured against spreading them
             // over the MFMA steps, issuing them together at the top is faster.
             if (t + 1 < nf) {
-                ds.issue(t + 1, An, An + Gm::A_SZ);
+                ds.issue(t + 1, Sn);
                 pin_order();
             }
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                mfma_steps<Gm, TRANS_B>(acc, f[g & 1], 0, 1);
-                pin_order();
-                if (g + 1 < G) {
-                    read_frags<Gm, TRANS_B>(f[(g + 1) & 1], As, Bs, g + 1, wm, wn, l32, hi);
-                } else if (t + 1 < nf) {
-                    __syncthreads();  // this wavefront's direct loads, then everyone's
-                    read_frags<Gm, TRANS_B>(f[G & 1], An, An + Gm::A_SZ, 0, wm, wn, l32, hi);
-                }
-                pin_order();
-                mfma_steps<Gm, TRANS_B>(acc, f[g & 1], 1, 4);
+                group_step<Gm, TRANS_B>(acc, f[g & 1], [&] {
+                    if (g + 1 < G) {
+                        read_frags<Gm, TRANS_B>(f[(g + 1) & 1], As, Bs, g + 1, ro.wm, ro.wn, ro.l32, ro.hi);
+                    } else if (t + 1 < nf) {
+                        __syncthreads();  // this wavefront's direct loads, then everyone's
+                        read_frags<Gm, TRANS_B>(f[G & 1], Sn + sl_off, Sn + sl_off + Gm::A_SZ, 0, ro.wm, ro.wn,
+                                                ro.l32, ro.hi);
+                    }
+                });
             }
         }
     }
-    epilogue<Gm, TRANS_B, true>(a, acc, m0, n0);
+    if (reduce_slices<Gm>(acc, smem, ro))
+        epilogue<Gm, TRANS_B, true>(a, acc, m0, n0, ro);
 }
 
 // GD: geometry of the direct path; GR: geometry of the register path (same
-// workgroup tile and wavefront layout, possibly a shorter k-tile so the register
-// staging fits next to the accumulators).
+// workgroup tile, wavefront layout and k-split, possibly a shorter k-tile so
+// the register staging fits next to the accumulators).
 template <class GD, class GR, bool TRANS_B, bool VEC>
 __global__ __launch_bounds__(GD::NT) __attribute__((amdgpu_waves_per_eu(GD::OCC)))
 void sgemm_mfma_kernel(GemmArgs a)
 {
-    static_assert(GD::BM == GR::BM && GD::BN == GR::BN && GD::NT == GR::NT && GD::WGN == GR::WGN,
+    static_assert(GD::BM == GR::BM && GD::BN == GR::BN && GD::NT == GR::NT && GD::WGN == GR::WGN &&
+                      GD::KS == GR::KS,
                   "both paths share the workgroup tile");
-    constexpr int SMEM = 2 * (GD::STAGE > GR::STAGE ? GD::STAGE : GR::STAGE);
+    constexpr int SMEM = GD::SMEM > GR::SMEM ? GD::SMEM : GR::SMEM;
     __shared__ __attribute__((aligned(1024))) float smem[SMEM];
     const int nbm = (a.M + GD::BM - 1) / GD::BM, nbn = (a.N + GD::BN - 1) / GD::BN;
     int tile_m, tile_n;
@@ -601,15 +680,15 @@ TileShape tile_shape(int kid)
     }
 }
 
-template <int BM, int BN, int BKD, int BKR, int WGM, int WGN, int OCC>
+template <int BM, int BN, int BKD, int BKR, int WGM, int WGN, int OCC, int KS>
 static void launch_cfg(const GemmArgs &a, bool transB, bool vec, hipStream_t stream)
 {
     const int64_t blocks = ceil_div(a.M, BM) * ceil_div(a.N, BN);
-    const dim3 grid((unsigned)blocks), block(64 * WGM * WGN);
-    typedef Geo<BM, BN, BKD, WGM, WGN, OCC, true> GDT;
-    typedef Geo<BM, BN, BKR, WGM, WGN, OCC, true> GRT;
-    typedef Geo<BM, BN, BKD, WGM, WGN, OCC, false> GDN;
-    typedef Geo<BM, BN, BKR, WGM, WGN, OCC, false> GRN;
+    const dim3 grid((unsigned)blocks), block(64 * WGM * WGN * KS);
+    typedef Geo<BM, BN, BKD, WGM, WGN, OCC, true, KS> GDT;
+    typedef Geo<BM, BN, BKR, WGM, WGN, OCC, true, KS> GRT;
+    typedef Geo<BM, BN, BKD, WGM, WGN, OCC, false, KS> GDN;
+    typedef Geo<BM, BN, BKR, WGM, WGN, OCC, false, KS> GRN;
     if (transB) {
         if (vec)
             sgemm_mfma_kernel<GDT, GRT, true, true><<<grid, block, 0, stream>>>(a);
@@ -627,9 +706,9 @@ hipError_t launch_mfma(const GemmArgs &a, int kid, bool transB, bool vec, hipStr
 {
     switch (kid) {
 #ifndef SGEMM_MFMA_EXPERIMENT
-    case KID_MFMA_L: launch_cfg<256, 256, 32, 16, 4, 2, 2>(a, transB, vec, stream); break;
-    case KID_MFMA_M: launch_cfg<128, 128, 32, 32, 2, 2, 2>(a, transB, vec, stream); break;
-    case KID_MFMA_S: launch_cfg<64, 64, 32, 32, 2, 2, 4>(a, transB, vec, stream); break;
+    case KID_MFMA_L: launch_cfg<256, 256, 32, 16, 4, 2, 2, 1>(a, transB, vec, stream); break;
+    case KID_MFMA_M: launch_cfg<128, 128, 32, 32, 2, 2, 2, 2>(a, transB, vec, stream); break;
+    case KID_MFMA_S: launch_cfg<64, 64, 32, 32, 2, 2, 4, 1>(a, transB, vec, stream); break;
 #else
     SGEMM_MFMA_EXPERIMENT
 #endif

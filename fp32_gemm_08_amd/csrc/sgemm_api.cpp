@@ -125,7 +125,7 @@ const char *kernel_label(int kid)
     case KID_TILED_NOPAD: return "lds_tiled_16x16_pad0";
     case KID_REGBLOCK: return "regblock_128x128x8_t8x8";
     case KID_MFMA_L: return "mfma_256x256x32_w4x2";
-    case KID_MFMA_M: return "mfma_128x128x32_w2x2";
+    case KID_MFMA_M: return "mfma_128x128x32_w2x2_ks2";
     case KID_MFMA_S: return "mfma_64x64x32_w2x2";
     default: return "unknown";
     }

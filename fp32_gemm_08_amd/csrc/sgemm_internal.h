@@ -32,7 +32,7 @@ enum KernelId : int {
     KID_TILED_NOPAD = 21,
     KID_REGBLOCK = 30,
     KID_MFMA_L = 40,        // 256 x 256 macro tile, 8 wavefronts
-    KID_MFMA_M = 41,        // 128 x 128, 4 wavefronts
+    KID_MFMA_M = 41,        // 128 x 128, 8 wavefronts: 2 x 2 over the tile x 2 over k
     KID_MFMA_S = 42,        // 64 x 64, 4 wavefronts
 };
 

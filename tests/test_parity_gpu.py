@@ -173,6 +173,39 @@ def test_degenerate_shapes(oracle_lib, algo):
         assert_parity(Dg[:, :N], D, S, K, f"degenerate {M}x{N}x{K} t{t}/{algo}")
 
 
+# (M, N, K, transB, lda): aligned operands with ragged edges and K tails (direct
+# path for interior tiles), unaligned leading dimensions (register path), K equal
+# to one LDS stage, and K shorter than one stage (only the zero-filled tail).
+MID_SHAPES = [(2000, 2100, 1004, 0, None), (2000, 2100, 1004, 1, None), (2048, 2048, 999, 0, None),
+              (2049, 2051, 517, 1, 521), (2048, 2304, 64, 0, None), (2048, 2304, 40, 1, None)]
+
+
+@pytest.mark.parametrize("shape", MID_SHAPES, ids=lambda s: "x".join(str(v) for v in s[:4]))
+def test_mid_tile_edges_and_tails(oracle_lib, shape):
+    """Shapes that the shape-based choice sends to the 128x128 tile whose k-range
+    is split over two wavefront groups: ragged edges in M and N, K tails (K %
+    32 != 0), op(B) = B^T, and an unaligned leading dimension (register path)."""
+    M, N, K, t, lda = shape
+    st, kid, tm, tn, name = lib.sgemm_f32_plan(0, M, N, K, 1.0, 1 << 32, lda or K, 1 << 40, K if t else N, t,
+                                              0.5, 1 << 44, N)
+    assert kid == 41, name
+    case = make_case(M, N, K, trans_b=t, alpha=1.25, beta=0.5, dist="uniform", seed=M + K, lda=lda)
+    st, Dg = run_case(case, "auto", guard=False)
+    assert st == 0
+    rows = sample_rows(M, n=24, seed=K, tile=128)
+    D, S = oracle_rows(oracle_lib, case, rows)
+    assert_parity(Dg[rows, :N], D, S, K, f"mid {M}x{N}x{K} t{t} lda={case.lda}")
+
+
+def test_mid_tile_integers_bit_exact(oracle_lib):
+    case = make_case(2000, 2100, 1004, trans_b=1, alpha=1.5, beta=-0.5, dist="int2", seed=9)
+    st, Dg = run_case(case, "auto", guard=False)
+    assert st == 0
+    rows = sample_rows(2000, n=16, seed=1, tile=128)
+    D, _ = oracle_rows(oracle_lib, case, rows)
+    assert np.array_equal(Dg[rows, :2100], D.astype(np.float32))
+
+
 def test_product_free_paths(oracle_lib):
     """alpha == 0 or K == 0: C <- beta*C; beta == 1 leaves C untouched bitwise;
     beta == 0 zeroes C without reading it (NaN in C)."""
