@@ -16,6 +16,14 @@ FP64 CPU oracle's rate on a bounded sample of the same workload.
 Other modes:
   --copy-calibration   run a plain device copy of known size (for scaling the
                        FETCH_SIZE / WRITE_SIZE counters) and exit.
+  --op transpose       the library's second operation, the out-of-place FP32
+                       transpose (default workload 4096x4096, the size the
+                       transpose page measures): one JSON line in GB/s against
+                       the HBM roofline.  Each step transposes the next of
+                       several source/destination pairs whose total exceeds the
+                       256 MB Infinity Cache, so every step streams from HBM.
+  --sweep              every algorithm on every workload of the chosen --op,
+                       as a table.
 """
 import argparse
 import hashlib
@@ -33,31 +41,35 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "FP32 GEMM TFLOP/s at 4096³ (and % of MI355X FP32 peak), 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mfma_c4_4096.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "fp32_gemm_08_amd", "csrc", f) for f in ("k_mfma.hip", "sgemm_internal.h")]
+TRANSPOSE_METRIC = "FP32 transpose effective bandwidth GB/s at 4096x4096 (and % of MI355X HBM peak), 1 GPU"
+TRANSPOSE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_transpose_t_4096.txt")
+TRANSPOSE_SOURCES = [os.path.join(ROOT, "fp32_gemm_08_amd", "csrc", f)
+                     for f in ("k_transpose.hip", "transpose_internal.h", "sgemm_internal.h")]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=KERNEL_SOURCES):
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic():
+def read_traffic(path=TRAFFIC_FILE, sources=KERNEL_SOURCES):
     """HBM bytes per launch from the committed counter summary, if it was taken
     on the current kernel source (else None)."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(path):
         return None
     vals = {}
-    for line in open(TRAFFIC_FILE, encoding="utf-8"):
+    for line in open(path, encoding="utf-8"):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash(sources):
         return None
     try:
         return float(vals["traffic_bytes_per_launch"])
@@ -175,17 +187,202 @@ def sweep(algos=("naive", "lds_tiled", "lds_tiled_nopad", "regblock", "mfma")):
     return rows
 
 
+def transpose_cpu_baseline(src, rows, cols, D_gpu_host, target_s):
+    """Time the transpose oracle on the same workload, repeated for about
+    ``target_s`` seconds, and check its result against the GPU's bit for bit."""
+    import numpy as np
+
+    import oracle
+    t0 = time.perf_counter()
+    want = oracle.transpose(src, rows, cols)
+    t1 = time.perf_counter() - t0
+    reps = max(1, int(target_s / max(t1, 1e-6)))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle.transpose(src, rows, cols)
+    t = time.perf_counter() - t0
+    same = bool(np.array_equal(want.view(np.uint32), np.ascontiguousarray(D_gpu_host).view(np.uint32)))
+    return {
+        "value": 8.0 * rows * cols * reps / t / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"the whole {rows}x{cols} transpose, {reps} times in {t:.1f} s "
+                  "(numpy row-by-row copy, one thread)",
+        "seconds": t,
+        "sample_parity": {"ok": same, "bit_exact": same},
+    }
+
+
+def _transpose_timed(lib, torch, algo_id, rows, cols, pairs, steps, warmup, stream):
+    """Back-to-back transposes rotating over ``pairs``; returns (event span, wall)."""
+    sp = stream.cuda_stream
+    R = len(pairs)
+
+    def step(k):
+        src, dst = pairs[k % R]
+        s = lib.sgemm_f32_transpose_algo(algo_id, rows, cols, src.data_ptr(), cols, dst.data_ptr(), rows, sp)
+        if s != 0:
+            raise RuntimeError(lib.sgemm_f32_status_string(s))
+
+    for k in range(warmup):
+        step(k)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for k in range(steps):
+        step(k)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3, time.perf_counter() - t0
+
+
+def _rotation(torch, src_host, rows, cols, dev, min_bytes=1 << 30):
+    """Source/destination pairs (each pair one copy of the workload) totalling at
+    least ``min_bytes``, well above the 256 MB Infinity Cache."""
+    per_pair = 8 * rows * cols
+    R = max(1, -(-min_bytes // per_pair))
+    base = torch.from_numpy(src_host).to(dev)
+    return [(base if i == 0 else base.clone(), torch.empty((cols, rows), dtype=torch.float32, device=dev))
+            for i in range(R)]
+
+
+def bench_transpose(args):
+    import torch
+
+    import fp32_gemm_08_amd as lib
+    from fp32_gemm_08_amd.inputs import TRANSPOSE_CONFIGS, make_transpose_config
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    name = args.config if args.config in TRANSPOSE_CONFIGS else "t_4096"
+    algo_name = args.algo if args.algo in lib.TRANSPOSE_ALGO else "auto"
+    algo = lib.TRANSPOSE_ALGO[algo_name]
+    cfg = TRANSPOSE_CONFIGS[name]
+    rows, cols = cfg["rows"], cfg["cols"]
+    log(f"bench transpose: config={name} algo={algo_name} steps={args.steps} warmup={args.warmup}")
+    src = make_transpose_config(name)
+    pairs = _rotation(torch, src, rows, cols, dev)
+    stream = torch.cuda.current_stream(dev)
+    st, kid, blocks, kname = lib.sgemm_f32_transpose_plan(algo, rows, cols, pairs[0][0].data_ptr(), cols,
+                                                          pairs[0][1].data_ptr(), rows)
+    if st != 0:
+        raise SystemExit(f"plan failed: {lib.sgemm_f32_status_string(st)}")
+    span, wall = _transpose_timed(lib, torch, algo, rows, cols, pairs, args.steps, args.warmup, stream)
+    nbytes = 8.0 * rows * cols            # one read and one write of every element
+    kern_avg = span / args.steps
+    achieved = nbytes / kern_avg / 1e9
+    value = args.steps * nbytes / wall / 1e9
+    log(f"kernel {kname}: avg {kern_avg * 1e6:.2f} us over {args.steps} calls rotating {len(pairs)} pairs")
+    same_pair = None
+    if args.same_pair:
+        # Context only: the same transpose repeated on one pair (source and
+        # destination then stay in the Infinity Cache between calls).
+        span1, _ = _transpose_timed(lib, torch, algo, rows, cols, pairs[:1], args.steps, 20, stream)
+        same_pair = round(nbytes / (span1 / args.steps) / 1e9, 1)
+        log(f"one pair repeated: {span1 / args.steps * 1e6:.2f} us")
+    D_host = pairs[0][1].cpu().numpy()
+    out = {
+        "metric": TRANSPOSE_METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "strong",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "config": {
+            "workload": f"transpose {rows}x{cols} float32 -> {cols}x{rows}, uniform inputs, seed {cfg['seed']}, "
+                        f"{len(pairs)} source/destination pairs in rotation",
+            "name": name, "rows": rows, "cols": cols, "algo": algo_name, "kernel": kname,
+            "workgroups": blocks, "pairs": len(pairs), "same_pair_gbs": same_pair,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": read_traffic(TRANSPOSE_TRAFFIC_FILE, TRANSPOSE_SOURCES)
+            if (name == "t_4096" and algo_name in ("auto", "lds")) else None,
+            "kernel_avg_ms": round(kern_avg * 1e3, 5),
+            "algorithmic_bytes_per_launch": nbytes,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: transpose oracle for ~{args.cpu_seconds:.0f} s")
+        out["cpu_baseline"] = transpose_cpu_baseline(src, rows, cols, D_host, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def sweep_transpose():
+    import torch
+
+    import fp32_gemm_08_amd as lib
+    from fp32_gemm_08_amd.inputs import TRANSPOSE_CONFIGS, make_transpose_config
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream(dev)
+    print("| workload | algorithm | kernel | pairs | avg us (rotating) | GB/s | % of 8000 | avg us (one pair) | GB/s |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for name, cfg in TRANSPOSE_CONFIGS.items():
+        rows, cols = cfg["rows"], cfg["cols"]
+        pairs = _rotation(torch, make_transpose_config(name), rows, cols, dev)
+        nbytes = 8.0 * rows * cols
+        for algo_name in ("naive", "narrow", "lds_nopad", "lds", "auto"):
+            a = lib.TRANSPOSE_ALGO[algo_name]
+            _, _, _, kname = lib.sgemm_f32_transpose_plan(a, rows, cols, pairs[0][0].data_ptr(), cols,
+                                                          pairs[0][1].data_ptr(), rows)
+            span, _ = _transpose_timed(lib, torch, a, rows, cols, pairs, 200, 100, stream)
+            span1, _ = _transpose_timed(lib, torch, a, rows, cols, pairs[:1], 200, 20, stream)
+            t, t1 = span / 200, span1 / 200
+            print(f"| {name} {rows}x{cols} | {algo_name} | {kname} | {len(pairs)} | {t * 1e6:.2f} | "
+                  f"{nbytes / t / 1e9:.0f} | {100 * nbytes / t / 1e9 / HBM_PEAK_GBS:.1f} | {t1 * 1e6:.2f} | "
+                  f"{nbytes / t1 / 1e9:.0f} |", flush=True)
+        # Reference point for what the memory system sustains: torch's own
+        # contiguous device copy of the same bytes over the same rotation.
+        R = len(pairs)
+        flat = [(a.view(-1), b.view(-1)) for a, b in pairs]
+        for k in range(100):
+            flat[k % R][1].copy_(flat[k % R][0])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for k in range(200):
+            flat[k % R][1].copy_(flat[k % R][0])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / 200
+        print(f"| {name} {rows}x{cols} | (device copy, same bytes) | torch copy_ | {R} | {t * 1e6:.2f} | "
+              f"{nbytes / t / 1e9:.0f} | {100 * nbytes / t / 1e9 / HBM_PEAK_GBS:.1f} | | |", flush=True)
+        del pairs, flat
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=200,
                     help="untimed calls first; the clock needs ~0.1 s of load to reach its steady state")
-    ap.add_argument("--config", default="c4_4096")
+    ap.add_argument("--op", choices=("gemm", "transpose"), default="gemm")
+    ap.add_argument("--config", default="c4_4096",
+                    help="workload name (GEMM: c1_128 ... c5_tall; transpose: t_4096 ...)")
     ap.add_argument("--algo", default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--same-pair", action="store_true",
+                    help="transpose: also time one source/destination pair repeated (cache-resident context)")
     ap.add_argument("--sweep", action="store_true",
                     help="time every algorithm on every workload and print a table (no JSON line)")
     args = ap.parse_args()
@@ -200,6 +397,12 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.op == "transpose":
+        if args.sweep:
+            sweep_transpose()
+        else:
+            bench_transpose(args)
         return
     if args.sweep:
         sweep()

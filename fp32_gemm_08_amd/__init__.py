@@ -1,4 +1,5 @@
-"""MI355X-native FP32 GEMM: C <- alpha*A*op(B) + beta*C, row-major, op(B) in {B, B^T}.
+"""MI355X-native FP32 GEMM: C <- alpha*A*op(B) + beta*C, row-major, op(B) in {B, B^T},
+and the out-of-place FP32 matrix transpose dst <- src^T.
 
 The compute path is the HIP library ``libsgemm_f32.so`` (hand-written gfx950
 kernels behind a C ABI, declared in include/sgemm_f32.h); this package is its
@@ -6,5 +7,7 @@ binding (``sgemm``), its build script (``build``) and the seeded input
 generator (``inputs``).  Importing the package loads nothing; the first call
 into ``sgemm`` loads the library and raises if it is missing.
 """
-from .sgemm import (ALGO, EXPORTS, LIB_PATH, SgemmError, gemm, load, sgemm_f32,  # noqa: F401
-                    sgemm_f32_algo, sgemm_f32_plan, sgemm_f32_status_string, sgemm_f32_version)
+from .sgemm import (ALGO, EXPORTS, LIB_PATH, TRANSPOSE_ALGO, SgemmError, gemm, load,  # noqa: F401
+                    sgemm_f32, sgemm_f32_algo, sgemm_f32_plan, sgemm_f32_status_string,
+                    sgemm_f32_transpose, sgemm_f32_transpose_algo, sgemm_f32_transpose_plan,
+                    sgemm_f32_version, transpose)

@@ -3,6 +3,7 @@
 // check is reported identically with or without a GPU.
 #include "sgemm_f32.h"
 #include "sgemm_internal.h"
+#include "transpose_internal.h"
 
 #include <atomic>
 #include <cstdio>
@@ -12,7 +13,11 @@
 namespace sgemm {
 namespace {
 
-constexpr int64_t kMaxDim = std::numeric_limits<int32_t>::max();
+// Row and column indices are formed in int32 inside the kernels, a tile past
+// the last one included: dimensions stay 1024 below 2^31.
+constexpr int64_t kMaxDim = ((int64_t)1 << 31) - 1025;
+// A launch covers fewer than 2^32 work-items.
+constexpr int64_t kMaxWorkItems = ((int64_t)1 << 32) - 1;
 constexpr int kMaxDevices = 64;
 
 struct Plan {
@@ -57,6 +62,11 @@ int choose_mfma(int64_t M, int64_t N)
     return KID_MFMA_S;
 }
 
+int threads_per_block(int kid)
+{
+    return (kid == KID_MFMA_L || kid == KID_MFMA_M) ? 512 : 256;
+}
+
 Plan make_plan(int algo, int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
                const float *B, int64_t ldb, int transB, float beta, const float *C, int64_t ldc)
 {
@@ -92,6 +102,8 @@ Plan make_plan(int algo, int64_t M, int64_t N, int64_t K, float alpha, const flo
         p.kid = KID_SCALE;
         p.tiles_m = M;
         p.tiles_n = ceil_div(N, 256);
+        if (p.tiles_m * p.tiles_n * 256 > kMaxWorkItems)
+            return fail(SGEMM_ERR_INVALID_VALUE);
         return p;
     }
     if (A == nullptr || B == nullptr)
@@ -110,8 +122,65 @@ Plan make_plan(int algo, int64_t M, int64_t N, int64_t K, float alpha, const flo
     const TileShape t = tile_shape(p.kid);
     p.tiles_m = ceil_div(M, t.bm);
     p.tiles_n = ceil_div(N, t.bn);
-    if (p.tiles_m * p.tiles_n > (int64_t)std::numeric_limits<int32_t>::max())
+    if (p.tiles_m * p.tiles_n * threads_per_block(p.kid) > kMaxWorkItems)
         return fail(SGEMM_ERR_INVALID_VALUE);
+    return p;
+}
+
+// AUTO sends matrices with fewer source rows (columns) than this to the
+// element-per-work-item kernels.
+constexpr int64_t kTransposeNarrow = 32;
+
+struct TransposePlan {
+    int status = SGEMM_OK;
+    int kid = KID_NONE;
+    bool vec = false;
+    int64_t blocks = 0;
+    int64_t rows = 0, cols = 0;
+};
+
+TransposePlan make_transpose_plan(int algo, int64_t rows, int64_t cols, const float *src, int64_t ld_src,
+                                  const float *dst, int64_t ld_dst)
+{
+    TransposePlan p;
+    p.rows = rows;
+    p.cols = cols;
+    auto fail = [&](int s) {
+        p.status = s;
+        p.kid = KID_NONE;
+        p.blocks = 0;
+        return p;
+    };
+    if (algo < SGEMM_TRANSPOSE_AUTO || algo > SGEMM_TRANSPOSE_NARROW)
+        return fail(SGEMM_ERR_INVALID_VALUE);
+    if (rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim)
+        return fail(SGEMM_ERR_INVALID_VALUE);
+    if (ld_src < (cols > 1 ? cols : 1) || ld_dst < (rows > 1 ? rows : 1))
+        return fail(SGEMM_ERR_INVALID_VALUE);
+    const int64_t src_bytes = span_bytes(rows, cols, ld_src);
+    const int64_t dst_bytes = span_bytes(cols, rows, ld_dst);
+    if (src_bytes < 0 || dst_bytes < 0)
+        return fail(SGEMM_ERR_INVALID_VALUE);
+    if (rows == 0 || cols == 0)
+        return p;  // nothing to do
+    if (src == nullptr || dst == nullptr)
+        return fail(SGEMM_ERR_INVALID_VALUE);
+    if (overlaps(dst, dst_bytes, src, src_bytes))
+        return fail(SGEMM_ERR_ALIAS);
+    switch (algo) {
+    case SGEMM_TRANSPOSE_NAIVE: p.kid = KID_TRANSPOSE_NAIVE; break;
+    case SGEMM_TRANSPOSE_LDS: p.kid = KID_TRANSPOSE_LDS_PAD; break;
+    case SGEMM_TRANSPOSE_LDS_NOPAD: p.kid = KID_TRANSPOSE_LDS_NOPAD; break;
+    case SGEMM_TRANSPOSE_NARROW: p.kid = KID_TRANSPOSE_NARROW; break;
+    default:  // AUTO: tiles unless a 128-wide tile would run mostly empty
+        p.kid = rows < kTransposeNarrow ? KID_TRANSPOSE_NAIVE
+                : cols < kTransposeNarrow ? KID_TRANSPOSE_NARROW : KID_TRANSPOSE_LDS_PAD;
+        break;
+    }
+    p.vec = aligned16(src, ld_src);
+    if (transpose_tiles(p.kid, rows, cols) > (int64_t)UINT32_MAX)
+        return fail(SGEMM_ERR_INVALID_VALUE);
+    p.blocks = transpose_blocks(p.kid, rows, cols);
     return p;
 }
 
@@ -127,6 +196,10 @@ const char *kernel_label(int kid)
     case KID_MFMA_L: return "mfma_256x256x32_w4x2";
     case KID_MFMA_M: return "mfma_128x128x32_w2x2_ks2";
     case KID_MFMA_S: return "mfma_64x64x32_w2x2";
+    case KID_TRANSPOSE_NAIVE: return "transpose_naive_64x16";
+    case KID_TRANSPOSE_LDS_PAD: return "transpose_lds_128x128_pad1";
+    case KID_TRANSPOSE_LDS_NOPAD: return "transpose_lds_128x128_pad0";
+    case KID_TRANSPOSE_NARROW: return "transpose_narrow_64x16";
     default: return "unknown";
     }
 }
@@ -189,6 +262,27 @@ int run(int algo, int64_t M, int64_t N, int64_t K, float alpha, const float *A, 
     return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
 }
 
+int run_transpose(int algo, int64_t rows, int64_t cols, const float *src, int64_t ld_src, float *dst,
+                  int64_t ld_dst, void *stream)
+{
+    const TransposePlan p = make_transpose_plan(algo, rows, cols, src, ld_src, dst, ld_dst);
+    if (p.status != SGEMM_OK || p.kid == KID_NONE)
+        return p.status;
+    const int dev_status = check_device();
+    if (dev_status != SGEMM_OK)
+        return dev_status;
+    TransposeArgs a;
+    a.src = src;
+    a.dst = dst;
+    a.ld_src = ld_src;
+    a.ld_dst = ld_dst;
+    a.rows = (int)rows;
+    a.cols = (int)cols;
+    (void)hipGetLastError();
+    const hipError_t e = launch_transpose(a, p.kid, p.vec, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
+}
+
 }  // namespace
 }  // namespace sgemm
 
@@ -224,12 +318,50 @@ int sgemm_f32_plan(int algo, int64_t M, int64_t N, int64_t K, float alpha, const
     return p.status;
 }
 
+int sgemm_f32_transpose(int64_t rows, int64_t cols, const float *src, int64_t ld_src, float *dst, int64_t ld_dst,
+                        void *stream)
+{
+    return sgemm::run_transpose(SGEMM_TRANSPOSE_AUTO, rows, cols, src, ld_src, dst, ld_dst, stream);
+}
+
+int sgemm_f32_transpose_algo(int algo, int64_t rows, int64_t cols, const float *src, int64_t ld_src, float *dst,
+                             int64_t ld_dst, void *stream)
+{
+    return sgemm::run_transpose(algo, rows, cols, src, ld_src, dst, ld_dst, stream);
+}
+
+int sgemm_f32_transpose_plan(int algo, int64_t rows, int64_t cols, const float *src, int64_t ld_src,
+                             const float *dst, int64_t ld_dst, int *kernel_id, int64_t *blocks, char *name,
+                             int name_len)
+{
+    const sgemm::TransposePlan p = sgemm::make_transpose_plan(algo, rows, cols, src, ld_src, dst, ld_dst);
+    if (kernel_id)
+        *kernel_id = p.kid;
+    if (blocks)
+        *blocks = p.blocks;
+    if (name && name_len > 0) {
+        const bool tiles = p.kid == sgemm::KID_TRANSPOSE_LDS_PAD || p.kid == sgemm::KID_TRANSPOSE_LDS_NOPAD;
+        const int shape = tiles ? sgemm::transpose_shape(p.rows, p.cols) : -1;
+        const char *label = !tiles ? sgemm::kernel_label(p.kid)
+                            : shape == sgemm::TSHAPE_SMALL
+                                ? (p.kid == sgemm::KID_TRANSPOSE_LDS_PAD ? "transpose_lds_64x64_pad1"
+                                                                          : "transpose_lds_64x64_pad0")
+                                : sgemm::kernel_label(p.kid);
+        const char *suffix = !tiles ? ""
+                             : shape == sgemm::TSHAPE_SMALL ? ""
+                             : shape == sgemm::TSHAPE_PIPE ? "_pipe"
+                             : (p.vec && p.kid == sgemm::KID_TRANSPOSE_LDS_PAD) ? "_stream_v4" : "_stream";
+        std::snprintf(name, (size_t)name_len, "%s%s", label, suffix);
+    }
+    return p.status;
+}
+
 const char *sgemm_f32_status_string(int status)
 {
     switch (status) {
     case SGEMM_OK: return "SGEMM_OK";
     case SGEMM_ERR_INVALID_VALUE: return "SGEMM_ERR_INVALID_VALUE: invalid argument";
-    case SGEMM_ERR_ALIAS: return "SGEMM_ERR_ALIAS: C overlaps A or B";
+    case SGEMM_ERR_ALIAS: return "SGEMM_ERR_ALIAS: output overlaps an input";
     case SGEMM_ERR_NO_DEVICE: return "SGEMM_ERR_NO_DEVICE: no HIP device is current";
     case SGEMM_ERR_UNSUPPORTED_ARCH: return "SGEMM_ERR_UNSUPPORTED_ARCH: device is not gfx950";
     case SGEMM_ERR_LAUNCH: return "SGEMM_ERR_LAUNCH: kernel launch failed";

@@ -114,3 +114,47 @@ def make_config(name: str, **overrides) -> Case:
 def flops(M, N, K) -> float:
     """2*M*N*K, the FLOP convention every throughput figure uses."""
     return 2.0 * M * N * K
+
+
+# Transpose workloads.  "现代 CUDA 工具箱实战" measures a 4096 x 4096 float32
+# transpose (section 性能实测); the other shapes exercise ragged edges and
+# strided storage.
+TRANSPOSE_CONFIGS = {
+    "t_4096": dict(rows=4096, cols=4096, seed=5),
+    "t_8192": dict(rows=8192, cols=8192, seed=9),
+    "t_ragged": dict(rows=1000, cols=1017, seed=6),
+    "t_wide": dict(rows=3, cols=262147, seed=7),
+    "t_tall": dict(rows=262147, cols=3, seed=8),
+}
+
+# Bit patterns that a transpose must carry through unchanged: quiet and
+# signalling NaNs with payloads, both infinities, both zeros, subnormals and the
+# largest finite values.
+SPECIAL_BITS = np.array([0x7FC00001, 0xFFC12345, 0x7F800001, 0x7FA00000, 0x7F800000, 0xFF800000,
+                         0x00000000, 0x80000000, 0x00000001, 0x807FFFFF, 0x7F7FFFFF, 0xFF7FFFFF],
+                        dtype=np.uint32)
+
+
+def make_transpose_input(rows, cols, seed=0, ld_src=None, dist="uniform", specials=False,
+                         pad_value=np.nan) -> np.ndarray:
+    """Source storage (rows x ld_src float32) for a transpose.
+
+    Draws the rows x cols matrix from ``dist``; with ``specials`` about one
+    element in 64 is then overwritten with a pattern from SPECIAL_BITS (chosen
+    by the same generator).  Padding columns hold ``pad_value``.
+    """
+    rng = np.random.default_rng(seed)
+    ld_src = max(1, cols) if ld_src is None else ld_src
+    x = _draw(rng, dist, (rows, cols))
+    if specials and x.size:
+        mask = rng.random(size=x.shape) < 1.0 / 64
+        pick = rng.integers(0, SPECIAL_BITS.size, size=x.shape)
+        xb = x.view(np.uint32)
+        xb[mask] = SPECIAL_BITS[pick[mask]]
+    return _store(x, ld_src, pad_value)
+
+
+def make_transpose_config(name: str, **overrides) -> np.ndarray:
+    p = dict(TRANSPOSE_CONFIGS[name])
+    p.update(overrides)
+    return make_transpose_input(**p)

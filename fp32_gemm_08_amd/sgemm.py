@@ -24,9 +24,11 @@ SGEMM_ERR_UNSUPPORTED_ARCH = 4
 SGEMM_ERR_LAUNCH = 5
 
 ALGO = {"auto": 0, "naive": 1, "lds_tiled": 2, "regblock": 3, "mfma": 4, "lds_tiled_nopad": 5}
+TRANSPOSE_ALGO = {"auto": 0, "naive": 1, "lds": 2, "lds_nopad": 3, "narrow": 4}
 
 # Symbols declared in include/sgemm_f32.h.
 EXPORTS = ("sgemm_f32", "sgemm_f32_algo", "sgemm_f32_plan", "sgemm_f32_status_string",
+           "sgemm_f32_transpose", "sgemm_f32_transpose_algo", "sgemm_f32_transpose_plan",
            "sgemm_f32_version")
 
 _lock = threading.Lock()
@@ -59,6 +61,14 @@ def load():
         lib.sgemm_f32_plan.argtypes = [ci, i64, i64, i64, f32, vp, i64, vp, i64, ci, f32, vp, i64,
                                        ctypes.POINTER(ci), ctypes.POINTER(i64), ctypes.POINTER(i64),
                                        ctypes.c_char_p, ci]
+        tr_args = [i64, i64, vp, i64, vp, i64, vp]
+        lib.sgemm_f32_transpose.restype = ci
+        lib.sgemm_f32_transpose.argtypes = tr_args
+        lib.sgemm_f32_transpose_algo.restype = ci
+        lib.sgemm_f32_transpose_algo.argtypes = [ci] + tr_args
+        lib.sgemm_f32_transpose_plan.restype = ci
+        lib.sgemm_f32_transpose_plan.argtypes = [ci, i64, i64, vp, i64, vp, i64, ctypes.POINTER(ci),
+                                                 ctypes.POINTER(i64), ctypes.c_char_p, ci]
         lib.sgemm_f32_status_string.restype = ctypes.c_char_p
         lib.sgemm_f32_status_string.argtypes = [ci]
         lib.sgemm_f32_version.restype = ctypes.c_char_p
@@ -88,6 +98,26 @@ def sgemm_f32_plan(algo, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc):
     return st, kid.value, tm.value, tn.value, buf.value.decode()
 
 
+def sgemm_f32_transpose(rows, cols, src, ld_src, dst, ld_dst, stream=0) -> int:
+    """dst <- src^T (AUTO algorithm).  Returns the status code."""
+    return load().sgemm_f32_transpose(rows, cols, src, ld_src, dst, ld_dst, stream)
+
+
+def sgemm_f32_transpose_algo(algo, rows, cols, src, ld_src, dst, ld_dst, stream=0) -> int:
+    """dst <- src^T with an explicit algorithm id.  Returns the status code."""
+    return load().sgemm_f32_transpose_algo(algo, rows, cols, src, ld_src, dst, ld_dst, stream)
+
+
+def sgemm_f32_transpose_plan(algo, rows, cols, src, ld_src, dst, ld_dst):
+    """Host-only planning query: (status, kernel_id, blocks, name)."""
+    kid = ctypes.c_int(0)
+    blocks = ctypes.c_int64(0)
+    buf = ctypes.create_string_buffer(128)
+    st = load().sgemm_f32_transpose_plan(algo, rows, cols, src, ld_src, dst, ld_dst, ctypes.byref(kid),
+                                         ctypes.byref(blocks), buf, 128)
+    return st, kid.value, blocks.value, buf.value.decode()
+
+
 def sgemm_f32_status_string(status: int) -> str:
     return load().sgemm_f32_status_string(status).decode()
 
@@ -101,10 +131,25 @@ def _check(status):
         raise SgemmError(status, sgemm_f32_status_string(status))
 
 
-def _algo_id(algo):
+def _algo_id(algo, table=ALGO):
     if isinstance(algo, str):
-        return ALGO[algo]
+        return table[algo]
     return int(algo)
+
+
+def _check_matrix(name, t):
+    import torch
+
+    if t.dtype != torch.float32 or not t.is_cuda or t.dim() != 2:
+        raise TypeError(f"{name} must be a 2-D float32 device tensor")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit stride along its last dimension")
+    if t.shape[0] > 1 and t.stride(0) < t.shape[1]:
+        raise ValueError(f"{name} rows overlap (row stride below the row length)")
+
+
+def _ld(t):
+    return max(t.stride(0) if t.shape[0] > 1 else t.shape[1], t.shape[1], 1)
 
 
 def gemm(A, B, C, alpha=1.0, beta=0.0, trans_b=False, algo="auto", stream=None):
@@ -117,23 +162,37 @@ def gemm(A, B, C, alpha=1.0, beta=0.0, trans_b=False, algo="auto", stream=None):
     import torch  # plumbing only: device memory and streams
 
     for name, t in (("A", A), ("B", B), ("C", C)):
-        if t.dtype != torch.float32 or not t.is_cuda or t.dim() != 2:
-            raise TypeError(f"{name} must be a 2-D float32 device tensor")
-        if t.shape[1] > 1 and t.stride(1) != 1:
-            raise ValueError(f"{name} must have unit stride along its last dimension")
-        if t.shape[0] > 1 and t.stride(0) < t.shape[1]:
-            raise ValueError(f"{name} rows overlap (row stride below the row length)")
+        _check_matrix(name, t)
     M, K = A.shape
     N = B.shape[0] if trans_b else B.shape[1]
     if (B.shape[1] if trans_b else B.shape[0]) != K or tuple(C.shape) != (M, N):
         raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)} "
                          f"(trans_b={trans_b}), C {tuple(C.shape)}")
-    def ld(t):
-        return max(t.stride(0) if t.shape[0] > 1 else t.shape[1], t.shape[1], 1)
-
+    ld = _ld
     s = (stream if stream is not None else torch.cuda.current_stream(C.device)).cuda_stream
     with torch.cuda.device(C.device):
         st = sgemm_f32_algo(_algo_id(algo), M, N, K, float(alpha), A.data_ptr(), ld(A), B.data_ptr(), ld(B),
                             int(bool(trans_b)), float(beta), C.data_ptr(), ld(C), s)
     _check(st)
     return C
+
+
+def transpose(src, dst, algo="auto", stream=None):
+    """dst <- src^T on torch float32 CUDA tensors; returns dst.
+
+    src is (rows, cols) and dst is (cols, rows); either may be a row-strided view
+    (last-dimension stride 1) whose row stride is its leading dimension.
+    """
+    import torch  # plumbing only: device memory and streams
+
+    _check_matrix("src", src)
+    _check_matrix("dst", dst)
+    rows, cols = src.shape
+    if tuple(dst.shape) != (cols, rows):
+        raise ValueError(f"shape mismatch: src {tuple(src.shape)}, dst {tuple(dst.shape)}")
+    s = (stream if stream is not None else torch.cuda.current_stream(dst.device)).cuda_stream
+    with torch.cuda.device(dst.device):
+        st = sgemm_f32_transpose_algo(_algo_id(algo, TRANSPOSE_ALGO), rows, cols, src.data_ptr(), _ld(src),
+                                      dst.data_ptr(), _ld(dst), s)
+    _check(st)
+    return dst

@@ -38,10 +38,11 @@
  *
  * Errors are returned before any HIP call where possible, so they are testable
  * without a GPU:
- *   SGEMM_ERR_INVALID_VALUE   negative or too large (> 2^31-1) dimension, a leading
- *                             dimension below its minimum, transB not 0/1, a NULL
- *                             pointer for an operand that would be read or written,
- *                             or an unknown algorithm id;
+ *   SGEMM_ERR_INVALID_VALUE   negative or too large (> 2^31 - 1025) dimension, a
+ *                             leading dimension below its minimum, transB not 0/1, a
+ *                             NULL pointer for an operand that would be read or
+ *                             written, an unknown algorithm id, or a launch that
+ *                             would need 2^32 or more work-items;
  *   SGEMM_ERR_ALIAS           C's byte range overlaps A's or B's (the kernels rely on
  *                             the no-alias premise of __restrict__, section 5.3 of the
  *                             first page); A and B may overlap each other;
@@ -127,6 +128,83 @@ int sgemm_f32_plan(int algo, int64_t M, int64_t N, int64_t K, float alpha,
                    float beta, const float *C, int64_t ldc,
                    int *kernel_id, int64_t *tiles_m, int64_t *tiles_n,
                    char *name, int name_len);
+
+/*
+ * Out-of-place FP32 matrix transpose (a second, memory-bound operation of the
+ * library):
+ *
+ *     dst(j, i) = src(i, j)        0 <= i < rows, 0 <= j < cols
+ *
+ * The operation, its naive baseline and its shared-memory version with one
+ * padding column per tile row are those of "现代 CUDA 工具箱实战：从朴素代码到硬件
+ * 极限的优化之路", section 代码实现 (square N x N there; any rows x cols here).
+ *
+ * Layout (row-major, leading dimensions in elements):
+ *   src    rows x cols,  element (i,j) at src[i*ld_src + j],  ld_src >= max(1, cols)
+ *   dst    cols x rows,  element (j,i) at dst[j*ld_dst + i],  ld_dst >= max(1, rows)
+ * Elements are moved bit for bit (NaN payloads, signed zeros and subnormals
+ * included); dst elements outside the cols x rows window (row padding) are not
+ * written.
+ *
+ * Ownership and asynchrony as for sgemm_f32: device pointers owned by the caller,
+ * no allocation, no workspace, no synchronisation; the call enqueues one kernel
+ * on `stream` and returns.
+ *
+ * Quick return: rows == 0 or cols == 0 touches nothing and returns SGEMM_OK.
+ * Errors:
+ *   SGEMM_ERR_INVALID_VALUE   negative or too large (> 2^31 - 1025) dimension, a
+ *                             leading dimension below its minimum, a NULL pointer
+ *                             with a non-zero extent, an unknown algorithm id, or
+ *                             2^32 or more work units of the chosen kernel (never
+ *                             reached within device memory);
+ *   SGEMM_ERR_ALIAS           dst's byte range overlaps src's (the transpose is out
+ *                             of place only);
+ *   SGEMM_ERR_NO_DEVICE, SGEMM_ERR_UNSUPPORTED_ARCH, SGEMM_ERR_LAUNCH as above.
+ *
+ * Algorithms:
+ *   NAIVE      one work-item per element: source rows read contiguously,
+ *              destination written with a stride of ld_dst between lanes (the
+ *              page's baseline);
+ *   LDS        128 x 128 tiles staged through LDS with a row pitch of 129
+ *              floats: contiguous reads and writes, conflict-free LDS access (the
+ *              page's shared-memory + padding version); up to 2048 tiles a
+ *              persistent grid overlaps each workgroup's next loads with its
+ *              current stores, above that one tile per workgroup with
+ *              non-temporal loads and stores; with fewer tiles than CUs, 64 x 64
+ *              tiles (pitch 65) instead;
+ *   LDS_NOPAD  the same kernels without the padding column (the page's "forgot
+ *              the padding" case); kept to measure the bank conflicts;
+ *   NARROW     one work-item per destination element: destination rows written
+ *              contiguously, source read with a stride of ld_src;
+ *   AUTO       NAIVE for fewer than 32 source rows, NARROW for fewer than 32
+ *              source columns, LDS otherwise.
+ */
+typedef enum {
+    SGEMM_TRANSPOSE_AUTO = 0,
+    SGEMM_TRANSPOSE_NAIVE = 1,
+    SGEMM_TRANSPOSE_LDS = 2,
+    SGEMM_TRANSPOSE_LDS_NOPAD = 3,
+    SGEMM_TRANSPOSE_NARROW = 4
+} sgemm_transpose_algo;
+
+/* dst <- src^T with the AUTO algorithm.  Returns an sgemm_status. */
+int sgemm_f32_transpose(int64_t rows, int64_t cols, const float *src, int64_t ld_src,
+                        float *dst, int64_t ld_dst, void *stream);
+
+/* The same operation with an explicit algorithm (an sgemm_transpose_algo value). */
+int sgemm_f32_transpose_algo(int algo, int64_t rows, int64_t cols, const float *src,
+                             int64_t ld_src, float *dst, int64_t ld_dst, void *stream);
+
+/*
+ * Host-only planning query for the transpose, no HIP call: validates exactly as
+ * sgemm_f32_transpose_algo would and reports the kernel id (0 when nothing
+ * would launch), the number of workgroups launched (each loops over tiles; at
+ * most 2^20) and a NUL-terminated kernel name (name may be NULL/0).  Returns the status the call would return before
+ * touching the device.
+ */
+int sgemm_f32_transpose_plan(int algo, int64_t rows, int64_t cols, const float *src,
+                             int64_t ld_src, const float *dst, int64_t ld_dst,
+                             int *kernel_id, int64_t *blocks, char *name, int name_len);
 
 /* Static, NUL-terminated text for a status code (unknown codes included). */
 const char *sgemm_f32_status_string(int status);

@@ -72,6 +72,7 @@ def call(algo=0, M=64, N=64, K=64, alpha=1.0, A=PA, lda=None, B=PB, ldb=None, tr
     dict(transB=2), dict(transB=-1),
     dict(lda=63), dict(ldb=63), dict(ldc=63), dict(transB=1, ldb=63),
     dict(A=0), dict(B=0), dict(C=0), dict(algo=6), dict(algo=-1),
+    dict(M=(1 << 31) - 1024), dict(N=(1 << 31) - 1024), dict(K=(1 << 31) - 1024),
     dict(M=2, K=2, lda=1 << 61),
 ])
 def test_invalid_arguments(kw):
@@ -175,3 +176,14 @@ def test_gemm_wrapper_rejects_host_tensors():
     a = torch.zeros(4, 4)
     with pytest.raises(TypeError):
         lib.gemm(a, a, a.clone())
+
+
+def test_launch_work_item_limit():
+    # The naive kernel's 4 x 64 tiles at 2^17 x 2^17 would need 2^34 work-items;
+    # the MFMA tiles of the same shape stay far below 2^32.
+    n = 1 << 17
+    assert plan(algo=1, M=n, N=n, K=1, lda=1, ldb=n, ldc=n, C=1 << 50)[0] == INVALID
+    st, kid, tm, tn, _ = plan(algo=0, M=n, N=n, K=1, lda=1, ldb=n, ldc=n, C=1 << 50)
+    assert (st, kid, tm, tn) == (OK, KID_L, n // 256, n // 256)
+    # largest accepted dimension
+    assert plan(M=(1 << 31) - 1025, N=1, K=1, lda=1, ldb=1, ldc=1, C=1 << 50)[0] == OK
