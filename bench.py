@@ -368,16 +368,82 @@ def sweep_transpose():
         torch.cuda.empty_cache()
 
 
+SPLITK_SHAPES = [("c1_128", None), ("c5_512", None), ("c2_1024", None), ("c3_ragged_bt", None),
+                 ("768^3", (768, 768, 768)), ("1024x1024x4096", (1024, 1024, 4096)),
+                 ("512x512x8192", (512, 512, 8192)), ("256x256x8192", (256, 256, 8192)),
+                 ("64x64x65536", (64, 64, 65536)), ("c5_2048", None)]
+
+
+def sweep_splitk(splits_list=(1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 0)):
+    """Time the k-split path for several split counts on the small and long-k
+    workloads (both kernels, average over back-to-back calls)."""
+    import torch
+
+    import fp32_gemm_08_amd as lib
+    from fp32_gemm_08_amd.inputs import make_case, make_config
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream(dev)
+    w = torch.rand(4096, 4096, device=dev)
+    wc = torch.empty_like(w)
+    for _ in range(300):
+        lib.gemm(w, w, wc, algo="mfma")
+    torch.cuda.synchronize()
+    del w, wc
+    print("| workload | splits asked | splits used | partial-pass kernel | workspace MiB | avg us | TFLOP/s |")
+    print("|---|---|---|---|---|---|---|")
+    for name, shape in SPLITK_SHAPES:
+        case = make_config(name) if shape is None else make_case(*shape, seed=31)
+        M, N, K = case.M, case.N, case.K
+        dA = torch.from_numpy(case.A).to(dev)
+        dB = torch.from_numpy(case.B).to(dev)
+        dC = torch.zeros((M, case.ldc), dtype=torch.float32, device=dev)
+        if case.C is not None:
+            dC.copy_(torch.from_numpy(case.C))
+        need = max(lib.sgemm_f32_splitk_plan(sp, M, N, K, int(case.trans_b))[3] for sp in splits_list)
+        ws = torch.empty(max(need, 4) // 4, dtype=torch.float32, device=dev)
+        flop = 2.0 * M * N * K
+        for sp in splits_list:
+            _, used, kid, nb = lib.sgemm_f32_splitk_plan(sp, M, N, K, int(case.trans_b))
+            args = (M, N, K, case.alpha, dA.data_ptr(), case.lda, dB.data_ptr(), case.ldb, int(case.trans_b),
+                    case.beta, dC.data_ptr(), case.ldc, ws.data_ptr(), need, stream.cuda_stream)
+
+            def call():
+                st = lib.sgemm_f32_splitk(sp, *args) if sp else lib.sgemm_f32_ws(*args)
+                if st != 0:
+                    raise RuntimeError(lib.sgemm_f32_status_string(st))
+
+            reps = int(max(10, min(300, 0.1 / max(flop / 60e12, 2e-6))))
+            for _ in range(max(5, reps // 4)):
+                call()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3 / reps
+            kname = {40: "mfma 256x256", 41: "mfma 128x128 ks2", 42: "mfma 64x64"}.get(kid, str(kid))
+            print(f"| {name} {M}x{N}x{K} | {sp if sp else 'auto'} | {used} | {kname} | {nb / 2**20:.1f} | "
+                  f"{t * 1e6:.2f} | {flop / t / 1e12:.2f} |", flush=True)
+        del dA, dB, dC, ws
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=200,
                     help="untimed calls first; the clock needs ~0.1 s of load to reach its steady state")
-    ap.add_argument("--op", choices=("gemm", "transpose"), default="gemm")
+    ap.add_argument("--op", choices=("gemm", "transpose", "splitk"), default="gemm",
+                    help="splitk: table of the k-split path over split counts (no JSON line)")
     ap.add_argument("--config", default="c4_4096",
                     help="workload name (GEMM: c1_128 ... c5_tall; transpose: t_4096 ...)")
     ap.add_argument("--algo", default="auto")
+    ap.add_argument("--workspace", action="store_true",
+                    help="GEMM: call sgemm_f32_ws with the workspace its plan asks for (k-split when the "
+                         "output tiles are too few; a step is then the partial pass plus the reduction)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -397,6 +463,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.op == "splitk":
+        sweep_splitk()
         return
     if args.op == "transpose":
         if args.sweep:
@@ -431,10 +500,22 @@ def main():
                                                 int(case.trans_b), case.beta, pc, case.ldc)
     if st != 0:
         raise SystemExit(f"plan failed: {lib.sgemm_f32_status_string(st)}")
+    splits, ws, ws_bytes = 1, None, 0
+    if args.workspace:
+        _, splits, skid, ws_bytes = lib.sgemm_f32_splitk_plan(0, M, N, K, int(case.trans_b))
+        if splits > 1:
+            ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device=dev)
+            kid = skid
+            kname = f"k-split x{splits}: mfma_64x64x32_w2x2 partial pass + splitk_reduce"
+            tm, tn = -(-M // 64) * splits, -(-N // 64)
 
     def step():
-        s = lib.sgemm_f32_algo(algo, M, N, K, case.alpha, pa, case.lda, pb, case.ldb, int(case.trans_b),
-                               case.beta, pc, case.ldc, sp)
+        if ws is not None:
+            s = lib.sgemm_f32_ws(M, N, K, case.alpha, pa, case.lda, pb, case.ldb, int(case.trans_b), case.beta,
+                                 pc, case.ldc, ws.data_ptr(), ws_bytes, sp)
+        else:
+            s = lib.sgemm_f32_algo(algo, M, N, K, case.alpha, pa, case.lda, pb, case.ldb, int(case.trans_b),
+                                   case.beta, pc, case.ldc, sp)
         if s != 0:
             raise RuntimeError(lib.sgemm_f32_status_string(s))
 
@@ -464,7 +545,8 @@ def main():
     achieved = flop / kern_avg / 1e12
     mfma = kid in (40, 41, 42)
     peak = FP32_MFMA_PEAK_TFLOPS if mfma else FP32_VALU_PEAK_TFLOPS
-    log(f"kernel {kname}: avg {kern_avg * 1e3:.4f} ms over {K_steps} calls "
+    log(f"{'step (both kernels)' if ws is not None else 'kernel'} {kname}: avg {kern_avg * 1e3:.4f} ms "
+        f"over {K_steps} calls "
         f"(event span {span * 1e3:.3f} ms, wall {wall * 1e3:.3f} ms)")
 
     # output for the sample check (beta != 0 workloads accumulate across steps:
@@ -476,7 +558,7 @@ def main():
     D_host = dC.cpu().numpy()
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if args.config == "c4_4096" else f"FP32 GEMM TFLOP/s ({args.config}), 1 GPU",
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -496,6 +578,7 @@ def main():
             "name": args.config, "M": M, "N": N, "K": K, "trans_b": case.trans_b,
             "lda": case.lda, "ldb": case.ldb, "ldc": case.ldc,
             "algo": args.algo, "kernel": kname, "workgroups": tm * tn,
+            "k_splits": splits, "workspace_bytes": ws_bytes,
         },
         "roofline": {
             "bound": "mfma" if mfma else "alu",

@@ -649,6 +649,14 @@ void sgemm_mfma_kernel(GemmArgs a)
                   "both paths share the workgroup tile");
     constexpr int SMEM = GD::SMEM > GR::SMEM ? GD::SMEM : GR::SMEM;
     __shared__ __attribute__((aligned(1024))) float smem[SMEM];
+    if (gridDim.y > 1) {
+        // k-split partial pass: this split's k-range and partial-product slice.
+        const int s = blockIdx.y, k0 = s * a.k_split;
+        a.A += k0;
+        a.B += TRANS_B ? (int64_t)k0 : (int64_t)k0 * a.ldb;
+        a.K = min(a.k_split, a.K - k0);
+        a.C += (int64_t)s * a.c_split_stride;
+    }
     const int nbm = (a.M + GD::BM - 1) / GD::BM, nbn = (a.N + GD::BN - 1) / GD::BN;
     int tile_m, tile_n;
     map_tile(blockIdx.x, nbm, nbn, tile_m, tile_n);
@@ -681,10 +689,10 @@ TileShape tile_shape(int kid)
 }
 
 template <int BM, int BN, int BKD, int BKR, int WGM, int WGN, int OCC, int KS>
-static void launch_cfg(const GemmArgs &a, bool transB, bool vec, hipStream_t stream)
+static void launch_cfg(const GemmArgs &a, bool transB, bool vec, hipStream_t stream, int splits)
 {
     const int64_t blocks = ceil_div(a.M, BM) * ceil_div(a.N, BN);
-    const dim3 grid((unsigned)blocks), block(64 * WGM * WGN * KS);
+    const dim3 grid((unsigned)blocks, (unsigned)splits), block(64 * WGM * WGN * KS);
     typedef Geo<BM, BN, BKD, WGM, WGN, OCC, true, KS> GDT;
     typedef Geo<BM, BN, BKR, WGM, WGN, OCC, true, KS> GRT;
     typedef Geo<BM, BN, BKD, WGM, WGN, OCC, false, KS> GDN;
@@ -702,13 +710,13 @@ static void launch_cfg(const GemmArgs &a, bool transB, bool vec, hipStream_t str
     }
 }
 
-hipError_t launch_mfma(const GemmArgs &a, int kid, bool transB, bool vec, hipStream_t stream)
+hipError_t launch_mfma(const GemmArgs &a, int kid, bool transB, bool vec, hipStream_t stream, int splits)
 {
     switch (kid) {
 #ifndef SGEMM_MFMA_EXPERIMENT
-    case KID_MFMA_L: launch_cfg<256, 256, 32, 16, 4, 2, 2, 1>(a, transB, vec, stream); break;
-    case KID_MFMA_M: launch_cfg<128, 128, 32, 32, 2, 2, 2, 2>(a, transB, vec, stream); break;
-    case KID_MFMA_S: launch_cfg<64, 64, 32, 32, 2, 2, 4, 1>(a, transB, vec, stream); break;
+    case KID_MFMA_L: launch_cfg<256, 256, 32, 16, 4, 2, 2, 1>(a, transB, vec, stream, splits); break;
+    case KID_MFMA_M: launch_cfg<128, 128, 32, 32, 2, 2, 2, 2>(a, transB, vec, stream, splits); break;
+    case KID_MFMA_S: launch_cfg<64, 64, 32, 32, 2, 2, 4, 1>(a, transB, vec, stream, splits); break;
 #else
     SGEMM_MFMA_EXPERIMENT
 #endif

@@ -62,6 +62,35 @@ int choose_mfma(int64_t M, int64_t N)
     return KID_MFMA_S;
 }
 
+// k-split geometry: k per split, a whole number of 32-wide k-tiles, and the
+// number of non-empty splits that gives.
+constexpr int64_t kSplitKTile = 32;
+constexpr int64_t kMaxSplits = 64;
+void split_geometry(int64_t K, int64_t splits, int64_t &kc, int64_t &used)
+{
+    kc = ceil_div(ceil_div(K, splits), kSplitKTile) * kSplitKTile;
+    used = ceil_div(K, kc);
+}
+
+// Splits AUTO uses with a workspace (measured on MI355X): none while the
+// 64 x 64 tile grid keeps at least half of the 256 CUs busy (splitting such
+// grids unbalances them more than it gains); otherwise the most splits that
+// still give one workgroup per CU and at least kSplitMinK of k each.  The
+// partial pass always runs the 64 x 64 tile, the fastest per split measured.
+constexpr int64_t kSplitMinK = 128;
+constexpr int64_t kSplitMinTiles = 128;
+int64_t auto_splits(int64_t M, int64_t N, int64_t K)
+{
+    const TileShape t = tile_shape(KID_MFMA_S);
+    const int64_t tiles = ceil_div(M, t.bm) * ceil_div(N, t.bn);
+    if (tiles >= kSplitMinTiles)
+        return 1;
+    int64_t s = 256 / tiles;
+    s = s < K / kSplitMinK ? s : K / kSplitMinK;
+    s = s < kMaxSplits ? s : kMaxSplits;
+    return s > 1 ? s : 1;
+}
+
 int threads_per_block(int kid)
 {
     return (kid == KID_MFMA_L || kid == KID_MFMA_M) ? 512 : 256;
@@ -248,6 +277,8 @@ int run(int algo, int64_t M, int64_t N, int64_t K, float alpha, const float *A, 
     a.beta = beta;
     const int64_t off_limit = ((int64_t)1 << 31) / 256;
     a.flags = (lda < off_limit && ldb < off_limit) ? GEMM_FLAG_DIRECT : 0;
+    a.k_split = 0;
+    a.c_split_stride = 0;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     (void)hipGetLastError();  // report this launch's status, not an older one
     hipError_t e;
@@ -259,6 +290,110 @@ int run(int algo, int64_t M, int64_t N, int64_t K, float alpha, const float *A, 
     case KID_REGBLOCK: e = launch_regblock(a, p.transB, p.vec, s); break;
     default: e = launch_mfma(a, p.kid, p.transB, p.vec, s); break;
     }
+    return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
+}
+
+struct SplitPlan {
+    Plan base;            // the plain call's validation and plan
+    int64_t splits = 1;   // splits that will run (1: the plain path)
+    int64_t kc = 0;       // k per split
+    int kid = KID_NONE;   // MFMA tile of the partial pass
+    int64_t bytes = 0;    // workspace bytes the partial pass needs
+};
+
+// splits_req: 0 = AUTO, otherwise the requested count (clipped to non-empty
+// splits).  With too small a workspace AUTO runs the plain path and an
+// explicit request fails.
+SplitPlan make_split_plan(int64_t splits_req, int64_t M, int64_t N, int64_t K, float alpha, const float *A,
+                          int64_t lda, const float *B, int64_t ldb, int transB, float beta, const float *C,
+                          int64_t ldc, const void *ws, int64_t ws_bytes, bool check_ws)
+{
+    SplitPlan sp;
+    sp.base = make_plan(SGEMM_ALGO_AUTO, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc);
+    auto fail = [&](int s) {
+        sp.base.status = s;
+        sp.base.kid = KID_NONE;
+        sp.splits = 1;
+        sp.kid = KID_NONE;
+        sp.bytes = 0;
+        return sp;
+    };
+    if (splits_req < 0 || splits_req > kMaxSplits || ws_bytes < 0)
+        return fail(SGEMM_ERR_INVALID_VALUE);
+    sp.kid = sp.base.kid;
+    const bool mfma = sp.base.kid == KID_MFMA_L || sp.base.kid == KID_MFMA_M || sp.base.kid == KID_MFMA_S;
+    if (sp.base.status != SGEMM_OK || !mfma)
+        return sp;  // errors, quick returns and the product-free cases are the plain call's
+    const int64_t want = splits_req == 0 ? auto_splits(M, N, K) : splits_req;
+    int64_t kc, used;
+    split_geometry(K, want, kc, used);
+    if (used <= 1)
+        return sp;
+    const int64_t bytes = used * M * N * (int64_t)sizeof(float);
+    if (!check_ws) {  // query: report what a large enough workspace would get
+        sp.splits = used;
+        sp.kc = kc;
+        sp.kid = KID_MFMA_S;
+        sp.bytes = bytes;
+        return sp;
+    }
+    if (ws == nullptr || ws_bytes < bytes) {
+        if (splits_req == 0)
+            return sp;  // AUTO without room for the partials: the plain path
+        return fail(SGEMM_ERR_INVALID_VALUE);
+    }
+    const int64_t a_bytes = span_bytes(M, K, lda);
+    const int64_t b_bytes = span_bytes(sp.base.transB ? N : K, sp.base.transB ? K : N, ldb);
+    const int64_t c_bytes = span_bytes(M, N, ldc);
+    if (overlaps(ws, bytes, A, a_bytes) || overlaps(ws, bytes, B, b_bytes) || overlaps(ws, bytes, C, c_bytes))
+        return fail(SGEMM_ERR_ALIAS);
+    sp.splits = used;
+    sp.kc = kc;
+    sp.kid = KID_MFMA_S;
+    sp.bytes = bytes;
+    const TileShape t = tile_shape(sp.kid);
+    if (ceil_div(M, t.bm) * ceil_div(N, t.bn) * used * threads_per_block(sp.kid) > kMaxWorkItems)
+        return fail(SGEMM_ERR_INVALID_VALUE);
+    return sp;
+}
+
+int run_split(int64_t splits_req, int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
+              const float *B, int64_t ldb, int transB, float beta, float *C, int64_t ldc, void *ws,
+              int64_t ws_bytes, void *stream)
+{
+    const SplitPlan sp = make_split_plan(splits_req, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, ws,
+                                         ws_bytes, true);
+    if (sp.base.status != SGEMM_OK)
+        return sp.base.status;
+    if (sp.splits <= 1)
+        return run(SGEMM_ALGO_AUTO, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, stream);
+    const int dev_status = check_device();
+    if (dev_status != SGEMM_OK)
+        return dev_status;
+    float *W = static_cast<float *>(ws);
+    GemmArgs a;
+    a.A = A;
+    a.B = B;
+    a.C = W;
+    a.lda = lda;
+    a.ldb = ldb;
+    a.ldc = N;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.alpha = 1.0f;
+    a.beta = 0.0f;
+    const int64_t off_limit = ((int64_t)1 << 31) / 256;
+    a.flags = (lda < off_limit && ldb < off_limit) ? GEMM_FLAG_DIRECT : 0;
+    a.k_split = (int)sp.kc;
+    a.c_split_stride = M * N;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    hipError_t e = launch_mfma(a, sp.kid, sp.base.transB, sp.base.vec, s, (int)sp.splits);
+    if (e != hipSuccess)
+        return SGEMM_ERR_LAUNCH;
+    const bool rvec = (N % 4) == 0 && aligned16(W, N) && aligned16(C, ldc);
+    e = launch_splitk_reduce(W, (int)sp.splits, M * N, (int)M, (int)N, alpha, beta, C, ldc, rvec, s);
     return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
 }
 
@@ -316,6 +451,45 @@ int sgemm_f32_plan(int algo, int64_t M, int64_t N, int64_t K, float alpha, const
                       p.transB ? 1 : 0, p.vec ? 1 : 0);
     }
     return p.status;
+}
+
+int sgemm_f32_splitk_plan(int64_t splits, int64_t M, int64_t N, int64_t K, int transB, int64_t *splits_used,
+                          int *kernel_id, int64_t *workspace_bytes)
+{
+    // Shape-only query: fake, well-separated operands with minimal leading
+    // dimensions stand in for the caller's.
+    const float *A = reinterpret_cast<const float *>((uintptr_t)1 << 40);
+    const float *B = reinterpret_cast<const float *>((uintptr_t)1 << 50);
+    const float *C = reinterpret_cast<const float *>((uintptr_t)1 << 58);
+    const int64_t lda = K > 1 ? K : 1, ldc = N > 1 ? N : 1;
+    const int64_t ldb = transB == 1 ? lda : ldc;
+    const sgemm::SplitPlan sp = sgemm::make_split_plan(splits, M, N, K, 1.0f, A, lda, B, ldb, transB, 0.0f, C, ldc,
+                                                       nullptr, 0, false);
+    if (splits_used)
+        *splits_used = sp.base.status == SGEMM_OK ? sp.splits : 0;
+    if (kernel_id)
+        *kernel_id = sp.kid;
+    if (workspace_bytes)
+        *workspace_bytes = sp.bytes;
+    return sp.base.status;
+}
+
+int sgemm_f32_ws(int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda, const float *B,
+                 int64_t ldb, int transB, float beta, float *C, int64_t ldc, void *workspace,
+                 int64_t workspace_bytes, void *stream)
+{
+    return sgemm::run_split(0, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, workspace, workspace_bytes,
+                            stream);
+}
+
+int sgemm_f32_splitk(int64_t splits, int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
+                     const float *B, int64_t ldb, int transB, float beta, float *C, int64_t ldc, void *workspace,
+                     int64_t workspace_bytes, void *stream)
+{
+    if (splits < 1)
+        return SGEMM_ERR_INVALID_VALUE;
+    return sgemm::run_split(splits, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, workspace,
+                            workspace_bytes, stream);
 }
 
 int sgemm_f32_transpose(int64_t rows, int64_t cols, const float *src, int64_t ld_src, float *dst, int64_t ld_dst,

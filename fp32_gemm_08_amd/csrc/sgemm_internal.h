@@ -16,6 +16,11 @@ struct GemmArgs {
     int M, N, K;
     float alpha, beta;
     int flags;  // GEMM_FLAG_* bits
+    // k-split partial pass (MFMA kernel, launched with gridDim.y = number of
+    // splits): split s multiplies k in [s*k_split, min(K, (s+1)*k_split)) and
+    // writes its raw product to C + s*c_split_stride.  Unused when gridDim.y == 1.
+    int k_split;
+    int64_t c_split_stride;
 };
 
 // The MFMA kernel may stage interior tiles with direct global->LDS loads, whose
@@ -47,7 +52,10 @@ hipError_t launch_scale(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_naive(const GemmArgs &a, bool transB, hipStream_t stream);
 hipError_t launch_tiled(const GemmArgs &a, bool transB, bool pad, hipStream_t stream);
 hipError_t launch_regblock(const GemmArgs &a, bool transB, bool vec, hipStream_t stream);
-hipError_t launch_mfma(const GemmArgs &a, int kid, bool transB, bool vec, hipStream_t stream);
+hipError_t launch_mfma(const GemmArgs &a, int kid, bool transB, bool vec, hipStream_t stream, int splits = 1);
+// C <- alpha * sum_{s<splits} W[s*stride + i*N + j] + beta*C (C not read when beta == 0).
+hipError_t launch_splitk_reduce(const float *W, int splits, int64_t stride, int M, int N, float alpha, float beta,
+                                float *C, int64_t ldc, bool vec, hipStream_t stream);
 
 // Number of workgroup tiles along one dimension.
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -35,6 +35,14 @@ CONFIGS = {
     "c5_tall":     dict(M=16384, N=4096, K=1024, trans_b=False, alpha=1.0, beta=1.0, dist="normal", seed=4),
 }
 
+# Products with few output tiles and a long k-range, where a caller workspace
+# lets the k-range split over workgroups.
+SPLITK_CONFIGS = {
+    "k_256x256x8192": dict(M=256, N=256, K=8192, trans_b=False, alpha=1.0, beta=0.0, dist="uniform", seed=31),
+    "k_512x512x8192": dict(M=512, N=512, K=8192, trans_b=False, alpha=1.0, beta=0.0, dist="uniform", seed=32),
+    "k_64x64x65536": dict(M=64, N=64, K=65536, trans_b=False, alpha=1.0, beta=0.0, dist="uniform", seed=33),
+}
+
 
 @dataclass
 class Case:
@@ -104,7 +112,7 @@ def make_case(M, N, K, trans_b=False, alpha=1.0, beta=0.0, dist="uniform", seed=
 
 
 def make_config(name: str, **overrides) -> Case:
-    p = dict(CONFIGS[name])
+    p = dict(CONFIGS[name] if name in CONFIGS else SPLITK_CONFIGS[name])
     p.update(overrides)
     c = make_case(**p)
     c.meta["config"] = name

@@ -27,9 +27,9 @@ ALGO = {"auto": 0, "naive": 1, "lds_tiled": 2, "regblock": 3, "mfma": 4, "lds_ti
 TRANSPOSE_ALGO = {"auto": 0, "naive": 1, "lds": 2, "lds_nopad": 3, "narrow": 4}
 
 # Symbols declared in include/sgemm_f32.h.
-EXPORTS = ("sgemm_f32", "sgemm_f32_algo", "sgemm_f32_plan", "sgemm_f32_status_string",
-           "sgemm_f32_transpose", "sgemm_f32_transpose_algo", "sgemm_f32_transpose_plan",
-           "sgemm_f32_version")
+EXPORTS = ("sgemm_f32", "sgemm_f32_algo", "sgemm_f32_plan", "sgemm_f32_splitk", "sgemm_f32_splitk_plan",
+           "sgemm_f32_status_string", "sgemm_f32_transpose", "sgemm_f32_transpose_algo",
+           "sgemm_f32_transpose_plan", "sgemm_f32_version", "sgemm_f32_ws")
 
 _lock = threading.Lock()
 _lib = None
@@ -61,6 +61,14 @@ def load():
         lib.sgemm_f32_plan.argtypes = [ci, i64, i64, i64, f32, vp, i64, vp, i64, ci, f32, vp, i64,
                                        ctypes.POINTER(ci), ctypes.POINTER(i64), ctypes.POINTER(i64),
                                        ctypes.c_char_p, ci]
+        ws_args = gemm_args[:-1] + [vp, i64, vp]
+        lib.sgemm_f32_ws.restype = ci
+        lib.sgemm_f32_ws.argtypes = ws_args
+        lib.sgemm_f32_splitk.restype = ci
+        lib.sgemm_f32_splitk.argtypes = [i64] + ws_args
+        lib.sgemm_f32_splitk_plan.restype = ci
+        lib.sgemm_f32_splitk_plan.argtypes = [i64, i64, i64, i64, ci, ctypes.POINTER(i64), ctypes.POINTER(ci),
+                                              ctypes.POINTER(i64)]
         tr_args = [i64, i64, vp, i64, vp, i64, vp]
         lib.sgemm_f32_transpose.restype = ci
         lib.sgemm_f32_transpose.argtypes = tr_args
@@ -96,6 +104,29 @@ def sgemm_f32_plan(algo, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc):
     st = load().sgemm_f32_plan(algo, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc,
                                ctypes.byref(kid), ctypes.byref(tm), ctypes.byref(tn), buf, 128)
     return st, kid.value, tm.value, tn.value, buf.value.decode()
+
+
+def sgemm_f32_ws(M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, workspace, workspace_bytes,
+                 stream=0) -> int:
+    """C <- alpha*A*op(B) + beta*C, splitting k when the workspace allows.  Returns the status."""
+    return load().sgemm_f32_ws(M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, workspace,
+                               workspace_bytes, stream)
+
+
+def sgemm_f32_splitk(splits, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, workspace, workspace_bytes,
+                     stream=0) -> int:
+    """The same with an explicit split count.  Returns the status."""
+    return load().sgemm_f32_splitk(splits, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, workspace,
+                                   workspace_bytes, stream)
+
+
+def sgemm_f32_splitk_plan(splits, M, N, K, transB=0):
+    """Host-only query: (status, splits_used, kernel_id, workspace_bytes)."""
+    su = ctypes.c_int64(0)
+    kid = ctypes.c_int(0)
+    nb = ctypes.c_int64(0)
+    st = load().sgemm_f32_splitk_plan(splits, M, N, K, transB, ctypes.byref(su), ctypes.byref(kid), ctypes.byref(nb))
+    return st, su.value, kid.value, nb.value
 
 
 def sgemm_f32_transpose(rows, cols, src, ld_src, dst, ld_dst, stream=0) -> int:
@@ -152,12 +183,15 @@ def _ld(t):
     return max(t.stride(0) if t.shape[0] > 1 else t.shape[1], t.shape[1], 1)
 
 
-def gemm(A, B, C, alpha=1.0, beta=0.0, trans_b=False, algo="auto", stream=None):
+def gemm(A, B, C, alpha=1.0, beta=0.0, trans_b=False, algo="auto", stream=None, workspace=None, splits=0):
     """C <- alpha*A*op(B) + beta*C on torch float32 CUDA tensors, in place; returns C.
 
     A is (M, K), B is (K, N) or, with trans_b, (N, K); C is (M, N).  Each may be a
     row-strided view (last-dimension stride 1); its row stride is the leading
     dimension.  Runs on ``stream`` (a torch stream) or torch's current stream.
+    With ``workspace`` (a contiguous device tensor) the product may split k over
+    several workgroups per tile (``splits`` = 0: the library's choice, else that
+    count; ``algo`` is then not used).
     """
     import torch  # plumbing only: device memory and streams
 
@@ -171,8 +205,16 @@ def gemm(A, B, C, alpha=1.0, beta=0.0, trans_b=False, algo="auto", stream=None):
     ld = _ld
     s = (stream if stream is not None else torch.cuda.current_stream(C.device)).cuda_stream
     with torch.cuda.device(C.device):
-        st = sgemm_f32_algo(_algo_id(algo), M, N, K, float(alpha), A.data_ptr(), ld(A), B.data_ptr(), ld(B),
-                            int(bool(trans_b)), float(beta), C.data_ptr(), ld(C), s)
+        if workspace is None:
+            st = sgemm_f32_algo(_algo_id(algo), M, N, K, float(alpha), A.data_ptr(), ld(A), B.data_ptr(), ld(B),
+                                int(bool(trans_b)), float(beta), C.data_ptr(), ld(C), s)
+        else:
+            if not workspace.is_cuda or not workspace.is_contiguous():
+                raise ValueError("workspace must be a contiguous device tensor")
+            nbytes = workspace.numel() * workspace.element_size()
+            args = (M, N, K, float(alpha), A.data_ptr(), ld(A), B.data_ptr(), ld(B), int(bool(trans_b)),
+                    float(beta), C.data_ptr(), ld(C), workspace.data_ptr(), nbytes, s)
+            st = sgemm_f32_splitk(int(splits), *args) if splits else sgemm_f32_ws(*args)
     _check(st)
     return C
 

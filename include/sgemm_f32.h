@@ -206,6 +206,64 @@ int sgemm_f32_transpose_plan(int algo, int64_t rows, int64_t cols, const float *
                              int64_t ld_src, const float *dst, int64_t ld_dst,
                              int *kernel_id, int64_t *blocks, char *name, int name_len);
 
+/*
+ * k-split with a caller workspace.  A product whose 64 x 64 output tiles are
+ * too few to keep the 256 CUs busy (for example 512^3, or a small M x N with a
+ * long K such as 256 x 256 x 8192) can split its k-range over several
+ * workgroups per tile: split s multiplies k in [s*kc, min(K, (s+1)*kc)) (kc a
+ * multiple of 32) into its own FP32 partial product in the workspace, and a
+ * second kernel adds the partials in a fixed order and applies the epilogue
+ *     C <- alpha * sum_s partial_s + beta*C      (C not read when beta == 0).
+ * The result is the same operation under the same accuracy contract as
+ * sgemm_f32 (each element is still a sum of its K products, "CUDA矩阵乘法性能优化
+ * 实战：从朴素内核到寄存器分块与Nsight剖析" section 1.1; splitting a sum into partial
+ * sums is the Tiling page's own device, "GPU矩阵乘法优化：共享内存Tiling技术实战"
+ * section 4.2), reproducible from call to call, but its rounding differs from
+ * the unsplit kernel's.
+ *
+ * Workspace: a DEVICE buffer owned by the caller, at least splits*M*N*4 bytes
+ * (sgemm_f32_splitk_plan reports the size), any alignment (16-byte aligned
+ * with N % 4 == 0 lets the reduction use 128-bit accesses), not overlapping A,
+ * B or C (SGEMM_ERR_ALIAS).  Its contents on entry are ignored and on return
+ * undefined; it must stay allocated until the kernels enqueued on `stream`
+ * have run.  Calls that share one workspace must be ordered on one stream.
+ * The library itself still allocates nothing.
+ */
+
+/*
+ * Host-only query, no HIP call: the split count a call with this shape would
+ * use (`splits` = 0: what sgemm_f32_ws chooses -- no split while the 64 x 64
+ * tile grid has at least 128 tiles, otherwise the most splits that keep one
+ * workgroup per CU with at least 128 of k each; otherwise the requested count,
+ * clipped to the non-empty splits), the MFMA kernel id of the partial pass, and
+ * the workspace bytes it needs.  *splits_used = 1 and *workspace_bytes = 0 when
+ * the call runs unsplit (shapes that already fill the chip, K too short to
+ * split, product-free cases).  Returns SGEMM_ERR_INVALID_VALUE for invalid
+ * dimensions, transB or a split count outside 0..64.  Output pointers may be NULL.
+ */
+int sgemm_f32_splitk_plan(int64_t splits, int64_t M, int64_t N, int64_t K, int transB,
+                          int64_t *splits_used, int *kernel_id, int64_t *workspace_bytes);
+
+/*
+ * sgemm_f32 with a workspace: splits k as sgemm_f32_splitk_plan(0, ...) reports
+ * when workspace_bytes is at least the size it reports; otherwise (including
+ * workspace == NULL) it runs exactly as sgemm_f32.
+ */
+int sgemm_f32_ws(int64_t M, int64_t N, int64_t K, float alpha,
+                 const float *A, int64_t lda, const float *B, int64_t ldb, int transB,
+                 float beta, float *C, int64_t ldc,
+                 void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * The same with an explicit split count (1..64; 1 runs the plain MFMA path).
+ * A workspace smaller than sgemm_f32_splitk_plan(splits, ...) reports is
+ * SGEMM_ERR_INVALID_VALUE.
+ */
+int sgemm_f32_splitk(int64_t splits, int64_t M, int64_t N, int64_t K, float alpha,
+                     const float *A, int64_t lda, const float *B, int64_t ldb, int transB,
+                     float beta, float *C, int64_t ldc,
+                     void *workspace, int64_t workspace_bytes, void *stream);
+
 /* Static, NUL-terminated text for a status code (unknown codes included). */
 const char *sgemm_f32_status_string(int status);
 

@@ -1,0 +1,86 @@
+"""k-split entry points without a GPU: the planning query, and every argument
+check that returns before a device call.  The addresses are fake, so every
+call here must be rejected or be a quick return: a call that passed
+validation would launch on a GPU host."""
+import os
+
+import pytest
+
+import fp32_gemm_08_amd as lib
+
+OK, INVALID, ALIAS = 0, 1, 2
+KID_L, KID_M, KID_S = 40, 41, 42
+PA, PB, PC, PW = 1 << 32, 1 << 40, 1 << 44, 1 << 48
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    if not os.path.exists(lib.LIB_PATH):
+        pytest.skip("libsgemm_f32.so not built")
+
+
+@pytest.mark.parametrize("shape,auto", [
+    ((4096, 4096, 4096), (1, KID_L, 0)),          # fills the chip: never split
+    ((2048, 2048, 2048), (1, KID_M, 0)),
+    ((1024, 1024, 1024), (1, KID_S, 0)),          # 256 tiles of 64 x 64
+    ((512, 512, 512), (4, KID_S, 4 * 512 * 512 * 4)),
+    ((768, 768, 768), (1, KID_S, 0)),              # 144 tiles: over half the CUs busy already
+    ((512, 512, 8192), (4, KID_S, 4 * 512 * 512 * 4)),
+    ((256, 256, 8192), (16, KID_S, 16 * 256 * 256 * 4)),
+    ((64, 64, 65536), (64, KID_S, 64 * 64 * 64 * 4)),
+    ((128, 128, 128), (1, KID_S, 0)),             # k too short to split at 256 per split
+])
+def test_auto_split_choice(shape, auto):
+    st, used, kid, nbytes = lib.sgemm_f32_splitk_plan(0, *shape)
+    assert st == OK and (used, kid, nbytes) == auto
+
+
+def test_explicit_split_geometry():
+    # K = 100 in 8 splits: 32 per split (whole k-tiles) leaves 4 non-empty splits.
+    assert lib.sgemm_f32_splitk_plan(8, 512, 512, 100)[:2] == (OK, 4)
+    # K <= 32 cannot split.
+    assert lib.sgemm_f32_splitk_plan(4, 512, 512, 32)[1:] == (1, KID_S, 0)
+    # an explicit count splits any shape, always with the 64 x 64 partial tile
+    assert lib.sgemm_f32_splitk_plan(4, 1024, 1024, 1024)[1:] == (4, KID_S, 4 * 1024 * 1024 * 4)
+    assert lib.sgemm_f32_splitk_plan(16, 4096, 4096, 4096)[1:] == (16, KID_S, 16 * 4096 * 4096 * 4)
+    # transB does not change the plan
+    assert lib.sgemm_f32_splitk_plan(3, 1000, 1017, 999, 1) == lib.sgemm_f32_splitk_plan(3, 1000, 1017, 999, 0)
+
+
+@pytest.mark.parametrize("args", [(-1, 64, 64, 64, 0), (65, 64, 64, 64, 0), (2, -1, 64, 64, 0),
+                                  (2, 64, 64, 1 << 31, 0), (2, 64, 64, 64, 2)])
+def test_plan_rejects_invalid(args):
+    assert lib.sgemm_f32_splitk_plan(*args)[0] == INVALID
+
+
+def call(splits, M=512, N=512, K=512, alpha=1.0, A=PA, lda=None, B=PB, ldb=None, transB=0, beta=0.0, C=PC,
+         ldc=None, W=PW, wbytes=None):
+    lda = K if lda is None else lda
+    ldb = (K if transB else N) if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    wbytes = 16 * M * N * 4 if wbytes is None else wbytes
+    if splits is None:
+        return lib.sgemm_f32_ws(M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, W, wbytes, 0)
+    return lib.sgemm_f32_splitk(splits, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, W, wbytes, 0)
+
+
+@pytest.mark.parametrize("kw", [dict(splits=0), dict(splits=-2), dict(splits=65), dict(splits=2, M=-1),
+                                dict(splits=2, lda=100), dict(splits=2, transB=3), dict(splits=2, A=0),
+                                dict(splits=4, wbytes=4 * 512 * 512 * 4 - 4), dict(splits=2, W=0),
+                                dict(splits=None, wbytes=-1)])
+def test_invalid_calls(kw):
+    assert call(**kw) == INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(W=PA), dict(W=PC + 4), dict(W=PB - 2 * 512 * 512 * 4 + 4),
+                                dict(splits=None, W=PA + 8)])
+def test_workspace_alias(kw):
+    # the 2-split partials need 2 * 512 * 512 * 4 bytes from W on
+    kw.setdefault("splits", 2)
+    assert call(**kw) == ALIAS
+
+
+def test_quick_returns_touch_nothing():
+    # No launch happens for these, so fake addresses are safe.
+    assert call(2, M=0) == OK and call(None, N=0, ldb=1, ldc=1) == OK
+    assert call(2, alpha=0.0, beta=1.0) == OK and call(None, K=0, lda=1, beta=1.0) == OK
