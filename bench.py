@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 FP32_MFMA_PEAK_TFLOPS = 157.3   # matrix cores: 256 CU x 256 FLOP/clk x 2.4 GHz
 FP32_VALU_PEAK_TFLOPS = 157.3   # vector ALU, same published figure (256 CU x 4 SIMD x 64 FLOP/clk x 2.4 GHz)
+HALF_MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16 matrix cores (published MI355X figure)
 HBM_PEAK_GBS = 8000.0
 METRIC = "FP32 GEMM TFLOP/s at 4096³ (and % of MI355X FP32 peak), 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mfma_c4_4096.txt")
@@ -88,13 +89,17 @@ def copy_calibration(nbytes=1 << 30, reps=5):
     log(f"copy calibration: {reps} copies of {nbytes} bytes ({nbytes // 1024} KiB read and written each)")
 
 
-def cpu_baseline(case, D_gpu_host, target_s):
+def cpu_baseline(case, D_gpu_host, target_s, precision=None):
     """Time the FP64 oracle on a bounded sample of the same workload (whole
-    output rows), and check those rows of the GPU result against it."""
+    output rows), and check those rows of the GPU result against it.  With a
+    precision, the mixed-precision oracle (operands rounded first)."""
     import numpy as np
 
     import oracle
     M, N, K = case.M, case.N, case.K
+    if precision is not None:
+        import dataclasses
+        case = dataclasses.replace(case, A=oracle.round_to(precision, case.A), B=oracle.round_to(precision, case.B))
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
     rng = np.random.default_rng(12345)
     # calibrate with one row per thread
@@ -441,6 +446,9 @@ def main():
     ap.add_argument("--config", default="c4_4096",
                     help="workload name (GEMM: c1_128 ... c5_tall; transpose: t_4096 ...)")
     ap.add_argument("--algo", default="auto")
+    ap.add_argument("--precision", choices=("fp32", "fp16", "bf16"), default="fp32",
+                    help="GEMM: fp16/bf16 run sgemm_f32_lowp (operands rounded to that format, FP32 sums), "
+                         "reported against the dense fp16/bf16 matrix-core peak")
     ap.add_argument("--workspace", action="store_true",
                     help="GEMM: call sgemm_f32_ws with the workspace its plan asks for (k-split when the "
                          "output tiles are too few; a step is then the partial pass plus the reduction)")
@@ -501,7 +509,14 @@ def main():
     if st != 0:
         raise SystemExit(f"plan failed: {lib.sgemm_f32_status_string(st)}")
     splits, ws, ws_bytes = 1, None, 0
-    if args.workspace:
+    lowp = args.precision != "fp32"
+    if lowp:
+        st, kid, tm, tn, kname = lib.sgemm_f32_lowp_plan(lib.PRECISION[args.precision], M, N, K, case.alpha, pa,
+                                                         case.lda, pb, case.ldb, int(case.trans_b), case.beta, pc,
+                                                         case.ldc)
+        if st != 0:
+            raise SystemExit(f"plan failed: {lib.sgemm_f32_status_string(st)}")
+    if args.workspace and not lowp:
         _, splits, skid, ws_bytes = lib.sgemm_f32_splitk_plan(0, M, N, K, int(case.trans_b))
         if splits > 1:
             ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device=dev)
@@ -510,7 +525,10 @@ def main():
             tm, tn = -(-M // 64) * splits, -(-N // 64)
 
     def step():
-        if ws is not None:
+        if lowp:
+            s = lib.sgemm_f32_lowp(lib.PRECISION[args.precision], M, N, K, case.alpha, pa, case.lda, pb, case.ldb,
+                                   int(case.trans_b), case.beta, pc, case.ldc, sp)
+        elif ws is not None:
             s = lib.sgemm_f32_ws(M, N, K, case.alpha, pa, case.lda, pb, case.ldb, int(case.trans_b), case.beta,
                                  pc, case.ldc, ws.data_ptr(), ws_bytes, sp)
         else:
@@ -543,8 +561,8 @@ def main():
     value = K_steps * flop / wall / 1e12
     kern_avg = span / K_steps
     achieved = flop / kern_avg / 1e12
-    mfma = kid in (40, 41, 42)
-    peak = FP32_MFMA_PEAK_TFLOPS if mfma else FP32_VALU_PEAK_TFLOPS
+    mfma = kid in (40, 41, 42, 60, 61)
+    peak = HALF_MFMA_PEAK_TFLOPS if lowp else FP32_MFMA_PEAK_TFLOPS if mfma else FP32_VALU_PEAK_TFLOPS
     log(f"{'step (both kernels)' if ws is not None else 'kernel'} {kname}: avg {kern_avg * 1e3:.4f} ms "
         f"over {K_steps} calls "
         f"(event span {span * 1e3:.3f} ms, wall {wall * 1e3:.3f} ms)")
@@ -558,7 +576,8 @@ def main():
     D_host = dC.cpu().numpy()
 
     out = {
-        "metric": METRIC if args.config == "c4_4096" else f"FP32 GEMM TFLOP/s ({args.config}), 1 GPU",
+        "metric": (METRIC if args.config == "c4_4096" else f"FP32 GEMM TFLOP/s ({args.config}), 1 GPU")
+        if not lowp else f"mixed-precision GEMM TFLOP/s ({args.precision} operands, FP32 sums; {args.config}), 1 GPU",
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -568,9 +587,9 @@ def main():
         "higher_is_better": True,
         "scaling": "strong",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32" if not lowp else f"{args.precision} operands, f32 accumulate",
         "data": "synthetic",
-        "pct_of_peak": round(100.0 * value / FP32_MFMA_PEAK_TFLOPS, 2),
+        "pct_of_peak": round(100.0 * value / (HALF_MFMA_PEAK_TFLOPS if lowp else FP32_MFMA_PEAK_TFLOPS), 2),
         "config": {
             "workload": f"sgemm {M}x{N}x{K} row-major, D=alpha*A*{'B^T' if case.trans_b else 'B'}+beta*C, "
                         f"alpha={case.alpha:g}, beta={case.beta:g}, {case.meta['dist']} inputs, "
@@ -596,7 +615,8 @@ def main():
     out["roofline"]["traffic"] = traffic
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on a sample of rows for ~{args.cpu_seconds:.0f} s")
-        out["cpu_baseline"] = cpu_baseline(case, D_host, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(case, D_host, args.cpu_seconds,
+                                           None if not lowp else args.precision)
     print(json.dumps(out), flush=True)
 
 

@@ -225,6 +225,8 @@ const char *kernel_label(int kid)
     case KID_MFMA_L: return "mfma_256x256x32_w4x2";
     case KID_MFMA_M: return "mfma_128x128x32_w2x2_ks2";
     case KID_MFMA_S: return "mfma_64x64x32_w2x2";
+    case KID_MFMA_LP_F16: return "mfma_lp_f16_256x256x32_w4x2";
+    case KID_MFMA_LP_BF16: return "mfma_lp_bf16_256x256x32_w4x2";
     case KID_TRANSPOSE_NAIVE: return "transpose_naive_64x16";
     case KID_TRANSPOSE_LDS_PAD: return "transpose_lds_128x128_pad1";
     case KID_TRANSPOSE_LDS_NOPAD: return "transpose_lds_128x128_pad0";
@@ -397,6 +399,62 @@ int run_split(int64_t splits_req, int64_t M, int64_t N, int64_t K, float alpha, 
     return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
 }
 
+// Mixed precision: the FP32 call's validation and quick returns; the product
+// runs the 16-bit MFMA kernel.
+Plan make_lowp_plan(int precision, int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
+                    const float *B, int64_t ldb, int transB, float beta, const float *C, int64_t ldc)
+{
+    if (precision != SGEMM_PREC_FP16 && precision != SGEMM_PREC_BF16) {
+        Plan p;
+        p.status = SGEMM_ERR_INVALID_VALUE;
+        return p;
+    }
+    Plan p = make_plan(SGEMM_ALGO_AUTO, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc);
+    if (p.status != SGEMM_OK || !(p.kid == KID_MFMA_L || p.kid == KID_MFMA_M || p.kid == KID_MFMA_S))
+        return p;
+    p.kid = precision == SGEMM_PREC_BF16 ? KID_MFMA_LP_BF16 : KID_MFMA_LP_F16;
+    const TileShape t = lp_tile_shape();
+    p.tiles_m = ceil_div(M, t.bm);
+    p.tiles_n = ceil_div(N, t.bn);
+    if (p.tiles_m * p.tiles_n * 512 > kMaxWorkItems) {
+        p.status = SGEMM_ERR_INVALID_VALUE;
+        p.kid = KID_NONE;
+    }
+    return p;
+}
+
+int run_lowp(int precision, int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
+             const float *B, int64_t ldb, int transB, float beta, float *C, int64_t ldc, void *stream)
+{
+    const Plan p = make_lowp_plan(precision, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc);
+    if (p.status != SGEMM_OK || p.kid == KID_NONE)
+        return p.status;
+    if (p.kid == KID_SCALE)  // no product: C <- beta*C, the same as the FP32 call
+        return run(SGEMM_ALGO_AUTO, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, stream);
+    const int dev_status = check_device();
+    if (dev_status != SGEMM_OK)
+        return dev_status;
+    GemmArgs a;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.lda = lda;
+    a.ldb = ldb;
+    a.ldc = ldc;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.flags = 0;
+    a.k_split = 0;
+    a.c_split_stride = 0;
+    (void)hipGetLastError();
+    const hipError_t e = launch_mfma_lp(a, p.kid == KID_MFMA_LP_BF16, p.transB, p.vec,
+                                        reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
+}
+
 int run_transpose(int algo, int64_t rows, int64_t cols, const float *src, int64_t ld_src, float *dst,
                   int64_t ld_dst, void *stream)
 {
@@ -490,6 +548,29 @@ int sgemm_f32_splitk(int64_t splits, int64_t M, int64_t N, int64_t K, float alph
         return SGEMM_ERR_INVALID_VALUE;
     return sgemm::run_split(splits, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, workspace,
                             workspace_bytes, stream);
+}
+
+int sgemm_f32_lowp(int precision, int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
+                   const float *B, int64_t ldb, int transB, float beta, float *C, int64_t ldc, void *stream)
+{
+    return sgemm::run_lowp(precision, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, stream);
+}
+
+int sgemm_f32_lowp_plan(int precision, int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
+                        const float *B, int64_t ldb, int transB, float beta, const float *C, int64_t ldc,
+                        int *kernel_id, int64_t *tiles_m, int64_t *tiles_n, char *name, int name_len)
+{
+    const sgemm::Plan p = sgemm::make_lowp_plan(precision, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc);
+    if (kernel_id)
+        *kernel_id = p.kid;
+    if (tiles_m)
+        *tiles_m = p.kid == sgemm::KID_NONE ? 0 : p.tiles_m;
+    if (tiles_n)
+        *tiles_n = p.kid == sgemm::KID_NONE ? 0 : p.tiles_n;
+    if (name && name_len > 0)
+        std::snprintf(name, (size_t)name_len, "%s transB=%d vec=%d", sgemm::kernel_label(p.kid), p.transB ? 1 : 0,
+                      p.vec ? 1 : 0);
+    return p.status;
 }
 
 int sgemm_f32_transpose(int64_t rows, int64_t cols, const float *src, int64_t ld_src, float *dst, int64_t ld_dst,

@@ -39,6 +39,8 @@ enum KernelId : int {
     KID_MFMA_L = 40,        // 256 x 256 macro tile, 8 wavefronts
     KID_MFMA_M = 41,        // 128 x 128, 8 wavefronts: 2 x 2 over the tile x 2 over k
     KID_MFMA_S = 42,        // 64 x 64, 4 wavefronts
+    KID_MFMA_LP_F16 = 60,   // mixed precision, operands rounded to fp16, 256 x 256
+    KID_MFMA_LP_BF16 = 61,  // the same with bf16
 };
 
 // Tile geometry of each kernel (rows x cols of C per workgroup).
@@ -53,6 +55,9 @@ hipError_t launch_naive(const GemmArgs &a, bool transB, hipStream_t stream);
 hipError_t launch_tiled(const GemmArgs &a, bool transB, bool pad, hipStream_t stream);
 hipError_t launch_regblock(const GemmArgs &a, bool transB, bool vec, hipStream_t stream);
 hipError_t launch_mfma(const GemmArgs &a, int kid, bool transB, bool vec, hipStream_t stream, int splits = 1);
+// Mixed precision: operands rounded to fp16 (bf16 = false) or bf16 while staged.
+hipError_t launch_mfma_lp(const GemmArgs &a, bool bf16, bool transB, bool vec, hipStream_t stream);
+TileShape lp_tile_shape();
 // C <- alpha * sum_{s<splits} W[s*stride + i*N + j] + beta*C (C not read when beta == 0).
 hipError_t launch_splitk_reduce(const float *W, int splits, int64_t stride, int M, int N, float alpha, float beta,
                                 float *C, int64_t ldc, bool vec, hipStream_t stream);

@@ -27,7 +27,10 @@ ALGO = {"auto": 0, "naive": 1, "lds_tiled": 2, "regblock": 3, "mfma": 4, "lds_ti
 TRANSPOSE_ALGO = {"auto": 0, "naive": 1, "lds": 2, "lds_nopad": 3, "narrow": 4}
 
 # Symbols declared in include/sgemm_f32.h.
-EXPORTS = ("sgemm_f32", "sgemm_f32_algo", "sgemm_f32_plan", "sgemm_f32_splitk", "sgemm_f32_splitk_plan",
+PRECISION = {"fp16": 1, "bf16": 2}
+
+EXPORTS = ("sgemm_f32", "sgemm_f32_algo", "sgemm_f32_lowp", "sgemm_f32_lowp_plan", "sgemm_f32_plan",
+           "sgemm_f32_splitk", "sgemm_f32_splitk_plan",
            "sgemm_f32_status_string", "sgemm_f32_transpose", "sgemm_f32_transpose_algo",
            "sgemm_f32_transpose_plan", "sgemm_f32_version", "sgemm_f32_ws")
 
@@ -61,6 +64,12 @@ def load():
         lib.sgemm_f32_plan.argtypes = [ci, i64, i64, i64, f32, vp, i64, vp, i64, ci, f32, vp, i64,
                                        ctypes.POINTER(ci), ctypes.POINTER(i64), ctypes.POINTER(i64),
                                        ctypes.c_char_p, ci]
+        lib.sgemm_f32_lowp.restype = ci
+        lib.sgemm_f32_lowp.argtypes = [ci] + gemm_args
+        lib.sgemm_f32_lowp_plan.restype = ci
+        lib.sgemm_f32_lowp_plan.argtypes = [ci, i64, i64, i64, f32, vp, i64, vp, i64, ci, f32, vp, i64,
+                                            ctypes.POINTER(ci), ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                            ctypes.c_char_p, ci]
         ws_args = gemm_args[:-1] + [vp, i64, vp]
         lib.sgemm_f32_ws.restype = ci
         lib.sgemm_f32_ws.argtypes = ws_args
@@ -103,6 +112,22 @@ def sgemm_f32_plan(algo, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc):
     buf = ctypes.create_string_buffer(128)
     st = load().sgemm_f32_plan(algo, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc,
                                ctypes.byref(kid), ctypes.byref(tm), ctypes.byref(tn), buf, 128)
+    return st, kid.value, tm.value, tn.value, buf.value.decode()
+
+
+def sgemm_f32_lowp(precision, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, stream=0) -> int:
+    """Mixed precision: operands rounded to fp16 (1) or bf16 (2), FP32 sums.  Returns the status."""
+    return load().sgemm_f32_lowp(precision, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, stream)
+
+
+def sgemm_f32_lowp_plan(precision, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc):
+    """Host-only planning query: (status, kernel_id, tiles_m, tiles_n, name)."""
+    kid = ctypes.c_int(0)
+    tm = ctypes.c_int64(0)
+    tn = ctypes.c_int64(0)
+    buf = ctypes.create_string_buffer(128)
+    st = load().sgemm_f32_lowp_plan(precision, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc,
+                                    ctypes.byref(kid), ctypes.byref(tm), ctypes.byref(tn), buf, 128)
     return st, kid.value, tm.value, tn.value, buf.value.decode()
 
 
@@ -183,7 +208,8 @@ def _ld(t):
     return max(t.stride(0) if t.shape[0] > 1 else t.shape[1], t.shape[1], 1)
 
 
-def gemm(A, B, C, alpha=1.0, beta=0.0, trans_b=False, algo="auto", stream=None, workspace=None, splits=0):
+def gemm(A, B, C, alpha=1.0, beta=0.0, trans_b=False, algo="auto", stream=None, workspace=None, splits=0,
+         precision=None):
     """C <- alpha*A*op(B) + beta*C on torch float32 CUDA tensors, in place; returns C.
 
     A is (M, K), B is (K, N) or, with trans_b, (N, K); C is (M, N).  Each may be a
@@ -191,7 +217,9 @@ def gemm(A, B, C, alpha=1.0, beta=0.0, trans_b=False, algo="auto", stream=None, 
     dimension.  Runs on ``stream`` (a torch stream) or torch's current stream.
     With ``workspace`` (a contiguous device tensor) the product may split k over
     several workgroups per tile (``splits`` = 0: the library's choice, else that
-    count; ``algo`` is then not used).
+    count; ``algo`` is then not used).  With ``precision`` ("fp16" or "bf16")
+    the operands are rounded to that format and multiplied by the 16-bit matrix
+    cores with FP32 sums (sgemm_f32_lowp).
     """
     import torch  # plumbing only: device memory and streams
 
@@ -205,7 +233,12 @@ def gemm(A, B, C, alpha=1.0, beta=0.0, trans_b=False, algo="auto", stream=None, 
     ld = _ld
     s = (stream if stream is not None else torch.cuda.current_stream(C.device)).cuda_stream
     with torch.cuda.device(C.device):
-        if workspace is None:
+        if precision is not None:
+            if workspace is not None:
+                raise ValueError("the mixed-precision path takes no workspace")
+            st = sgemm_f32_lowp(PRECISION[precision], M, N, K, float(alpha), A.data_ptr(), ld(A), B.data_ptr(),
+                                ld(B), int(bool(trans_b)), float(beta), C.data_ptr(), ld(C), s)
+        elif workspace is None:
             st = sgemm_f32_algo(_algo_id(algo), M, N, K, float(alpha), A.data_ptr(), ld(A), B.data_ptr(), ld(B),
                                 int(bool(trans_b)), float(beta), C.data_ptr(), ld(C), s)
         else:

@@ -207,6 +207,49 @@ int sgemm_f32_transpose_plan(int algo, int64_t rows, int64_t cols, const float *
                              int *kernel_id, int64_t *blocks, char *name, int name_len);
 
 /*
+ * Mixed precision (a variant with its own accuracy contract, not a faster
+ * sgemm_f32):
+ *
+ *     C  <-  alpha * r(A) * r(op(B)) + beta * C
+ *
+ * A, B and C are the same FP32 row-major matrices as for sgemm_f32 (same
+ * layout, leading dimensions, ownership, asynchrony, quick returns, errors and
+ * aliasing rules); r converts each operand element to IEEE binary16 (`fp16`)
+ * or to bfloat16 (`bf16`), rounding to nearest with ties to even, as the tile
+ * is staged into LDS, and the matrix cores (v_mfma_f32_32x32x16_f16 / _bf16)
+ * multiply the converted values and sum the products in FP32.  This is the
+ * half-precision variant of "GPU矩阵乘法优化：共享内存Tiling技术实战", section 7.1
+ * (convert to half precision before the matrix cores), with bfloat16 as the
+ * second format.  fp16 keeps 11 significant bits and overflows past 65504
+ * (values that large become inf); bf16 keeps 8 significant bits with the FP32
+ * exponent range.  C, alpha and beta stay FP32.
+ *
+ * Accuracy: against the exact result on the ROUNDED operands,
+ *     |D - D~| <= 4*K*2^-24 * sum_k |r(a(i,k)) * r(b(k,j))| + 1e-6
+ * (every product of two rounded operands is exact in FP32, so only the
+ * summation rounds).  Against the exact FP32-operand product the difference
+ * is larger by up to (2u + u^2) * sum_k |a*b|, u = 2^-11 (fp16) or 2^-8 (bf16)
+ * -- the numerical-stability caveat of that section.
+ */
+typedef enum {
+    SGEMM_PREC_FP16 = 1,
+    SGEMM_PREC_BF16 = 2
+} sgemm_precision;
+
+/* The mixed-precision GEMM above; `precision` is an sgemm_precision value
+ * (anything else: SGEMM_ERR_INVALID_VALUE).  Returns an sgemm_status. */
+int sgemm_f32_lowp(int precision, int64_t M, int64_t N, int64_t K, float alpha,
+                   const float *A, int64_t lda, const float *B, int64_t ldb, int transB,
+                   float beta, float *C, int64_t ldc, void *stream);
+
+/* Host-only planning query for sgemm_f32_lowp, the counterpart of sgemm_f32_plan. */
+int sgemm_f32_lowp_plan(int precision, int64_t M, int64_t N, int64_t K, float alpha,
+                        const float *A, int64_t lda, const float *B, int64_t ldb, int transB,
+                        float beta, const float *C, int64_t ldc,
+                        int *kernel_id, int64_t *tiles_m, int64_t *tiles_n,
+                        char *name, int name_len);
+
+/*
  * k-split with a caller workspace.  A product whose 64 x 64 output tiles are
  * too few to keep the 256 CUs busy (for example 512^3, or a small M x N with a
  * long K such as 256 x 256 x 8192) can split its k-range over several

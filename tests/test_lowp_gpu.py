@@ -1,0 +1,164 @@
+"""GPU parity of the mixed-precision GEMM (sgemm_f32_lowp) through the C ABI.
+
+Bar: against the oracle on the rounded operands (fp16 or bf16, nearest-even),
+|D_gpu - D~| <= 4*K*2^-24*S~ + 1e-6 elementwise and finite, S~ = sum |r(a) r(b)|;
+bit-exact where every operand is representable and every sum exact (small
+integers).  Against the exact FP32-operand product the derived contract
+|D_gpu - D| <= (2u + u^2)*S + 4*K*2^-24*S~ + 1e-6 is checked too.  C carries
+canary guard rows and padding columns.
+"""
+import numpy as np
+import pytest
+
+import fp32_gemm_08_amd as lib
+from fp32_gemm_08_amd.inputs import make_case, make_config
+from oracle import check, gemm_lowp_rows, gemm_rows
+
+from gpu_helpers import CANARY, GUARD_ROWS, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+PRECS = ["fp16", "bf16"]
+UNIT = {"fp16": 2.0 ** -11, "bf16": 2.0 ** -8}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    assert lib.sgemm_f32_version()
+
+
+def run_lowp(case, prec, a_offset=0, ldc_pad=0, c_fill=np.nan):
+    import torch
+
+    dev = torch.device("cuda", 0)
+    M, N, K = case.M, case.N, case.K
+    ldc = case.ldc + ldc_pad
+    g = GUARD_ROWS
+    full = np.full((M + 2 * g, ldc), CANARY, dtype=np.float32)
+    full[g:g + M, :N] = case.C[:, :N] if case.C is not None else c_fill
+    dA = torch.from_numpy(np.concatenate([np.zeros(a_offset, np.float32), case.A.ravel()])).to(dev)
+    dB = torch.from_numpy(case.B.ravel().copy()).to(dev)
+    dC = torch.from_numpy(full.ravel().copy()).to(dev)
+    say(f"lowp {prec} M={M} N={N} K={K} transB={int(case.trans_b)} alpha={case.alpha} beta={case.beta} "
+        f"lda={case.lda} ldb={case.ldb} ldc={ldc} a_offset={a_offset} meta={case.meta}")
+    st = lib.sgemm_f32_lowp(lib.PRECISION[prec], M, N, K, case.alpha, dA.data_ptr() + 4 * a_offset, case.lda,
+                            dB.data_ptr(), case.ldb, int(case.trans_b), case.beta, dC.data_ptr() + 4 * g * ldc,
+                            ldc, torch.cuda.current_stream(dev).cuda_stream)
+    torch.cuda.synchronize()
+    out = dC.cpu().numpy().reshape(M + 2 * g, ldc)
+    assert np.all(out[:g].view(np.uint32) == CANARY.view(np.uint32)), "write above C"
+    assert np.all(out[g + M:].view(np.uint32) == CANARY.view(np.uint32)), "write below C"
+    if ldc > N:
+        assert np.all(out[g:g + M, N:].view(np.uint32) == CANARY.view(np.uint32)), "write into C padding"
+    return st, out[g:g + M, :N]
+
+
+def assert_lowp_parity(case, prec, D_gpu, rows=None, what=""):
+    D, S, _ = gemm_lowp_rows(prec, case.M, case.N, case.K, case.alpha, case.A, case.B, case.trans_b, case.beta,
+                             case.C, rows=rows)
+    Dg = D_gpu if rows is None else D_gpu[rows]
+    r = check(Dg, D, S, case.K)
+    say(f"{what} {prec}: max_abs={r['max_abs']:.3e} max_rho={r['max_rho']:.3f} fails={r['n_fail']}")
+    assert r["ok"], f"{what} {prec}: {r}"
+    # derived contract against the exact FP32-operand product
+    De, Se, _ = gemm_rows(case.M, case.N, case.K, case.alpha, case.A, case.B, case.trans_b, case.beta, case.C,
+                          rows=rows)
+    u = UNIT[prec]
+    bound = abs(case.alpha) * (2 * u + u * u) * Se + 4 * case.K * 2.0 ** -24 * S + 1e-6
+    err = np.abs(Dg.astype(np.float64) - De)
+    say(f"   vs FP32 operands: max |d| = {err.max():.3e}, max |d|/bound = {(err / bound).max():.3f}")
+    assert np.all(err <= bound)
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("name", ["c1_128", "c2_1024", "c3_ragged_bt", "c5_512"])
+def test_configs_full(prec, name):
+    case = make_config(name)
+    st, D = run_lowp(case, prec)
+    assert st == 0
+    assert_lowp_parity(case, prec, D, what=name)
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("name", ["c4_4096", "c5_2048", "c5_tall"])
+def test_configs_sampled(prec, name):
+    case = make_config(name)
+    st, D = run_lowp(case, prec)
+    assert st == 0
+    assert_lowp_parity(case, prec, D, rows=sample_rows(case.M, n=16, tile=256), what=name)
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("tb", [False, True])
+def test_integers_bit_exact(prec, tb):
+    # {-2..2} are exact in both formats and every partial sum is an exact small integer
+    case = make_case(300, 520, 1000, trans_b=tb, alpha=1.0, beta=1.0, dist="int2", seed=41)
+    st, D = run_lowp(case, prec)
+    assert st == 0
+    Dref, _, _ = gemm_lowp_rows(prec, 300, 520, 1000, 1.0, case.A, case.B, tb, 1.0, case.C)
+    assert np.array_equal(D.astype(np.float64), Dref)
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("shape", [(257, 255, 33, False, dict(lda=35)), (300, 270, 131, True, dict(ldb=140)),
+                                   (513, 1, 700, False, {}), (1, 700, 513, True, {}), (256, 256, 32, False, {})])
+def test_edges_and_unaligned(prec, shape):
+    M, N, K, tb, extra = shape
+    case = make_case(M, N, K, trans_b=tb, alpha=-0.75, beta=0.5, seed=M + N + K, **extra)
+    st, D = run_lowp(case, prec, ldc_pad=3)
+    assert st == 0
+    assert_lowp_parity(case, prec, D, what=f"{M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("prec", PRECS)
+def test_misaligned_base(prec):
+    case = make_case(400, 384, 260, seed=43)
+    st, D = run_lowp(case, prec, a_offset=1)
+    assert st == 0
+    assert_lowp_parity(case, prec, D, what="misaligned A")
+
+
+@pytest.mark.parametrize("prec", PRECS)
+def test_beta_zero_ignores_nan_c(prec):
+    case = make_case(300, 300, 300, alpha=2.0, beta=0.0, seed=44)
+    st, D = run_lowp(case, prec, c_fill=np.nan)
+    assert st == 0 and np.all(np.isfinite(D))
+    assert_lowp_parity(case, prec, D, what="beta 0")
+
+
+@pytest.mark.parametrize("prec,want", [("fp16", 1.0), ("bf16", 1.0)])
+def test_rounding_is_visible(prec, want):
+    # operands at a rounding tie of the format: the product uses the rounded value
+    tie = 1 + 2 ** -11 if prec == "fp16" else 1 + 2 ** -8
+    case = make_case(64, 64, 64, seed=45)
+    case.A[:] = np.float32(tie)
+    case.B[:] = np.float32(1.0)
+    st, D = run_lowp(case, prec)
+    assert st == 0 and np.all(D == 64 * want)
+
+
+def test_fp16_overflow_and_bf16_range():
+    # 1e5 is beyond fp16 (inf) but inside bf16's range (99840)
+    case = make_case(64, 96, 40, seed=46)
+    case.A[:] = np.float32(1.0)
+    case.B[:] = np.float32(1.0)
+    case.A[5, 7] = np.float32(1e5)
+    st, D16 = run_lowp(case, "fp16")
+    assert st == 0 and np.all(np.isposinf(D16[5])) and np.all(D16[np.arange(64) != 5] == 40.0)
+    st, Db = run_lowp(case, "bf16")
+    assert st == 0 and np.all(Db[5] == 99840.0 + 39.0)
+
+
+def test_torch_wrapper():
+    import torch
+
+    dev = torch.device("cuda", 0)
+    case = make_case(320, 256, 192, trans_b=True, alpha=1.25, seed=47)
+    A, B = torch.from_numpy(case.A).to(dev), torch.from_numpy(case.B).to(dev)
+    C = torch.empty(320, 256, device=dev)
+    lib.gemm(A, B, C, alpha=1.25, trans_b=True, precision="bf16")
+    torch.cuda.synchronize()
+    assert_lowp_parity(case, "bf16", C.cpu().numpy(), what="wrapper")
