@@ -131,7 +131,7 @@ def cpu_baseline(case, D_gpu_host, target_s, precision=None):
     }
 
 
-def sweep(algos=("naive", "lds_tiled", "lds_tiled_nopad", "regblock", "mfma")):
+def sweep(algos=("naive", "naive_wg", "lds_tiled", "lds_tiled_nopad", "regblock", "mfma")):
     """Every algorithm on every workload: average kernel time over back-to-back
     calls (after a warm-up that brings the engine clock to its steady state)."""
     import torch
@@ -163,7 +163,7 @@ def sweep(algos=("naive", "lds_tiled", "lds_tiled_nopad", "regblock", "mfma")):
             st, kid, tm, tn, kname = lib.sgemm_f32_plan(a, M, N, K, case.alpha, dA.data_ptr(), case.lda,
                                                         dB.data_ptr(), case.ldb, int(case.trans_b), case.beta,
                                                         dC.data_ptr(), case.ldc)
-            rate = 3e12 if algo in ("naive", "lds_tiled", "lds_tiled_nopad") else 60e12
+            rate = 3e12 if algo in ("naive", "naive_wg", "lds_tiled", "lds_tiled_nopad") else 60e12
             reps = int(max(3, min(200, 0.2 / max(flop / rate, 1e-7))))
 
             def call():

@@ -684,6 +684,7 @@ TileShape tile_shape(int kid)
     case KID_TILED_PAD:
     case KID_TILED_NOPAD: return {16, 16};
     case KID_NAIVE: return {4, 64};
+    case KID_NAIVE_WG: return {1, 1};
     default: return {0, 0};
     }
 }

@@ -37,6 +37,44 @@ __global__ __launch_bounds__(256) void sgemm_naive_kernel(GemmArgs a)
     *cp = (a.beta == 0.0f) ? a.alpha * acc : fmaf(a.alpha, acc, a.beta * *cp);
 }
 
+// The second naive formulation (Baidu Cloud article comparing the naive and 2-D
+// block-tiled CUDA matmul, paragraph on the naive implementation: one block per
+// output element, its threads forming partial products that the block reduces):
+// a group of work-items shares one output element; each forms a partial dot
+// product and the group reduces them.  On MI355X the group is one
+// 64-lane wavefront: lane l sums k = l, l+64, l+128, ... (the A row is read
+// contiguously across the lanes; B's column is strided unless op(B) = B^T), and
+// the 64 partials are added by a fixed butterfly of cross-lane exchanges
+// (xor 32, 16, 8, 4, 2, 1), so every lane ends with the same, reproducible sum.
+// Workgroups of one wavefront loop over the output elements.
+template <bool TRANS_B>
+__global__ __launch_bounds__(64) void sgemm_naive_wg_kernel(GemmArgs a)
+{
+    const int lane = threadIdx.x;
+    const int64_t outputs = (int64_t)a.M * a.N;
+    for (int64_t o = blockIdx.x; o < outputs; o += gridDim.x) {
+        const int row = (int)(o / a.N), col = (int)(o % a.N);
+        const float *__restrict__ arow = a.A + (int64_t)row * a.lda;
+        float part = 0.0f;
+        if (TRANS_B) {
+            const float *__restrict__ brow = a.B + (int64_t)col * a.ldb;
+            for (int k = lane; k < a.K; k += 64)
+                part = fmaf(arow[k], brow[k], part);
+        } else {
+            const float *__restrict__ bcol = a.B + col;
+            for (int k = lane; k < a.K; k += 64)
+                part = fmaf(arow[k], bcol[(int64_t)k * a.ldb], part);
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1)
+            part += __shfl_xor(part, off, 64);
+        if (lane == 0) {
+            float *cp = a.C + (int64_t)row * a.ldc + col;
+            *cp = (a.beta == 0.0f) ? a.alpha * part : fmaf(a.alpha, part, a.beta * *cp);
+        }
+    }
+}
+
 // C <- beta*C over the M x N window; beta == 0 writes zeros without reading C.
 __global__ __launch_bounds__(256) void sgemm_scale_kernel(GemmArgs a)
 {
@@ -56,6 +94,17 @@ hipError_t launch_naive(const GemmArgs &a, bool transB, hipStream_t stream)
         sgemm_naive_kernel<true><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(a);
     else
         sgemm_naive_kernel<false><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_naive_wg(const GemmArgs &a, bool transB, hipStream_t stream)
+{
+    const int64_t outputs = (int64_t)a.M * a.N;
+    const int64_t blocks = outputs < (1 << 20) ? outputs : (1 << 20);
+    if (transB)
+        sgemm_naive_wg_kernel<true><<<dim3((unsigned)blocks), dim3(64), 0, stream>>>(a);
+    else
+        sgemm_naive_wg_kernel<false><<<dim3((unsigned)blocks), dim3(64), 0, stream>>>(a);
     return hipGetLastError();
 }
 

@@ -105,7 +105,7 @@ Plan make_plan(int algo, int64_t M, int64_t N, int64_t K, float alpha, const flo
         p.kid = KID_NONE;
         return p;
     };
-    if (algo < SGEMM_ALGO_AUTO || algo > SGEMM_ALGO_LDS_TILED_NOPAD)
+    if (algo < SGEMM_ALGO_AUTO || algo > SGEMM_ALGO_NAIVE_WG)
         return fail(SGEMM_ERR_INVALID_VALUE);
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
         return fail(SGEMM_ERR_INVALID_VALUE);
@@ -142,6 +142,7 @@ Plan make_plan(int algo, int64_t M, int64_t N, int64_t K, float alpha, const flo
     p.vec = aligned16(A, lda) && aligned16(B, ldb);
     switch (algo) {
     case SGEMM_ALGO_NAIVE: p.kid = KID_NAIVE; break;
+    case SGEMM_ALGO_NAIVE_WG: p.kid = KID_NAIVE_WG; break;
     case SGEMM_ALGO_LDS_TILED: p.kid = KID_TILED_PAD; break;
     case SGEMM_ALGO_LDS_TILED_NOPAD: p.kid = KID_TILED_NOPAD; break;
     case SGEMM_ALGO_REGBLOCK: p.kid = KID_REGBLOCK; break;
@@ -151,7 +152,8 @@ Plan make_plan(int algo, int64_t M, int64_t N, int64_t K, float alpha, const flo
     const TileShape t = tile_shape(p.kid);
     p.tiles_m = ceil_div(M, t.bm);
     p.tiles_n = ceil_div(N, t.bn);
-    if (p.tiles_m * p.tiles_n * threads_per_block(p.kid) > kMaxWorkItems)
+    // (the wavefront-per-output kernel loops over outputs with a capped grid)
+    if (p.kid != KID_NAIVE_WG && p.tiles_m * p.tiles_n * threads_per_block(p.kid) > kMaxWorkItems)
         return fail(SGEMM_ERR_INVALID_VALUE);
     return p;
 }
@@ -219,6 +221,7 @@ const char *kernel_label(int kid)
     case KID_NONE: return "none";
     case KID_SCALE: return "scale";
     case KID_NAIVE: return "naive";
+    case KID_NAIVE_WG: return "naive_wave_per_output";
     case KID_TILED_PAD: return "lds_tiled_16x16_pad1";
     case KID_TILED_NOPAD: return "lds_tiled_16x16_pad0";
     case KID_REGBLOCK: return "regblock_128x128x8_t8x8";
@@ -287,6 +290,7 @@ int run(int algo, int64_t M, int64_t N, int64_t K, float alpha, const float *A, 
     switch (p.kid) {
     case KID_SCALE: e = launch_scale(a, s); break;
     case KID_NAIVE: e = launch_naive(a, p.transB, s); break;
+    case KID_NAIVE_WG: e = launch_naive_wg(a, p.transB, s); break;
     case KID_TILED_PAD: e = launch_tiled(a, p.transB, true, s); break;
     case KID_TILED_NOPAD: e = launch_tiled(a, p.transB, false, s); break;
     case KID_REGBLOCK: e = launch_regblock(a, p.transB, p.vec, s); break;

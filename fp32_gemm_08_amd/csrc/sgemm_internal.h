@@ -33,6 +33,7 @@ enum KernelId : int {
     KID_NONE = 0,
     KID_SCALE = 1,          // C <- beta*C (alpha == 0 or K == 0)
     KID_NAIVE = 10,
+    KID_NAIVE_WG = 11,      // one wavefront per output element, cross-lane reduction
     KID_TILED_PAD = 20,
     KID_TILED_NOPAD = 21,
     KID_REGBLOCK = 30,
@@ -52,6 +53,7 @@ TileShape tile_shape(int kid);
 // Launchers: enqueue one kernel on `stream`, return hipGetLastError().
 hipError_t launch_scale(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_naive(const GemmArgs &a, bool transB, hipStream_t stream);
+hipError_t launch_naive_wg(const GemmArgs &a, bool transB, hipStream_t stream);
 hipError_t launch_tiled(const GemmArgs &a, bool transB, bool pad, hipStream_t stream);
 hipError_t launch_regblock(const GemmArgs &a, bool transB, bool vec, hipStream_t stream);
 hipError_t launch_mfma(const GemmArgs &a, int kid, bool transB, bool vec, hipStream_t stream, int splits = 1);

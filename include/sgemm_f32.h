@@ -89,6 +89,12 @@ typedef enum {
  *                    section 3.2).  Vector FP32 FMA (v_fmac_f32).
  *   MFMA             CDNA matrix-core path: v_mfma_f32_32x32x2_f32, FP32 inputs and
  *                    FP32 accumulation, multi-level tiling (second page, section 7.3).
+ *   NAIVE_WG         one 64-lane wavefront per output element: lanes form partial
+ *                    dot products over k (k = lane, lane + 64, ...) and a fixed
+ *                    cross-lane butterfly adds them (Baidu Cloud article comparing
+ *                    the naive and 2-D block-tiled CUDA matmul, paragraph on the
+ *                    naive implementation: one block per output element with an
+ *                    in-block reduction).
  *   AUTO             MFMA with a tile chosen from the problem shape.
  */
 typedef enum {
@@ -97,7 +103,8 @@ typedef enum {
     SGEMM_ALGO_LDS_TILED = 2,
     SGEMM_ALGO_REGBLOCK = 3,
     SGEMM_ALGO_MFMA = 4,
-    SGEMM_ALGO_LDS_TILED_NOPAD = 5
+    SGEMM_ALGO_LDS_TILED_NOPAD = 5,
+    SGEMM_ALGO_NAIVE_WG = 6
 } sgemm_algo;
 
 /*

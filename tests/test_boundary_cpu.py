@@ -18,6 +18,7 @@ HEADER = os.path.join(ROOT, "include", "sgemm_f32.h")
 
 OK, INVALID, ALIAS = 0, 1, 2
 KID_NONE, KID_SCALE, KID_NAIVE, KID_TILED, KID_TILED_NOPAD, KID_REG = 0, 1, 10, 20, 21, 30
+KID_NAIVE_WG = 11
 KID_L, KID_M, KID_S = 40, 41, 42
 
 # Fake, well-separated "device" addresses: planning only compares ranges.
@@ -71,7 +72,7 @@ def call(algo=0, M=64, N=64, K=64, alpha=1.0, A=PA, lda=None, B=PB, ldb=None, tr
     dict(M=-1), dict(N=-1), dict(K=-1), dict(M=1 << 31), dict(K=1 << 31),
     dict(transB=2), dict(transB=-1),
     dict(lda=63), dict(ldb=63), dict(ldc=63), dict(transB=1, ldb=63),
-    dict(A=0), dict(B=0), dict(C=0), dict(algo=6), dict(algo=-1),
+    dict(A=0), dict(B=0), dict(C=0), dict(algo=7), dict(algo=-1),
     dict(M=(1 << 31) - 1024), dict(N=(1 << 31) - 1024), dict(K=(1 << 31) - 1024),
     dict(M=2, K=2, lda=1 << 61),
 ])
@@ -126,12 +127,15 @@ def test_product_free_cases_scale_c():
         assert (tm, tn) == (64, 1)
 
 
-@pytest.mark.parametrize("algo,kid", [(1, KID_NAIVE), (2, KID_TILED), (3, KID_REG), (5, KID_TILED_NOPAD)])
+@pytest.mark.parametrize("algo,kid", [(1, KID_NAIVE), (2, KID_TILED), (3, KID_REG), (5, KID_TILED_NOPAD),
+                                      (6, KID_NAIVE_WG)])
 def test_explicit_algorithms(algo, kid):
     st, k, tm, tn, name = plan(algo=algo, M=1000, N=1017, K=999)
     assert (st, k) == (OK, kid)
     if kid == KID_NAIVE:
         assert (tm, tn) == (250, 16)
+    elif kid == KID_NAIVE_WG:
+        assert (tm, tn) == (1000, 1017) and name.startswith("naive_wave_per_output")
     elif kid in (KID_TILED, KID_TILED_NOPAD):
         assert (tm, tn) == (63, 64)
     else:
@@ -187,3 +191,9 @@ def test_launch_work_item_limit():
     assert (st, kid, tm, tn) == (OK, KID_L, n // 256, n // 256)
     # largest accepted dimension
     assert plan(M=(1 << 31) - 1025, N=1, K=1, lda=1, ldb=1, ldc=1, C=1 << 50)[0] == OK
+
+
+def test_wave_per_output_has_no_grid_limit():
+    # the kernel loops over outputs: 2^17 x 2^17 outputs are still accepted
+    n = 1 << 17
+    assert plan(algo=6, M=n, N=n, K=1, lda=1, ldb=n, ldc=n, C=1 << 50)[:2] == (OK, KID_NAIVE_WG)

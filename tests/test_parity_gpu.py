@@ -151,7 +151,7 @@ def _sweep_cases(n, seed):
     return out
 
 
-@pytest.mark.parametrize("algo", ["mfma", "regblock", "lds_tiled", "naive"])
+@pytest.mark.parametrize("algo", ["mfma", "regblock", "lds_tiled", "naive", "naive_wg"])
 def test_random_ragged_sweep(oracle_lib, algo):
     """Seeded sweep of ragged shapes in [1, 700]^3, both op(B), random alpha/beta."""
     for (M, N, K, t, alpha, beta, seed) in _sweep_cases(24 if algo == "mfma" else 8, 42):
@@ -162,7 +162,7 @@ def test_random_ragged_sweep(oracle_lib, algo):
         assert_parity(Dg[:, :N], D, S, K, f"sweep {M}x{N}x{K} t{t}/{algo}")
 
 
-@pytest.mark.parametrize("algo", ["mfma", "regblock", "lds_tiled", "naive"])
+@pytest.mark.parametrize("algo", ["mfma", "regblock", "lds_tiled", "naive", "naive_wg"])
 def test_degenerate_shapes(oracle_lib, algo):
     for (M, N, K, t) in [(1, 1, 1, 0), (1, 1, 1, 1), (1, 513, 1, 0), (513, 1, 2, 1), (31, 33, 1, 0),
                          (64, 64, 8, 1), (65, 65, 9, 0), (7, 5, 4099, 1)]:
