@@ -328,45 +328,72 @@ struct RegStage {
     }
 };
 
-// Direct staging of full stages: each wavefront fills A_BLK_W + B_BLK_W 1 KB
-// LDS blocks with global_load_lds_dwordx4 (lane L writes bytes 16L..16L+15 of a
-// block).  Per-lane sources are 32-bit float offsets from the tile's first
-// element, valid because the host allows this path only when a tile's extent
-// fits (rows x leading dimension < 2^31).
-template <class Gm, bool TRANS_B>
+// Direct staging of full stages with global->LDS loads.  A wavefront
+// instruction fills one LDS block of BW floats, lane L writing float(s)
+// e = BW*block + W*L .. +W-1 of the stage's slice tile: W = 4 floats
+// (global_load_lds_dwordx4, 1 KB blocks) when the operands are 16-byte aligned,
+// W = 1 (global_load_lds_dword, 256-byte blocks) otherwise.  Each lane's
+// source follows from where its LDS float lies: in a k-contiguous tile (A, and
+// op(B) = B^T) float e is row e / BK, physical k-position e % BK, whose 4-float
+// chunk holds logical chunk (e % BK / 4) ^ swz(row); in the n-contiguous op(B) = B
+// tile it is row e / BN, column e % BN.  Sources are 32-bit float offsets from
+// the tile's first element, valid because the host allows this path only when
+// a tile's extent fits (rows x leading dimension < 2^31).
+//
+// EDGE: the tile reaches past M or N.  Rows of A (and of B^T) past the matrix
+// load its last row instead, and for op(B) = B columns past N load its last
+// column (its last whole 4-column chunk with W = 4, which the caller allows
+// only when N % 4 == 0): those values only reach outputs that the masked
+// epilogue does not store, and every address stays inside the operands.
+template <class Gm, bool TRANS_B, bool DW>
 struct DirectStage {
-    static constexpr int CPR = Gm::CPR, RPB = 256 / Gm::BK;  // k-contiguous rows per block
-    uint32_t a_off[Gm::A_BLK_W], b_off[Gm::B_BLK_W];
-    int a_lds[Gm::A_BLK_W], b_lds[Gm::B_BLK_W];   // LDS float offsets within a stage (wave-uniform)
+    static constexpr int W = DW ? 1 : 4, BW = 64 * W;
+    static constexpr int A_N = Gm::KS * Gm::A_SZ / BW / Gm::NW;   // instructions per wavefront
+    static constexpr int B_N = Gm::KS * Gm::B_SZ / BW / Gm::NW;
+    static constexpr int A_BPS = Gm::A_SZ / BW, B_BPS = Gm::B_SZ / BW;  // blocks per slice tile
+    static_assert(A_N * BW * Gm::NW == Gm::KS * Gm::A_SZ && B_N * BW * Gm::NW == Gm::KS * Gm::B_SZ,
+                  "direct staging split");
+    uint32_t a_off[A_N], b_off[B_N];
+    int a_lds[A_N], b_lds[B_N];   // LDS float offsets within a stage (wave-uniform)
     const float *a_base;
     const float *b_base;
     int64_t b_kstep;
 
+    // Source offset of LDS float e (first of W) of a k-contiguous tile row-major
+    // in memory with leading dimension ld; rows clamped to `last` on edges.
+    template <bool EDGE>
+    static __device__ __forceinline__ uint32_t kcontig(int e, int sl, int ld, int last)
+    {
+        const int r = e / Gm::BK, q = e % Gm::BK;
+        const int c = (q / 4) ^ swz<Gm::CPR>(r);
+        const int rg = EDGE ? min(r, last) : r;
+        return (uint32_t)(rg * ld + sl * Gm::BK + 4 * c + q % 4);
+    }
+
+    template <bool EDGE>
     __device__ __forceinline__ void init(const GemmArgs &a, int m0, int n0)
     {
         const int lane = threadIdx.x & 63, wave = wave_id();
 #pragma unroll
-        for (int j = 0; j < Gm::A_BLK_W; ++j) {
-            const int b = wave * Gm::A_BLK_W + j;
-            const int sl = b / Gm::A_BLK, lb = b % Gm::A_BLK;
-            const int r = lb * RPB + lane / CPR;
-            const int c = (lane % CPR) ^ swz<CPR>(r);
-            a_off[j] = (uint32_t)(r * a.lda + sl * Gm::BK + 4 * c);
-            a_lds[j] = sl * Gm::SLICE + lb * 256;
+        for (int j = 0; j < A_N; ++j) {
+            const int b = wave * A_N + j;
+            const int sl = b / A_BPS, lb = b % A_BPS;
+            a_off[j] = kcontig<EDGE>(lb * BW + W * lane, sl, (int)a.lda, a.M - 1 - m0);
+            a_lds[j] = sl * Gm::SLICE + lb * BW;
         }
 #pragma unroll
-        for (int j = 0; j < Gm::B_BLK_W; ++j) {
-            const int b = wave * Gm::B_BLK_W + j;
-            const int sl = b / Gm::B_BLK, lb = b % Gm::B_BLK;
+        for (int j = 0; j < B_N; ++j) {
+            const int b = wave * B_N + j;
+            const int sl = b / B_BPS, lb = b % B_BPS;
+            const int e = lb * BW + W * lane;
             if constexpr (TRANS_B) {
-                const int r = lb * RPB + lane / CPR;   // n within the tile
-                const int c = (lane % CPR) ^ swz<CPR>(r);
-                b_off[j] = (uint32_t)(r * a.ldb + sl * Gm::BK + 4 * c);
+                b_off[j] = kcontig<EDGE>(e, sl, (int)a.ldb, a.N - 1 - n0);
             } else {
-                const int e = lb * 256 + 4 * lane;     // float index in the [BK][BN] slice tile
-                b_off[j] = (uint32_t)((sl * Gm::BK + e / Gm::BN) * a.ldb + e % Gm::BN);
+                const int col = e % Gm::BN;
+                const int cg = EDGE ? min(col, a.N - W - n0) : col;
+                b_off[j] = (uint32_t)((sl * Gm::BK + e / Gm::BN) * (int)a.ldb + cg);
             }
-            b_lds[j] = sl * Gm::SLICE + Gm::A_SZ + lb * 256;
+            b_lds[j] = sl * Gm::SLICE + Gm::A_SZ + lb * BW;
         }
         a_base = a.A + (int64_t)m0 * a.lda;
         b_base = TRANS_B ? a.B + (int64_t)n0 * a.ldb : a.B + n0;
@@ -378,11 +405,11 @@ struct DirectStage {
         const float *ak = a_base + (int64_t)kt * Gm::KT;
         const float *bk = b_base + (int64_t)kt * b_kstep;
 #pragma unroll
-        for (int j = 0; j < Gm::A_BLK_W; ++j)
-            __builtin_amdgcn_global_load_lds(ak + a_off[j], (lds_void *)(stage + a_lds[j]), 16, 0, 0);
+        for (int j = 0; j < A_N; ++j)
+            __builtin_amdgcn_global_load_lds(ak + a_off[j], (lds_void *)(stage + a_lds[j]), 4 * W, 0, 0);
 #pragma unroll
-        for (int j = 0; j < Gm::B_BLK_W; ++j)
-            __builtin_amdgcn_global_load_lds(bk + b_off[j], (lds_void *)(stage + b_lds[j]), 16, 0, 0);
+        for (int j = 0; j < B_N; ++j)
+            __builtin_amdgcn_global_load_lds(bk + b_off[j], (lds_void *)(stage + b_lds[j]), 4 * W, 0, 0);
     }
 };
 
@@ -573,7 +600,7 @@ __device__ __forceinline__ void gemm_tile_regs(const GemmArgs &a, float *smem, i
 }
 
 // Direct-staged k-loop for interior tiles with 16-byte aligned operands.
-template <class Gm, bool TRANS_B>
+template <class Gm, bool TRANS_B, bool EDGE, bool DW>
 __device__ __forceinline__ void gemm_tile_direct(const GemmArgs &a, float *smem, int m0, int n0)
 {
     constexpr int G = Gm::G;
@@ -587,15 +614,15 @@ __device__ __forceinline__ void gemm_tile_direct(const GemmArgs &a, float *smem,
     const int nf = a.K / Gm::KT;  // full stages
     Frags<Gm, TRANS_B> f[2];
 
-    DirectStage<Gm, TRANS_B> ds;
-    ds.init(a, m0, n0);
+    DirectStage<Gm, TRANS_B, DW> ds;
+    ds.template init<EDGE>(a, m0, n0);
     if (nf > 0)
         ds.issue(0, buf0);
 
     // Partial last stage first (the order of the k sum is free): registers with
     // zero fill, through buffer 1, while stage 0 lands in buffer 0.
     if (nf * Gm::KT < a.K) {
-        RegStage<Gm, TRANS_B, true> st;
+        RegStage<Gm, TRANS_B, !DW> st;
         st.init(a, m0, n0);
         st.template load<true>(a, m0, n0, nf);
         st.store(buf1);
@@ -634,7 +661,7 @@ __device__ __forceinline__ void gemm_tile_direct(const GemmArgs &a, float *smem,
         }
     }
     if (reduce_slices<Gm>(acc, smem, ro))
-        epilogue<Gm, TRANS_B, true>(a, acc, m0, n0, ro);
+        epilogue<Gm, TRANS_B, !EDGE>(a, acc, m0, n0, ro);
 }
 
 // GD: geometry of the direct path; GR: geometry of the register path (same
@@ -662,10 +689,21 @@ void sgemm_mfma_kernel(GemmArgs a)
     map_tile(blockIdx.x, nbm, nbn, tile_m, tile_n);
     const int m0 = tile_m * GD::BM, n0 = tile_n * GD::BN;
     const bool full = m0 + GD::BM <= a.M && n0 + GD::BN <= a.N;
-    if constexpr (VEC) {
-        if (full && (a.flags & GEMM_FLAG_DIRECT)) {
-            gemm_tile_direct<GD, TRANS_B>(a, smem, m0, n0);
-            return;
+    // 16-byte direct loads for aligned operands, 4-byte ones otherwise (not on
+    // the 256 x 256 tile: its 32 per-lane source offsets would not fit beside
+    // the accumulators).  Edge tiles stage directly too whenever every clamped
+    // address is exact (with 16-byte loads op(B) = B needs whole 4-column chunks).
+    constexpr bool direct_ok = VEC || GD::BM * GD::BN <= 128 * 128;
+    if constexpr (direct_ok) {
+        if (a.flags & GEMM_FLAG_DIRECT) {
+            if (full) {
+                gemm_tile_direct<GD, TRANS_B, false, !VEC>(a, smem, m0, n0);
+                return;
+            }
+            if (!VEC || TRANS_B || (a.N & 3) == 0) {
+                gemm_tile_direct<GD, TRANS_B, true, !VEC>(a, smem, m0, n0);
+                return;
+            }
         }
     }
     if (full)

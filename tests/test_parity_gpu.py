@@ -206,6 +206,72 @@ def test_mid_tile_integers_bit_exact(oracle_lib):
     assert np.array_equal(Dg[rows, :2100], D.astype(np.float32))
 
 
+# (M, N, K, transB, expected kernel): aligned operands whose tiles reach past M
+# and/or N, for each MFMA tile.  Edge tiles stage directly with clamped rows
+# (op(B) = B^T, or op(B) = B with N % 4 == 0) or through masked registers
+# (op(B) = B with N % 4 != 0); K tails on some.
+EDGE_SHAPES = [(1000, 1000, 1024, 0, 42), (1000, 1000, 1024, 1, 42), (1000, 1004, 999, 0, 42),
+               (1003, 1001, 1000, 1, 42), (1001, 1003, 1000, 0, 42), (2000, 2052, 1000, 0, 41),
+               (2001, 1999, 777, 1, 41), (3999, 4000, 512, 0, 40), (4000, 3998, 520, 1, 40),
+               (4001, 4003, 300, 0, 40)]
+
+
+@pytest.mark.parametrize("shape", EDGE_SHAPES, ids=lambda s: "x".join(str(v) for v in s[:4]))
+def test_edge_tiles_aligned(oracle_lib, shape):
+    M, N, K, t, want = shape
+    r4 = lambda v: (v + 3) // 4 * 4  # noqa: E731  (leading dimensions padded to 16 bytes)
+    case = make_case(M, N, K, trans_b=t, alpha=0.75, beta=-1.25, dist="uniform", seed=M * 3 + N,
+                     lda=r4(K), ldb=r4(K) if t else r4(N))
+    st, kid, tm, tn, name = lib.sgemm_f32_plan(0, M, N, K, 1.0, 1 << 32, case.lda, 1 << 40, case.ldb, t,
+                                              0.5, 1 << 44, N)
+    assert kid == want and "vec=1" in name, name
+    st, Dg = run_case(case, "auto", ldc_pad=4)
+    assert st == 0
+    rows = np.unique(np.concatenate([sample_rows(M, n=20, seed=K, tile=64), np.arange(M - 70, M)]))
+    D, S = oracle_rows(oracle_lib, case, rows)
+    assert_parity(Dg[rows, :N], D, S, K, f"edge {M}x{N}x{K} t{t}")
+
+
+# Unaligned operands (leading dimension not a multiple of 4, or a base address
+# off by one float): the 64x64 and 128x128 tiles stage them with 4-byte direct
+# loads (edges clamped per element), the 256x256 tile through masked registers.
+UNALIGNED_SHAPES = [(1000, 1017, 999, 1, 0, 42), (1001, 1003, 1000, 0, 0, 42), (1000, 1000, 1024, 0, 1, 42),
+                    (2001, 1999, 777, 1, 0, 41), (2048, 2050, 1001, 0, 1, 41), (3999, 4001, 501, 0, 0, 40)]
+
+
+@pytest.mark.parametrize("shape", UNALIGNED_SHAPES, ids=lambda s: "x".join(str(v) for v in s[:5]))
+def test_unaligned_operands(oracle_lib, shape):
+    M, N, K, t, a_off, want = shape
+    case = make_case(M, N, K, trans_b=t, alpha=1.5, beta=0.25, dist="uniform", seed=M + 7 * N)
+    st, kid, tm, tn, name = lib.sgemm_f32_plan(0, M, N, K, 1.0, (1 << 32) + 4 * a_off, case.lda, 1 << 40, case.ldb,
+                                              t, 0.5, 1 << 44, N)
+    assert kid == want and "vec=0" in name, name
+    st, Dg = run_case(case, "auto", a_offset=a_off, ldc_pad=1)
+    assert st == 0
+    rows = np.unique(np.concatenate([sample_rows(M, n=20, seed=K, tile=64), np.arange(M - 70, M)]))
+    D, S = oracle_rows(oracle_lib, case, rows)
+    assert_parity(Dg[rows, :N], D, S, K, f"unaligned {M}x{N}x{K} t{t} a_off={a_off}")
+
+
+@pytest.mark.parametrize("t", [0, 1])
+def test_unaligned_integers_bit_exact(oracle_lib, t):
+    case = make_case(1003, 1001, 999, trans_b=t, alpha=1.0, beta=1.0, dist="int2", seed=23)
+    st, Dg = run_case(case, "auto", a_offset=1)
+    assert st == 0
+    D, _ = oracle_rows(oracle_lib, case)
+    assert np.array_equal(Dg[:, :1001], D.astype(np.float32))
+
+
+@pytest.mark.parametrize("t", [0, 1])
+def test_edge_tiles_integers_bit_exact(oracle_lib, t):
+    case = make_case(1003, 1004, 1000, trans_b=t, alpha=1.0, beta=1.0, dist="int2", seed=19)
+    assert case.lda % 4 == 0 and case.ldb % 4 == 0
+    st, Dg = run_case(case, "auto")
+    assert st == 0
+    D, _ = oracle_rows(oracle_lib, case)
+    assert np.array_equal(Dg[:, :1004], D.astype(np.float32))
+
+
 def test_product_free_paths(oracle_lib):
     """alpha == 0 or K == 0: C <- beta*C; beta == 1 leaves C untouched bitwise;
     beta == 0 zeroes C without reading it (NaN in C)."""
