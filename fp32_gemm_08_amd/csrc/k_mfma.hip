@@ -63,6 +63,12 @@ template <> __device__ __forceinline__ float vget<1>(const float &v, int) { retu
 template <> __device__ __forceinline__ float vget<2>(const f32x2 &v, int i) { return v[i]; }
 template <> __device__ __forceinline__ float vget<4>(const f32x4 &v, int i) { return v[i]; }
 
+template <int W>
+__device__ __forceinline__ void vset(typename vec_of<W>::type &v, int i, float x);
+template <> __device__ __forceinline__ void vset<1>(float &v, int, float x) { v = x; }
+template <> __device__ __forceinline__ void vset<2>(f32x2 &v, int i, float x) { v[i] = x; }
+template <> __device__ __forceinline__ void vset<4>(f32x4 &v, int i, float x) { v[i] = x; }
+
 // Wavefront index within the workgroup, as a wave-uniform (scalar) value: the
 // LDS block addresses derived from it then stay in scalar registers, and M0 for
 // the direct loads is set without a per-load vector-to-scalar move (measured ~1%).
@@ -451,72 +457,93 @@ __device__ __forceinline__ bool reduce_slices(f32x16 (&acc)[Gm::FM][Gm::FN], flo
     }
 }
 
-template <class Gm, bool TRANS_B, bool FULL>
-__device__ __forceinline__ void epilogue(const GemmArgs &a, const f32x16 (&acc)[Gm::FM][Gm::FN], int m0, int n0,
-                                         const Role<Gm> &ro)
+template <class Gm, bool TRANS_B, bool FULL, bool RD>
+__device__ __forceinline__ void epilogue_rows(const GemmArgs &a, const f32x16 (&acc)[Gm::FM][Gm::FN], int m0, int n0,
+                                              const Role<Gm> &ro)
 {
     // Accumulator register r of a 32x32 block holds row 8*(r/4) + 4*hi + (r%4)
-    // and column l32 of that block.
+    // and column l32 of that block.  Rows go 8 at a time; with beta != 0 the
+    // old C values of all 8 are loaded before the first of them is stored:
+    // loads and stores share the pointer C, so a load written after a store
+    // cannot be hoisted above it and would wait out a whole memory round trip.
+    // beta == 0 reads nothing and takes its own copy of the loop.
     typedef typename vec_of<Gm::IL>::type bvec;
     constexpr int IL = Gm::IL;
     const int l32 = ro.l32, hi = ro.hi, wm = ro.wm, wn = ro.wn;
     const uintptr_t cbase = reinterpret_cast<uintptr_t>(a.C);
     const bool cvec = IL > 1 && (cbase % (4 * IL)) == 0 && (a.ldc % IL) == 0;
+    constexpr bool rd = RD;
 #pragma unroll
     for (int fm = 0; fm < Gm::FM; ++fm) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = m0 + wm * Gm::WM + 32 * fm + 8 * (r / 4) + 4 * hi + (r % 4);
-            if (!FULL && row >= a.M)
-                continue;
-            float *crow = a.C + (int64_t)row * a.ldc;
-            if constexpr (TRANS_B) {
+        for (int h = 0; h < 2; ++h) {
+            float old[8][Gm::FN];
+            if constexpr (rd) {
 #pragma unroll
-                for (int fn = 0; fn < Gm::FN; ++fn) {
-                    const int col = n0 + wn * Gm::WN + 32 * fn + l32;
-                    if (FULL || col < a.N) {
-                        const float v = acc[fm][fn][r];
-                        crow[col] = (a.beta == 0.0f) ? a.alpha * v : fmaf(a.alpha, v, a.beta * crow[col]);
-                    }
-                }
-            } else {
+                for (int i = 0; i < 8; ++i) {
+                    const int r = 8 * h + i;
+                    const int row = m0 + wm * Gm::WM + 32 * fm + 8 * (r / 4) + 4 * hi + (r % 4);
+                    if (!FULL && row >= a.M)
+                        continue;
+                    const float *crow = a.C + (int64_t)row * a.ldc;
 #pragma unroll
-                for (int gr = 0; gr < Gm::NG; ++gr) {
-                    const int col = n0 + wn * Gm::WN + gr * 32 * IL + IL * l32;
-                    if (cvec && (FULL || col + IL <= a.N)) {
-                        bvec v;
-                        if constexpr (IL == 1) {
-                            v = a.alpha * acc[fm][gr][r];
+                    for (int gr = 0; gr < Gm::NG; ++gr) {
+                        const int col = n0 + wn * Gm::WN + gr * 32 * IL + IL * l32;
+                        if (IL > 1 && cvec && (FULL || col + IL <= a.N)) {
+                            const bvec o = *reinterpret_cast<const bvec *>(crow + col);
+#pragma unroll
+                            for (int b = 0; b < IL; ++b)
+                                old[i][gr * IL + b] = vget<IL>(o, b);
                         } else {
 #pragma unroll
                             for (int b = 0; b < IL; ++b)
-                                v[b] = a.alpha * acc[fm][gr * IL + b][r];
+                                old[i][gr * IL + b] = (FULL || col + b < a.N) ? crow[col + b] : 0.0f;
                         }
-                        if (a.beta != 0.0f) {
-                            const bvec old = *reinterpret_cast<const bvec *>(crow + col);
-                            if constexpr (IL == 1) {
-                                v = fmaf(a.alpha, acc[fm][gr][r], a.beta * old);
-                            } else {
+                    }
+                }
+            }
 #pragma unroll
-                                for (int b = 0; b < IL; ++b)
-                                    v[b] = fmaf(a.alpha, acc[fm][gr * IL + b][r], a.beta * old[b]);
-                            }
-                        }
-                        *reinterpret_cast<bvec *>(crow + col) = v;
+            for (int i = 0; i < 8; ++i) {
+                const int r = 8 * h + i;
+                const int row = m0 + wm * Gm::WM + 32 * fm + 8 * (r / 4) + 4 * hi + (r % 4);
+                if (!FULL && row >= a.M)
+                    continue;
+                float *crow = a.C + (int64_t)row * a.ldc;
+#pragma unroll
+                for (int gr = 0; gr < Gm::NG; ++gr) {
+                    const int col = n0 + wn * Gm::WN + gr * 32 * IL + IL * l32;
+                    float v[IL];
+#pragma unroll
+                    for (int b = 0; b < IL; ++b) {
+                        const float x = acc[fm][gr * IL + b][r];
+                        v[b] = rd ? fmaf(a.alpha, x, a.beta * old[i][gr * IL + b]) : a.alpha * x;
+                    }
+                    if (IL > 1 && cvec && (FULL || col + IL <= a.N)) {
+                        bvec o;
+#pragma unroll
+                        for (int b = 0; b < IL; ++b)
+                            vset<IL>(o, b, v[b]);
+                        *reinterpret_cast<bvec *>(crow + col) = o;
                     } else {
 #pragma unroll
-                        for (int b = 0; b < IL; ++b) {
-                            if (col + b < a.N) {
-                                const float v = acc[fm][gr * IL + b][r];
-                                float *cp = crow + col + b;
-                                *cp = (a.beta == 0.0f) ? a.alpha * v : fmaf(a.alpha, v, a.beta * *cp);
-                            }
-                        }
+                        for (int b = 0; b < IL; ++b)
+                            if (FULL || col + b < a.N)
+                                crow[col + b] = v[b];
                     }
                 }
             }
         }
     }
+}
+
+template <class Gm, bool TRANS_B, bool FULL>
+__device__ __forceinline__ void epilogue(const GemmArgs &a, const f32x16 (&acc)[Gm::FM][Gm::FN], int m0, int n0,
+                                         const Role<Gm> &ro)
+{
+    if (a.beta != 0.0f)
+        epilogue_rows<Gm, TRANS_B, FULL, true>(a, acc, m0, n0, ro);
+    else
+        epilogue_rows<Gm, TRANS_B, FULL, false>(a, acc, m0, n0, ro);
 }
 
 // One k-group of one stage: the first MFMA step runs on fragments read a whole

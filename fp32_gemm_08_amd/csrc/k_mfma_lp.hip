@@ -14,21 +14,22 @@
 // row 8*(r/4) + 4*(l/32) + r%4, column l%32 of the block.
 //
 // Workgroup tile 256 x 256, 8 wavefronts as 4 (m) x 2 (n), each 64 x 128 =
-// 2 x 4 blocks of 32 x 32 (128 FP32 accumulators per lane).  k-tiles of 32.
-// LDS holds both operands k-contiguous as 16-bit values, A as As[256][40] and
-// op(B) as Bs[256][40] (n-major): 32 values per row plus 8 of padding, an
+// 2 x 4 blocks of 32 x 32 (128 FP32 accumulators per lane), or for products
+// with fewer than 256 such tiles 64 x 64 with 2 wavefronts of 32 x 64.  k-tiles
+// of 32.  LDS holds both operands k-contiguous as 16-bit values, A as
+// As[BM][40] and op(B) as Bs[BN][40] (n-major): 32 values per row plus 8 of padding, an
 // 80-byte pitch, so the 16-byte operand reads of 16 consecutive rows fall on
 // 16 distinct 4-bank groups (bank unit 20*r mod 64).  Two stages, one barrier
 // per k-tile; the next k-tile's FP32 loads are in flight while the current one
 // is multiplied, then converted and written to the other stage.
 //
-// Staging per k-tile (512 work-items):
-//   A (and op(B) = B^T, stored N x K): 256 rows x 4 chunks of 8 k values; each
-//     work-item loads two chunks as 2 x 128 bits each, converts, and writes
+// Staging per k-tile:
+//   A (and op(B) = B^T, stored N x K): BM rows x 4 chunks of 8 k values; each
+//     work-item loads its chunks as 2 x 128 bits each, converts, and writes
 //     16 bytes per chunk.
-//   op(B) = B (stored K x N): 8 quads of k x 64 quads of n; each work-item
-//     loads a 4 (k) x 4 (n) block (4 x 128 bits along n), converts, and writes
-//     it transposed: 4 n-rows x 4 k values (8 bytes each).
+//   op(B) = B (stored K x N): 8 quads of k x BN/4 quads of n; each work-item
+//     loads 4 (k) x 4 (n) blocks (4 x 128 bits along n), converts, and writes
+//     them transposed: 4 n-rows x 4 k values (8 bytes each).
 // Edge tiles and the k tail load with masks and zero fill; misaligned operands
 // (base not 16-byte aligned or leading dimension not a multiple of 4) load
 // element by element.
@@ -64,11 +65,23 @@ template <> struct Lp<true> {
     }
 };
 
-constexpr int LBM = 256, LBN = 256, LBK = 32, LNT = 512;
-constexpr int LWM = 64, LWN = 128, LFM = LWM / 32, LFN = LWN / 32;
+constexpr int LBK = 32;
 constexpr int LP_PITCH = LBK + 8;                      // 16-bit values per LDS row
-constexpr int LP_STAGE = (LBM + LBN) * LP_PITCH;       // 16-bit values per stage
-static_assert(2 * LP_STAGE * 2 <= 160 * 1024, "two stages fit the LDS");
+
+// Workgroup tile BM x BN, WGM x WGN wavefronts each owning (BM/WGM) x (BN/WGN).
+template <int BM_, int BN_, int WGM_, int WGN_>
+struct LpGeo {
+    static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
+    static constexpr int NT = 64 * WGM * WGN;
+    static constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
+    static constexpr int STAGE = (BM + BN) * LP_PITCH;  // 16-bit values per stage
+    static constexpr int UA = 4 * BM / NT;               // A units (8 k values) per work-item
+    static constexpr int UBT = 4 * BN / NT;              // B^T units per work-item
+    static constexpr int UB = 2 * BN / NT;               // B units (4 k x 4 n) per work-item
+    static_assert(WM % 32 == 0 && WN % 32 == 0, "whole 32 x 32 blocks");
+    static_assert(UA * NT == 4 * BM && UBT * NT == 4 * BN && UB * NT == 2 * BN && UB >= 1, "staging split");
+    static_assert(2 * STAGE * 2 <= 160 * 1024, "two stages fit the LDS");
+};
 
 __device__ __forceinline__ int lp_wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
@@ -88,15 +101,15 @@ __device__ __forceinline__ void lp_map_tile(int bid, int nbm, int nbn, int &tm, 
     tn = (id % group) / gm;
 }
 
-template <bool BF16, bool TRANS_B, bool VEC>
+template <class Gm, bool BF16, bool TRANS_B, bool VEC>
 struct LpStage {
     typedef typename Lp<BF16>::T T;
     typedef typename Lp<BF16>::V8 V8;
     typedef typename Lp<BF16>::V4 V4;
-    // A units (and B^T units): 2 per work-item, 8 k values each
-    float a[2][8];
-    // B units: TRANS_B ? 2 units of 8 k values : one 4 (k) x 4 (n) block
-    float b[TRANS_B ? 2 : 4][TRANS_B ? 8 : 4];
+    // A units (and B^T units): 8 k values each
+    float a[Gm::UA][8];
+    // B units: TRANS_B ? units of 8 k values : 4 (k) x 4 (n) blocks
+    float b[TRANS_B ? Gm::UBT : Gm::UB][TRANS_B ? 8 : 16];
 
     // Load 8 consecutive floats of a k-contiguous row (zero past the matrix).
     template <bool MASKED>
@@ -122,34 +135,38 @@ struct LpStage {
     {
         const int t = threadIdx.x;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int u = t + LNT * i, r = u >> 2, c = u & 3;
+        for (int i = 0; i < Gm::UA; ++i) {
+            const int u = t + Gm::NT * i, r = u >> 2, c = u & 3;
             const int k = k0 + 8 * c;
             load8<MASKED>(a[i], g.A + (int64_t)(m0 + r) * g.lda + k, m0 + r < g.M, k, g.K);
         }
         if constexpr (TRANS_B) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int u = t + LNT * i, r = u >> 2, c = u & 3;
+            for (int i = 0; i < Gm::UBT; ++i) {
+                const int u = t + Gm::NT * i, r = u >> 2, c = u & 3;
                 const int k = k0 + 8 * c;
                 load8<MASKED>(b[i], g.B + (int64_t)(n0 + r) * g.ldb + k, n0 + r < g.N, k, g.K);
             }
         } else {
-            const int kq = (t >> 3) & 7, nq = (t & 7) | ((t >> 6) << 3);
-            const int n = n0 + 4 * nq;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int k = k0 + 4 * kq + i;
-                const float *p = g.B + (int64_t)k * g.ldb + n;
-                if (!MASKED && VEC) {
-                    const lp_f32x4 x = *reinterpret_cast<const lp_f32x4 *>(p);
+            for (int i = 0; i < Gm::UB; ++i) {
+                const int u = t + Gm::NT * i;
+                const int kq = (u >> 3) & 7, nq = (u & 7) | ((u >> 6) << 3);
+                const int n = n0 + 4 * nq;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        b[i][q] = x[q];
-                } else {
+                for (int j = 0; j < 4; ++j) {
+                    const int k = k0 + 4 * kq + j;
+                    const float *p = g.B + (int64_t)k * g.ldb + n;
+                    if (!MASKED && VEC) {
+                        const lp_f32x4 x = *reinterpret_cast<const lp_f32x4 *>(p);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        b[i][q] = (!MASKED || (k < g.K && n + q < g.N)) ? p[q] : 0.0f;
+                        for (int q = 0; q < 4; ++q)
+                            b[i][4 * j + q] = x[q];
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            b[i][4 * j + q] = (!MASKED || (k < g.K && n + q < g.N)) ? p[q] : 0.0f;
+                    }
                 }
             }
         }
@@ -168,35 +185,41 @@ struct LpStage {
     {
         const int t = threadIdx.x;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int u = t + LNT * i, r = u >> 2, c = u & 3;
+        for (int i = 0; i < Gm::UA; ++i) {
+            const int u = t + Gm::NT * i, r = u >> 2, c = u & 3;
             *reinterpret_cast<V8 *>(as + r * LP_PITCH + 8 * c) = cvt8(a[i]);
         }
         if constexpr (TRANS_B) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int u = t + LNT * i, r = u >> 2, c = u & 3;
+            for (int i = 0; i < Gm::UBT; ++i) {
+                const int u = t + Gm::NT * i, r = u >> 2, c = u & 3;
                 *reinterpret_cast<V8 *>(bs + r * LP_PITCH + 8 * c) = cvt8(b[i]);
             }
         } else {
-            const int kq = (t >> 3) & 7, nq = (t & 7) | ((t >> 6) << 3);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                V4 v;
+            for (int i = 0; i < Gm::UB; ++i) {
+                const int u = t + Gm::NT * i;
+                const int kq = (u >> 3) & 7, nq = (u & 7) | ((u >> 6) << 3);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    v[i] = (T)b[i][j];
-                *reinterpret_cast<V4 *>(bs + (4 * nq + j) * LP_PITCH + 4 * kq) = v;
+                for (int j = 0; j < 4; ++j) {
+                    V4 v;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        v[q] = (T)b[i][4 * q + j];
+                    *reinterpret_cast<V4 *>(bs + (4 * nq + j) * LP_PITCH + 4 * kq) = v;
+                }
             }
         }
     }
 };
 
-template <bool BF16, bool TRANS_B, bool VEC>
-__global__ __launch_bounds__(LNT) void sgemm_mfma_lp_kernel(GemmArgs g)
+template <class Gm, bool BF16, bool TRANS_B, bool VEC>
+__global__ __launch_bounds__(Gm::NT) void sgemm_mfma_lp_kernel(GemmArgs g)
 {
     typedef typename Lp<BF16>::T T;
     typedef typename Lp<BF16>::V8 V8;
+    constexpr int LBM = Gm::BM, LBN = Gm::BN, LWM = Gm::WM, LWN = Gm::WN, LFM = Gm::FM, LFN = Gm::FN;
+    constexpr int LP_STAGE = Gm::STAGE;
     __shared__ __attribute__((aligned(16))) T smem[2 * LP_STAGE];
 
     const int nbm = (g.M + LBM - 1) / LBM, nbn = (g.N + LBN - 1) / LBN;
@@ -207,7 +230,7 @@ __global__ __launch_bounds__(LNT) void sgemm_mfma_lp_kernel(GemmArgs g)
     const int nk = (g.K + LBK - 1) / LBK;
 
     const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
-    const int w = lp_wave_id(), wm = w >> 1, wn = w & 1;
+    const int w = lp_wave_id(), wm = w / Gm::WGN, wn = w % Gm::WGN;
 
     lp_f32x16 acc[LFM][LFN];
 #pragma unroll
@@ -216,7 +239,7 @@ __global__ __launch_bounds__(LNT) void sgemm_mfma_lp_kernel(GemmArgs g)
         for (int fn = 0; fn < LFN; ++fn)
             acc[fm][fn] = lp_f32x16{};
 
-    LpStage<BF16, TRANS_B, VEC> st;
+    LpStage<Gm, BF16, TRANS_B, VEC> st;
     auto load_tile = [&](int kt) {
         const int k0 = kt * LBK;
         if (full && k0 + LBK <= g.K)
@@ -255,21 +278,59 @@ __global__ __launch_bounds__(LNT) void sgemm_mfma_lp_kernel(GemmArgs g)
         __syncthreads();
     }
 
-    // Epilogue: D = alpha * acc + beta * C (C not read when beta == 0).
+    // Epilogue: D = alpha * acc + beta * C (C not read when beta == 0).  With
+    // beta != 0 rows go 8 at a time and all 8 rows' old values are loaded
+    // before the first store: loads and stores share the pointer C, so a load
+    // after a store could not be hoisted and would wait a full round trip.
+    if (g.beta == 0.0f) {
+#pragma unroll
+        for (int fm = 0; fm < LFM; ++fm) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm * LWM + fm * 32 + 8 * (r / 4) + 4 * hi + (r % 4);
+                if (!full && row >= g.M)
+                    continue;
+                float *crow = g.C + (int64_t)row * g.ldc;
+#pragma unroll
+                for (int fn = 0; fn < LFN; ++fn) {
+                    const int col = n0 + wn * LWN + fn * 32 + l32;
+                    if (full || col < g.N)
+                        crow[col] = g.alpha * acc[fm][fn][r];
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int fm = 0; fm < LFM; ++fm) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = m0 + wm * LWM + fm * 32 + 8 * (r / 4) + 4 * hi + (r % 4);
-            if (!full && row >= g.M)
-                continue;
-            float *crow = g.C + (int64_t)row * g.ldc;
+        for (int h = 0; h < 2; ++h) {
+            float old[8][LFN];
 #pragma unroll
-            for (int fn = 0; fn < LFN; ++fn) {
-                const int col = n0 + wn * LWN + fn * 32 + l32;
-                if (full || col < g.N) {
-                    const float v = acc[fm][fn][r];
-                    crow[col] = (g.beta == 0.0f) ? g.alpha * v : fmaf(g.alpha, v, g.beta * crow[col]);
+            for (int i = 0; i < 8; ++i) {
+                const int r = 8 * h + i;
+                const int row = m0 + wm * LWM + fm * 32 + 8 * (r / 4) + 4 * hi + (r % 4);
+                if (!full && row >= g.M)
+                    continue;
+                const float *crow = g.C + (int64_t)row * g.ldc;
+#pragma unroll
+                for (int fn = 0; fn < LFN; ++fn) {
+                    const int col = n0 + wn * LWN + fn * 32 + l32;
+                    old[i][fn] = (full || col < g.N) ? crow[col] : 0.0f;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int r = 8 * h + i;
+                const int row = m0 + wm * LWM + fm * 32 + 8 * (r / 4) + 4 * hi + (r % 4);
+                if (!full && row >= g.M)
+                    continue;
+                float *crow = g.C + (int64_t)row * g.ldc;
+#pragma unroll
+                for (int fn = 0; fn < LFN; ++fn) {
+                    const int col = n0 + wn * LWN + fn * 32 + l32;
+                    if (full || col < g.N)
+                        crow[col] = fmaf(g.alpha, acc[fm][fn][r], g.beta * old[i][fn]);
                 }
             }
         }
@@ -278,13 +339,21 @@ __global__ __launch_bounds__(LNT) void sgemm_mfma_lp_kernel(GemmArgs g)
 
 }  // namespace
 
-TileShape lp_tile_shape() { return {LBM, LBN}; }
+// Measured on MI355X (bf16, 4096^3 ... 1024^3): the 256 x 256 tile is fastest
+// once it gives every CU a workgroup; below that the 64 x 64 tile (2 wavefronts,
+// up to 8 workgroups per CU) is, by 2x at 2048^3 and 3x at 1024^3.  128 x 256
+// and 128 x 128 tiles never led by more than 15%.
+typedef LpGeo<256, 256, 4, 2> LpL;   // 8 wavefronts of 64 x 128
+typedef LpGeo<64, 64, 2, 1> LpS;     // 2 wavefronts of 32 x 64
 
-hipError_t launch_mfma_lp(const GemmArgs &a, bool bf16, bool transB, bool vec, hipStream_t stream)
+TileShape lp_tile_shape(bool large) { return large ? TileShape{LpL::BM, LpL::BN} : TileShape{LpS::BM, LpS::BN}; }
+
+template <class Gm>
+static void launch_lp_cfg(const GemmArgs &a, bool bf16, bool transB, bool vec, hipStream_t stream)
 {
-    const int64_t blocks = ceil_div(a.M, LBM) * ceil_div(a.N, LBN);
-    const dim3 grid((unsigned)blocks), block(LNT);
-#define LP_LAUNCH(BF, TB, V) sgemm_mfma_lp_kernel<BF, TB, V><<<grid, block, 0, stream>>>(a)
+    const int64_t blocks = ceil_div(a.M, Gm::BM) * ceil_div(a.N, Gm::BN);
+    const dim3 grid((unsigned)blocks), block(Gm::NT);
+#define LP_LAUNCH(BF, TB, V) sgemm_mfma_lp_kernel<Gm, BF, TB, V><<<grid, block, 0, stream>>>(a)
     if (bf16) {
         if (transB) { if (vec) LP_LAUNCH(true, true, true); else LP_LAUNCH(true, true, false); }
         else { if (vec) LP_LAUNCH(true, false, true); else LP_LAUNCH(true, false, false); }
@@ -293,6 +362,14 @@ hipError_t launch_mfma_lp(const GemmArgs &a, bool bf16, bool transB, bool vec, h
         else { if (vec) LP_LAUNCH(false, false, true); else LP_LAUNCH(false, false, false); }
     }
 #undef LP_LAUNCH
+}
+
+hipError_t launch_mfma_lp(const GemmArgs &a, bool large, bool bf16, bool transB, bool vec, hipStream_t stream)
+{
+    if (large)
+        launch_lp_cfg<LpL>(a, bf16, transB, vec, stream);
+    else
+        launch_lp_cfg<LpS>(a, bf16, transB, vec, stream);
     return hipGetLastError();
 }
 

@@ -230,6 +230,8 @@ const char *kernel_label(int kid)
     case KID_MFMA_S: return "mfma_64x64x32_w2x2";
     case KID_MFMA_LP_F16: return "mfma_lp_f16_256x256x32_w4x2";
     case KID_MFMA_LP_BF16: return "mfma_lp_bf16_256x256x32_w4x2";
+    case KID_MFMA_LP_F16_S: return "mfma_lp_f16_64x64x32_w2x1";
+    case KID_MFMA_LP_BF16_S: return "mfma_lp_bf16_64x64x32_w2x1";
     case KID_TRANSPOSE_NAIVE: return "transpose_naive_64x16";
     case KID_TRANSPOSE_LDS_PAD: return "transpose_lds_128x128_pad1";
     case KID_TRANSPOSE_LDS_NOPAD: return "transpose_lds_128x128_pad0";
@@ -416,11 +418,15 @@ Plan make_lowp_plan(int precision, int64_t M, int64_t N, int64_t K, float alpha,
     Plan p = make_plan(SGEMM_ALGO_AUTO, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc);
     if (p.status != SGEMM_OK || !(p.kid == KID_MFMA_L || p.kid == KID_MFMA_M || p.kid == KID_MFMA_S))
         return p;
-    p.kid = precision == SGEMM_PREC_BF16 ? KID_MFMA_LP_BF16 : KID_MFMA_LP_F16;
-    const TileShape t = lp_tile_shape();
+    // the 256 x 256 tile once it gives every CU a workgroup, else 64 x 64
+    const TileShape tl = lp_tile_shape(true);
+    const bool large = ceil_div(M, tl.bm) * ceil_div(N, tl.bn) >= 256;
+    const bool bf16 = precision == SGEMM_PREC_BF16;
+    p.kid = large ? (bf16 ? KID_MFMA_LP_BF16 : KID_MFMA_LP_F16) : (bf16 ? KID_MFMA_LP_BF16_S : KID_MFMA_LP_F16_S);
+    const TileShape t = lp_tile_shape(large);
     p.tiles_m = ceil_div(M, t.bm);
     p.tiles_n = ceil_div(N, t.bn);
-    if (p.tiles_m * p.tiles_n * 512 > kMaxWorkItems) {
+    if (p.tiles_m * p.tiles_n * (large ? 512 : 128) > kMaxWorkItems) {
         p.status = SGEMM_ERR_INVALID_VALUE;
         p.kid = KID_NONE;
     }
@@ -454,8 +460,9 @@ int run_lowp(int precision, int64_t M, int64_t N, int64_t K, float alpha, const 
     a.k_split = 0;
     a.c_split_stride = 0;
     (void)hipGetLastError();
-    const hipError_t e = launch_mfma_lp(a, p.kid == KID_MFMA_LP_BF16, p.transB, p.vec,
-                                        reinterpret_cast<hipStream_t>(stream));
+    const bool large = p.kid == KID_MFMA_LP_F16 || p.kid == KID_MFMA_LP_BF16;
+    const bool bf16 = p.kid == KID_MFMA_LP_BF16 || p.kid == KID_MFMA_LP_BF16_S;
+    const hipError_t e = launch_mfma_lp(a, large, bf16, p.transB, p.vec, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
 }
 

@@ -42,6 +42,8 @@ enum KernelId : int {
     KID_MFMA_S = 42,        // 64 x 64, 4 wavefronts
     KID_MFMA_LP_F16 = 60,   // mixed precision, operands rounded to fp16, 256 x 256
     KID_MFMA_LP_BF16 = 61,  // the same with bf16
+    KID_MFMA_LP_F16_S = 62, // mixed precision, fp16, 64 x 64 (few output tiles)
+    KID_MFMA_LP_BF16_S = 63,
 };
 
 // Tile geometry of each kernel (rows x cols of C per workgroup).
@@ -58,8 +60,8 @@ hipError_t launch_tiled(const GemmArgs &a, bool transB, bool pad, hipStream_t st
 hipError_t launch_regblock(const GemmArgs &a, bool transB, bool vec, hipStream_t stream);
 hipError_t launch_mfma(const GemmArgs &a, int kid, bool transB, bool vec, hipStream_t stream, int splits = 1);
 // Mixed precision: operands rounded to fp16 (bf16 = false) or bf16 while staged.
-hipError_t launch_mfma_lp(const GemmArgs &a, bool bf16, bool transB, bool vec, hipStream_t stream);
-TileShape lp_tile_shape();
+hipError_t launch_mfma_lp(const GemmArgs &a, bool large, bool bf16, bool transB, bool vec, hipStream_t stream);
+TileShape lp_tile_shape(bool large);
 // C <- alpha * sum_{s<splits} W[s*stride + i*N + j] + beta*C (C not read when beta == 0).
 hipError_t launch_splitk_reduce(const float *W, int splits, int64_t stride, int M, int N, float alpha, float beta,
                                 float *C, int64_t ldc, bool vec, hipStream_t stream);

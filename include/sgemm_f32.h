@@ -249,7 +249,9 @@ int sgemm_f32_lowp(int precision, int64_t M, int64_t N, int64_t K, float alpha,
                    const float *A, int64_t lda, const float *B, int64_t ldb, int transB,
                    float beta, float *C, int64_t ldc, void *stream);
 
-/* Host-only planning query for sgemm_f32_lowp, the counterpart of sgemm_f32_plan. */
+/* Host-only planning query for sgemm_f32_lowp, the counterpart of sgemm_f32_plan.
+ * The kernel takes 256 x 256 output tiles when there are at least 256 of them
+ * (one per compute unit), else 64 x 64 tiles; tiles_m / tiles_n count them. */
 int sgemm_f32_lowp_plan(int precision, int64_t M, int64_t N, int64_t K, float alpha,
                         const float *A, int64_t lda, const float *B, int64_t ldb, int transB,
                         float beta, const float *C, int64_t ldc,

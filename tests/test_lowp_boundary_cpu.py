@@ -7,7 +7,7 @@ import pytest
 import fp32_gemm_08_amd as lib
 
 OK, INVALID, ALIAS = 0, 1, 2
-KID_SCALE, KID_LP_F16, KID_LP_BF16 = 1, 60, 61
+KID_SCALE, KID_LP_F16, KID_LP_BF16, KID_LP_F16_S, KID_LP_BF16_S = 1, 60, 61, 62, 63
 PA, PB, PC = 1 << 32, 1 << 40, 1 << 44
 
 
@@ -43,13 +43,20 @@ def test_alias(kw):
     assert plan(**kw)[0] == ALIAS and call(**kw) == ALIAS
 
 
-@pytest.mark.parametrize("prec,kid,tag", [(1, KID_LP_F16, "f16"), (2, KID_LP_BF16, "bf16")])
-@pytest.mark.parametrize("shape,tiles", [((4096, 4096, 4096), (16, 16)), ((1000, 1017, 999), (4, 4)),
-                                         ((1, 1, 1), (1, 1)), ((257, 256, 5), (2, 1))])
-def test_plan(prec, kid, tag, shape, tiles):
+@pytest.mark.parametrize("prec,tag", [(1, "f16"), (2, "bf16")])
+@pytest.mark.parametrize("shape,large,tiles", [
+    ((4096, 4096, 4096), True, (16, 16)),     # 256 tiles of 256 x 256: every CU busy
+    ((4096, 4000, 64), True, (16, 16)),
+    ((4000, 3840, 512), False, (63, 60)),     # 16 x 15 = 240 large tiles: the 64 x 64 tile
+    ((2048, 2048, 2048), False, (32, 32)),
+    ((1000, 1017, 999), False, (16, 16)),
+    ((1, 1, 1), False, (1, 1)),
+    ((257, 256, 5), False, (5, 4))])
+def test_plan(prec, tag, shape, large, tiles):
     st, k, tm, tn, name = plan(prec, *shape)
-    assert (st, k, (tm, tn)) == (OK, kid, tiles)
-    assert name.startswith(f"mfma_lp_{tag}_256x256x32")
+    kid = {(1, True): KID_LP_F16, (2, True): KID_LP_BF16, (1, False): KID_LP_F16_S, (2, False): KID_LP_BF16_S}
+    assert (st, k, (tm, tn)) == (OK, kid[(prec, large)], tiles)
+    assert name.startswith(f"mfma_lp_{tag}_256x256x32" if large else f"mfma_lp_{tag}_64x64x32")
 
 
 def test_quick_returns_and_product_free():
