@@ -192,6 +192,66 @@ def sweep(algos=("naive", "naive_wg", "lds_tiled", "lds_tiled_nopad", "regblock"
     return rows
 
 
+# Shapes for the MFMA tile-choice table: squares from 768 to 8192 and
+# rectangles whose tile counts fall just above or below a multiple of 256.
+TILE_SWEEP_SHAPES = [(n, n, n) for n in (768, 1024, 1280, 1536, 2048, 2560, 3072, 3584, 4096, 4608, 5120, 6144,
+                                         7168, 8192)] + [
+    (512, 4096, 4096), (1024, 8192, 2048), (3000, 3000, 3000), (16384, 4096, 1024), (8192, 1024, 4096),
+    (2048, 8192, 1024), (6144, 6144, 2048), (1536, 1536, 4096), (4096, 4096, 1024), (2304, 2304, 8192)]
+
+
+def sweep_tiles():
+    """Each fixed MFMA tile, AUTO, and torch.mm (the vendor library, as a
+    reference point) on uniform [-1, 1) operands, op(B) = B, alpha 1, beta 0:
+    TFLOP/s from HIP events over back-to-back calls."""
+    import torch
+
+    import fp32_gemm_08_amd as lib
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream(dev)
+    w = torch.rand(4096, 4096, device=dev)
+    wc = torch.empty_like(w)
+    for _ in range(300):
+        lib.gemm(w, w, wc, algo="mfma")
+    torch.cuda.synchronize()
+    del w, wc
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+
+    def timeit(fn, reps):
+        for _ in range(max(3, reps // 5)):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    algos = ("mfma_256", "mfma_128", "mfma_64", "auto")
+    print("| M×N×K | " + " | ".join(algos) + " | AUTO picks | torch.mm |")
+    print("|---|" + "---|" * (len(algos) + 2))
+    for (M, N, K) in TILE_SWEEP_SHAPES:
+        A = torch.rand(M, K, device=dev, generator=g) * 2 - 1
+        B = torch.rand(K, N, device=dev, generator=g) * 2 - 1
+        C = torch.empty(M, N, device=dev)
+        flop = 2.0 * M * N * K
+        reps = max(10, min(400, int(0.08 / (flop / 120e12))))
+        cells = []
+        for algo in algos:
+            t = timeit(lambda: lib.gemm(A, B, C, algo=algo), reps)
+            cells.append(f"{flop / t / 1e12:.1f}")
+        pick = lib.sgemm_f32_plan(0, M, N, K, 1.0, A.data_ptr(), K, B.data_ptr(), N, 0, 0.0, C.data_ptr(), N)[4]
+        t = timeit(lambda: torch.mm(A, B, out=C), reps)
+        print(f"| {M}×{N}×{K} | " + " | ".join(cells) + f" | {pick.split()[0]} | {flop / t / 1e12:.1f} |",
+              flush=True)
+        del A, B, C
+        torch.cuda.empty_cache()
+
+
 def transpose_cpu_baseline(src, rows, cols, D_gpu_host, target_s):
     """Time the transpose oracle on the same workload, repeated for about
     ``target_s`` seconds, and check its result against the GPU's bit for bit."""
@@ -459,6 +519,8 @@ def main():
                     help="transpose: also time one source/destination pair repeated (cache-resident context)")
     ap.add_argument("--sweep", action="store_true",
                     help="time every algorithm on every workload and print a table (no JSON line)")
+    ap.add_argument("--tile-sweep", action="store_true",
+                    help="time each fixed MFMA tile, AUTO and torch.mm over a spread of shapes (no JSON line)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -483,6 +545,9 @@ def main():
         return
     if args.sweep:
         sweep()
+        return
+    if args.tile_sweep:
+        sweep_tiles()
         return
 
     import fp32_gemm_08_amd as lib

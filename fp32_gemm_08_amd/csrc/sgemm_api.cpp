@@ -6,6 +6,7 @@
 #include "transpose_internal.h"
 
 #include <atomic>
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <limits>
@@ -50,16 +51,47 @@ bool overlaps(const void *p, int64_t pb, const void *q, int64_t qb)
 
 bool aligned16(const void *p, int64_t ld) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0 && (ld & 3) == 0; }
 
-// Largest MFMA tile that still gives every CU a workgroup; the smallest tile otherwise.
+// MFMA tile from a wave-quantisation model.  Every tile has the 256 CUs as
+// workgroup slots (the 256 x 256 and 128 x 128 tiles hold a CU each; 64 x 64
+// workgroups share one up to 4 at a time and are dealt round-robin), so the
+// busiest CU runs c = ceil(tiles / 256) of them and the grid runs at
+// rate x (tiles / 256) / c, times the share of the tiles' area inside M x N
+// (edge tiles compute their whole area).  Rates in TFLOP/s, measured on
+// MI355X over square and rectangular shapes from 768 to 8192: 256 x 256 143,
+// 128 x 128 136, 64 x 64 121 (97 with one workgroup per CU).  On the 24
+// shapes measured it picked the fastest of the three tiles every time.  Ties
+// go to the larger tile.
+double mfma_rate(int kid, int64_t M, int64_t N)
+{
+    const TileShape t = tile_shape(kid);
+    const double tiles = (double)(ceil_div(M, t.bm) * ceil_div(N, t.bn));
+    const double c = std::ceil(tiles / 256.0);
+    double r = 0.0;
+    switch (kid) {
+    case KID_MFMA_L: r = 143.0; break;
+    case KID_MFMA_M: r = 136.0; break;
+    default: r = c > 1.0 ? 121.0 : 97.0; break;
+    }
+    return r * (tiles / 256.0) / c * ((double)M * (double)N / (tiles * t.bm * t.bn));
+}
+
 int choose_mfma(int64_t M, int64_t N)
 {
     const int kids[3] = {KID_MFMA_L, KID_MFMA_M, KID_MFMA_S};
+    int best = KID_MFMA_L;
+    double best_rate = -1.0;
     for (int kid : kids) {
         const TileShape t = tile_shape(kid);
-        if (ceil_div(M, t.bm) * ceil_div(N, t.bn) >= 256)
-            return kid;
+        const int64_t threads = kid == KID_MFMA_S ? 256 : 512;
+        if (ceil_div(M, t.bm) * ceil_div(N, t.bn) * threads > kMaxWorkItems)
+            continue;  // grid too large for one launch
+        const double r = mfma_rate(kid, M, N);
+        if (r > best_rate) {
+            best_rate = r;
+            best = kid;
+        }
     }
-    return KID_MFMA_S;
+    return best;
 }
 
 // k-split geometry: k per split, a whole number of 32-wide k-tiles, and the
@@ -105,7 +137,7 @@ Plan make_plan(int algo, int64_t M, int64_t N, int64_t K, float alpha, const flo
         p.kid = KID_NONE;
         return p;
     };
-    if (algo < SGEMM_ALGO_AUTO || algo > SGEMM_ALGO_NAIVE_WG)
+    if (algo < SGEMM_ALGO_AUTO || algo > SGEMM_ALGO_MFMA_64)
         return fail(SGEMM_ERR_INVALID_VALUE);
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
         return fail(SGEMM_ERR_INVALID_VALUE);
@@ -148,6 +180,9 @@ Plan make_plan(int algo, int64_t M, int64_t N, int64_t K, float alpha, const flo
     case SGEMM_ALGO_REGBLOCK: p.kid = KID_REGBLOCK; break;
     case SGEMM_ALGO_MFMA:
     case SGEMM_ALGO_AUTO: p.kid = choose_mfma(M, N); break;
+    case SGEMM_ALGO_MFMA_256: p.kid = KID_MFMA_L; break;
+    case SGEMM_ALGO_MFMA_128: p.kid = KID_MFMA_M; break;
+    case SGEMM_ALGO_MFMA_64: p.kid = KID_MFMA_S; break;
     }
     const TileShape t = tile_shape(p.kid);
     p.tiles_m = ceil_div(M, t.bm);

@@ -95,6 +95,10 @@ typedef enum {
  *                    the naive and 2-D block-tiled CUDA matmul, paragraph on the
  *                    naive implementation: one block per output element with an
  *                    in-block reduction).
+ *   MFMA_256, MFMA_128, MFMA_64
+ *                    the MFMA path with its workgroup tile fixed: 256 x 256 (8
+ *                    wavefronts), 128 x 128 (8 wavefronts as two k-slices of 4) or
+ *                    64 x 64 (4 wavefronts, up to 4 workgroups per CU).
  *   AUTO             MFMA with a tile chosen from the problem shape.
  */
 typedef enum {
@@ -104,7 +108,10 @@ typedef enum {
     SGEMM_ALGO_REGBLOCK = 3,
     SGEMM_ALGO_MFMA = 4,
     SGEMM_ALGO_LDS_TILED_NOPAD = 5,
-    SGEMM_ALGO_NAIVE_WG = 6
+    SGEMM_ALGO_NAIVE_WG = 6,
+    SGEMM_ALGO_MFMA_256 = 7,
+    SGEMM_ALGO_MFMA_128 = 8,
+    SGEMM_ALGO_MFMA_64 = 9
 } sgemm_algo;
 
 /*

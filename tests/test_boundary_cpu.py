@@ -72,7 +72,7 @@ def call(algo=0, M=64, N=64, K=64, alpha=1.0, A=PA, lda=None, B=PB, ldb=None, tr
     dict(M=-1), dict(N=-1), dict(K=-1), dict(M=1 << 31), dict(K=1 << 31),
     dict(transB=2), dict(transB=-1),
     dict(lda=63), dict(ldb=63), dict(ldc=63), dict(transB=1, ldb=63),
-    dict(A=0), dict(B=0), dict(C=0), dict(algo=7), dict(algo=-1),
+    dict(A=0), dict(B=0), dict(C=0), dict(algo=10), dict(algo=-1),
     dict(M=(1 << 31) - 1024), dict(N=(1 << 31) - 1024), dict(K=(1 << 31) - 1024),
     dict(M=2, K=2, lda=1 << 61),
 ])
@@ -128,7 +128,7 @@ def test_product_free_cases_scale_c():
 
 
 @pytest.mark.parametrize("algo,kid", [(1, KID_NAIVE), (2, KID_TILED), (3, KID_REG), (5, KID_TILED_NOPAD),
-                                      (6, KID_NAIVE_WG)])
+                                      (6, KID_NAIVE_WG), (7, KID_L), (8, KID_M), (9, KID_S)])
 def test_explicit_algorithms(algo, kid):
     st, k, tm, tn, name = plan(algo=algo, M=1000, N=1017, K=999)
     assert (st, k) == (OK, kid)
@@ -138,6 +138,10 @@ def test_explicit_algorithms(algo, kid):
         assert (tm, tn) == (1000, 1017) and name.startswith("naive_wave_per_output")
     elif kid in (KID_TILED, KID_TILED_NOPAD):
         assert (tm, tn) == (63, 64)
+    elif kid == KID_L:
+        assert (tm, tn) == (4, 4) and name.startswith("mfma_256x256")
+    elif kid == KID_S:
+        assert (tm, tn) == (16, 16) and name.startswith("mfma_64x64")
     else:
         assert (tm, tn) == (8, 8)
 

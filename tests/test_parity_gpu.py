@@ -151,10 +151,11 @@ def _sweep_cases(n, seed):
     return out
 
 
-@pytest.mark.parametrize("algo", ["mfma", "regblock", "lds_tiled", "naive", "naive_wg"])
+@pytest.mark.parametrize("algo", ["mfma", "mfma_256", "mfma_128", "mfma_64", "regblock", "lds_tiled", "naive",
+                                  "naive_wg"])
 def test_random_ragged_sweep(oracle_lib, algo):
     """Seeded sweep of ragged shapes in [1, 700]^3, both op(B), random alpha/beta."""
-    for (M, N, K, t, alpha, beta, seed) in _sweep_cases(24 if algo == "mfma" else 8, 42):
+    for (M, N, K, t, alpha, beta, seed) in _sweep_cases(24 if algo.startswith("mfma") else 8, 42):
         case = make_case(M, N, K, trans_b=t, alpha=alpha, beta=beta, dist="uniform", seed=seed)
         st, Dg = run_case(case, algo)
         assert st == 0
@@ -162,7 +163,8 @@ def test_random_ragged_sweep(oracle_lib, algo):
         assert_parity(Dg[:, :N], D, S, K, f"sweep {M}x{N}x{K} t{t}/{algo}")
 
 
-@pytest.mark.parametrize("algo", ["mfma", "regblock", "lds_tiled", "naive", "naive_wg"])
+@pytest.mark.parametrize("algo", ["mfma", "mfma_256", "mfma_128", "mfma_64", "regblock", "lds_tiled", "naive",
+                                  "naive_wg"])
 def test_degenerate_shapes(oracle_lib, algo):
     for (M, N, K, t) in [(1, 1, 1, 0), (1, 1, 1, 1), (1, 513, 1, 0), (513, 1, 2, 1), (31, 33, 1, 0),
                          (64, 64, 8, 1), (65, 65, 9, 0), (7, 5, 4099, 1)]:
@@ -182,15 +184,15 @@ MID_SHAPES = [(2000, 2100, 1004, 0, None), (2000, 2100, 1004, 1, None), (2048, 2
 
 @pytest.mark.parametrize("shape", MID_SHAPES, ids=lambda s: "x".join(str(v) for v in s[:4]))
 def test_mid_tile_edges_and_tails(oracle_lib, shape):
-    """Shapes that the shape-based choice sends to the 128x128 tile whose k-range
-    is split over two wavefront groups: ragged edges in M and N, K tails (K %
-    32 != 0), op(B) = B^T, and an unaligned leading dimension (register path)."""
+    """The 128x128 tile whose k-range is split over two wavefront groups, on
+    ragged edges in M and N, K tails (K % 32 != 0), op(B) = B^T, and an
+    unaligned leading dimension (register path)."""
     M, N, K, t, lda = shape
-    st, kid, tm, tn, name = lib.sgemm_f32_plan(0, M, N, K, 1.0, 1 << 32, lda or K, 1 << 40, K if t else N, t,
-                                              0.5, 1 << 44, N)
+    st, kid, tm, tn, name = lib.sgemm_f32_plan(lib.ALGO["mfma_128"], M, N, K, 1.0, 1 << 32, lda or K, 1 << 40,
+                                              K if t else N, t, 0.5, 1 << 44, N)
     assert kid == 41, name
     case = make_case(M, N, K, trans_b=t, alpha=1.25, beta=0.5, dist="uniform", seed=M + K, lda=lda)
-    st, Dg = run_case(case, "auto", guard=False)
+    st, Dg = run_case(case, "mfma_128", guard=False)
     assert st == 0
     rows = sample_rows(M, n=24, seed=K, tile=128)
     D, S = oracle_rows(oracle_lib, case, rows)
@@ -199,17 +201,18 @@ def test_mid_tile_edges_and_tails(oracle_lib, shape):
 
 def test_mid_tile_integers_bit_exact(oracle_lib):
     case = make_case(2000, 2100, 1004, trans_b=1, alpha=1.5, beta=-0.5, dist="int2", seed=9)
-    st, Dg = run_case(case, "auto", guard=False)
+    st, Dg = run_case(case, "mfma_128", guard=False)
     assert st == 0
     rows = sample_rows(2000, n=16, seed=1, tile=128)
     D, _ = oracle_rows(oracle_lib, case, rows)
     assert np.array_equal(Dg[rows, :2100], D.astype(np.float32))
 
 
-# (M, N, K, transB, expected kernel): aligned operands whose tiles reach past M
-# and/or N, for each MFMA tile.  Edge tiles stage directly with clamped rows
+# (M, N, K, transB, kernel): aligned operands whose tiles reach past M and/or
+# N, for each MFMA tile (forced with its fixed-tile algorithm).  Edge tiles stage directly with clamped rows
 # (op(B) = B^T, or op(B) = B with N % 4 == 0) or through masked registers
 # (op(B) = B with N % 4 != 0); K tails on some.
+TILE_ALGO = {40: "mfma_256", 41: "mfma_128", 42: "mfma_64"}
 EDGE_SHAPES = [(1000, 1000, 1024, 0, 42), (1000, 1000, 1024, 1, 42), (1000, 1004, 999, 0, 42),
                (1003, 1001, 1000, 1, 42), (1001, 1003, 1000, 0, 42), (2000, 2052, 1000, 0, 41),
                (2001, 1999, 777, 1, 41), (3999, 4000, 512, 0, 40), (4000, 3998, 520, 1, 40),
@@ -222,10 +225,11 @@ def test_edge_tiles_aligned(oracle_lib, shape):
     r4 = lambda v: (v + 3) // 4 * 4  # noqa: E731  (leading dimensions padded to 16 bytes)
     case = make_case(M, N, K, trans_b=t, alpha=0.75, beta=-1.25, dist="uniform", seed=M * 3 + N,
                      lda=r4(K), ldb=r4(K) if t else r4(N))
-    st, kid, tm, tn, name = lib.sgemm_f32_plan(0, M, N, K, 1.0, 1 << 32, case.lda, 1 << 40, case.ldb, t,
-                                              0.5, 1 << 44, N)
+    algo = TILE_ALGO[want]
+    st, kid, tm, tn, name = lib.sgemm_f32_plan(lib.ALGO[algo], M, N, K, 1.0, 1 << 32, case.lda, 1 << 40, case.ldb,
+                                              t, 0.5, 1 << 44, N)
     assert kid == want and "vec=1" in name, name
-    st, Dg = run_case(case, "auto", ldc_pad=4)
+    st, Dg = run_case(case, algo, ldc_pad=4)
     assert st == 0
     rows = np.unique(np.concatenate([sample_rows(M, n=20, seed=K, tile=64), np.arange(M - 70, M)]))
     D, S = oracle_rows(oracle_lib, case, rows)
@@ -243,30 +247,33 @@ UNALIGNED_SHAPES = [(1000, 1017, 999, 1, 0, 42), (1001, 1003, 1000, 0, 0, 42), (
 def test_unaligned_operands(oracle_lib, shape):
     M, N, K, t, a_off, want = shape
     case = make_case(M, N, K, trans_b=t, alpha=1.5, beta=0.25, dist="uniform", seed=M + 7 * N)
-    st, kid, tm, tn, name = lib.sgemm_f32_plan(0, M, N, K, 1.0, (1 << 32) + 4 * a_off, case.lda, 1 << 40, case.ldb,
-                                              t, 0.5, 1 << 44, N)
+    algo = TILE_ALGO[want]
+    st, kid, tm, tn, name = lib.sgemm_f32_plan(lib.ALGO[algo], M, N, K, 1.0, (1 << 32) + 4 * a_off, case.lda,
+                                              1 << 40, case.ldb, t, 0.5, 1 << 44, N)
     assert kid == want and "vec=0" in name, name
-    st, Dg = run_case(case, "auto", a_offset=a_off, ldc_pad=1)
+    st, Dg = run_case(case, algo, a_offset=a_off, ldc_pad=1)
     assert st == 0
     rows = np.unique(np.concatenate([sample_rows(M, n=20, seed=K, tile=64), np.arange(M - 70, M)]))
     D, S = oracle_rows(oracle_lib, case, rows)
     assert_parity(Dg[rows, :N], D, S, K, f"unaligned {M}x{N}x{K} t{t} a_off={a_off}")
 
 
+@pytest.mark.parametrize("algo", ["mfma_256", "mfma_128", "mfma_64"])
 @pytest.mark.parametrize("t", [0, 1])
-def test_unaligned_integers_bit_exact(oracle_lib, t):
+def test_unaligned_integers_bit_exact(oracle_lib, t, algo):
     case = make_case(1003, 1001, 999, trans_b=t, alpha=1.0, beta=1.0, dist="int2", seed=23)
-    st, Dg = run_case(case, "auto", a_offset=1)
+    st, Dg = run_case(case, algo, a_offset=1)
     assert st == 0
     D, _ = oracle_rows(oracle_lib, case)
     assert np.array_equal(Dg[:, :1001], D.astype(np.float32))
 
 
+@pytest.mark.parametrize("algo", ["mfma_256", "mfma_128", "mfma_64"])
 @pytest.mark.parametrize("t", [0, 1])
-def test_edge_tiles_integers_bit_exact(oracle_lib, t):
+def test_edge_tiles_integers_bit_exact(oracle_lib, t, algo):
     case = make_case(1003, 1004, 1000, trans_b=t, alpha=1.0, beta=1.0, dist="int2", seed=19)
     assert case.lda % 4 == 0 and case.ldb % 4 == 0
-    st, Dg = run_case(case, "auto")
+    st, Dg = run_case(case, algo)
     assert st == 0
     D, _ = oracle_rows(oracle_lib, case)
     assert np.array_equal(Dg[:, :1004], D.astype(np.float32))
