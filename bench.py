@@ -232,8 +232,10 @@ def sweep_tiles():
         return e0.elapsed_time(e1) * 1e-3 / reps
 
     algos = ("mfma_256", "mfma_128", "mfma_64", "auto")
-    print("| M×N×K | " + " | ".join(algos) + " | AUTO picks | torch.mm |")
-    print("|---|" + "---|" * (len(algos) + 2))
+    ws = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    print("| M×N×K | " + " | ".join(algos) + " | AUTO picks | stream-K 256 | stream-K 128 | with workspace "
+          "| ws picks | torch.mm |")
+    print("|---|" + "---|" * (len(algos) + 6))
     for (M, N, K) in TILE_SWEEP_SHAPES:
         A = torch.rand(M, K, device=dev, generator=g) * 2 - 1
         B = torch.rand(K, N, device=dev, generator=g) * 2 - 1
@@ -245,9 +247,15 @@ def sweep_tiles():
             t = timeit(lambda: lib.gemm(A, B, C, algo=algo), reps)
             cells.append(f"{flop / t / 1e12:.1f}")
         pick = lib.sgemm_f32_plan(0, M, N, K, 1.0, A.data_ptr(), K, B.data_ptr(), N, 0, 0.0, C.data_ptr(), N)[4]
+        for tile in (256, 128):
+            t = timeit(lambda: lib.gemm(A, B, C, workspace=ws, streamk=tile), reps)
+            cells.append(f"{flop / t / 1e12:.1f}")
+        t = timeit(lambda: lib.gemm(A, B, C, workspace=ws), reps)
+        method = ("plain", "k-split", "stream-K")[lib.sgemm_f32_ws_plan(M, N, K, 0)[1]]
+        cells.append(f"{flop / t / 1e12:.1f}")
         t = timeit(lambda: torch.mm(A, B, out=C), reps)
-        print(f"| {M}×{N}×{K} | " + " | ".join(cells) + f" | {pick.split()[0]} | {flop / t / 1e12:.1f} |",
-              flush=True)
+        print(f"| {M}×{N}×{K} | " + " | ".join(cells[:4]) + f" | {pick.split()[0]} | " + " | ".join(cells[4:]) +
+              f" | {method} | {flop / t / 1e12:.1f} |", flush=True)
         del A, B, C
         torch.cuda.empty_cache()
 

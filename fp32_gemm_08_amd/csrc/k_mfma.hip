@@ -72,15 +72,34 @@ template <> __device__ __forceinline__ void vset<4>(f32x4 &v, int i, float x) { 
 // Wavefront index within the workgroup, as a wave-uniform (scalar) value: the
 // LDS block addresses derived from it then stay in scalar registers, and M0 for
 // the direct loads is set without a per-load vector-to-scalar move (measured ~1%).
-__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
-
-// Tile index for workgroup `bid` over an nbm x nbn tile grid (see header note).
-__device__ __forceinline__ void map_tile(int bid, int nbm, int nbn, int &tm, int &tn)
+// threadIdx.x; OPQ: behind an empty asm, so that each tile's set-up derives
+// its per-lane offsets afresh.  The stream-K kernel runs the tile code in a
+// loop and would otherwise hoist them out of it and hold them (spilled)
+// across the loop; the plain kernels keep the direct read (measured 0.6%
+// faster at 4096^3).
+template <bool OPQ>
+__device__ __forceinline__ int work_item()
 {
-    const int total = nbm * nbn;
-    int t = bid;
-    if ((total & 7) == 0)
-        t = (bid & 7) * (total >> 3) + (bid >> 3);
+    int t = (int)threadIdx.x;
+    if constexpr (OPQ)
+        asm volatile("" : "+v"(t));
+    return t;
+}
+
+template <bool OPQ>
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(work_item<OPQ>() >> 6); }
+
+// Tile order: workgroups are dealt round-robin to the 8 XCDs, so ids are
+// renumbered to give each XCD one contiguous run (xcd_remap), and the runs walk
+// the tile grid 8 tile-rows at a time, column by column (group_order), so the
+// tiles one XCD holds at once share rows of A and columns of B in its L2.
+__device__ __forceinline__ int xcd_remap(int bid, int total)
+{
+    return (total & 7) == 0 ? (bid & 7) * (total >> 3) + (bid >> 3) : bid;
+}
+
+__device__ __forceinline__ void group_order(int t, int nbm, int nbn, int &tm, int &tn)
+{
     constexpr int G = 8;
     const int per_group = G * nbn;
     const int gi = t / per_group;
@@ -89,6 +108,12 @@ __device__ __forceinline__ void map_tile(int bid, int nbm, int nbn, int &tm, int
     const int in = t - gi * per_group;
     tm = first + in % gsz;
     tn = in / gsz;
+}
+
+// Tile index for workgroup `bid` over an nbm x nbn tile grid.
+__device__ __forceinline__ void map_tile(int bid, int nbm, int nbn, int &tm, int &tn)
+{
+    group_order(xcd_remap(bid, nbm * nbn), nbm, nbn, tm, tn);
 }
 
 // Four consecutive floats from p.  MASKED: elements at or beyond `limit` (or all
@@ -119,9 +144,10 @@ __device__ __forceinline__ f32x4 load4(const float *p, bool ok, int first, int l
 // k-range of one output tile over KS groups of wavefronts ("k-slices"): an LDS
 // stage then holds KS consecutive BK-deep k-tiles, slice s multiplies the s-th
 // into its own accumulators, and the slices are added in LDS at the end.
-template <int BM_, int BN_, int BK_, int WGM_, int WGN_, int OCC_, bool TRANS_B, int KS_ = 1>
+template <int BM_, int BN_, int BK_, int WGM_, int WGN_, int OCC_, bool TRANS_B, int KS_ = 1, bool OPQ_ = false>
 struct Geo {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_, OCC = OCC_, KS = KS_;
+    static constexpr bool OPQ = OPQ_;                  // per-lane ids behind an asm (stream-K)
     static constexpr int NWO = WGM * WGN;              // wavefronts per k-slice (one output tile)
     static constexpr int NW = NWO * KS;                // wavefronts per workgroup
     static constexpr int NT = 64 * NW;                 // work-items per workgroup
@@ -160,8 +186,8 @@ struct Role {
     int lane, l32, hi, slice, wo, wm, wn;
     __device__ __forceinline__ Role()
     {
-        const int wave = wave_id();
-        lane = threadIdx.x & 63;
+        const int wave = wave_id<Gm::OPQ>();
+        lane = work_item<Gm::OPQ>() & 63;
         l32 = lane & 31;
         hi = lane >> 5;
         slice = wave / Gm::NWO;
@@ -274,7 +300,7 @@ struct RegStage {
 
     __device__ __forceinline__ void init(const GemmArgs &a, int m0, int n0)
     {
-        const int tid = threadIdx.x;
+        const int tid = work_item<Gm::OPQ>();
 #pragma unroll
         for (int i = 0; i < CA; ++i) {
             const int q = tid + i * Gm::NT;
@@ -379,7 +405,7 @@ struct DirectStage {
     template <bool EDGE>
     __device__ __forceinline__ void init(const GemmArgs &a, int m0, int n0)
     {
-        const int lane = threadIdx.x & 63, wave = wave_id();
+        const int lane = work_item<Gm::OPQ>() & 63, wave = wave_id<Gm::OPQ>();
 #pragma unroll
         for (int j = 0; j < A_N; ++j) {
             const int b = wave * A_N + j;
@@ -691,30 +717,14 @@ __device__ __forceinline__ void gemm_tile_direct(const GemmArgs &a, float *smem,
         epilogue<Gm, TRANS_B, !EDGE>(a, acc, m0, n0, ro);
 }
 
-// GD: geometry of the direct path; GR: geometry of the register path (same
-// workgroup tile, wavefront layout and k-split, possibly a shorter k-tile so
-// the register staging fits next to the accumulators).
+// One output tile at (m0, n0): direct staging for interior tiles with aligned
+// operands (and edge tiles whose clamped addresses are exact), registers
+// otherwise.  GD: geometry of the direct path; GR: geometry of the register
+// path (same workgroup tile, wavefront layout and k-split, possibly a shorter
+// k-tile so the register staging fits next to the accumulators).
 template <class GD, class GR, bool TRANS_B, bool VEC>
-__global__ __launch_bounds__(GD::NT) __attribute__((amdgpu_waves_per_eu(GD::OCC)))
-void sgemm_mfma_kernel(GemmArgs a)
+__device__ __forceinline__ void mfma_tile(const GemmArgs &a, float *smem, int m0, int n0)
 {
-    static_assert(GD::BM == GR::BM && GD::BN == GR::BN && GD::NT == GR::NT && GD::WGN == GR::WGN &&
-                      GD::KS == GR::KS,
-                  "both paths share the workgroup tile");
-    constexpr int SMEM = GD::SMEM > GR::SMEM ? GD::SMEM : GR::SMEM;
-    __shared__ __attribute__((aligned(1024))) float smem[SMEM];
-    if (gridDim.y > 1) {
-        // k-split partial pass: this split's k-range and partial-product slice.
-        const int s = blockIdx.y, k0 = s * a.k_split;
-        a.A += k0;
-        a.B += TRANS_B ? (int64_t)k0 : (int64_t)k0 * a.ldb;
-        a.K = min(a.k_split, a.K - k0);
-        a.C += (int64_t)s * a.c_split_stride;
-    }
-    const int nbm = (a.M + GD::BM - 1) / GD::BM, nbn = (a.N + GD::BN - 1) / GD::BN;
-    int tile_m, tile_n;
-    map_tile(blockIdx.x, nbm, nbn, tile_m, tile_n);
-    const int m0 = tile_m * GD::BM, n0 = tile_n * GD::BN;
     const bool full = m0 + GD::BM <= a.M && n0 + GD::BN <= a.N;
     // 16-byte direct loads for aligned operands, 4-byte ones otherwise (not on
     // the 256 x 256 tile: its 32 per-lane source offsets would not fit beside
@@ -737,6 +747,163 @@ void sgemm_mfma_kernel(GemmArgs a)
         gemm_tile_regs<GR, TRANS_B, VEC, true>(a, smem, m0, n0);
     else
         gemm_tile_regs<GR, TRANS_B, VEC, false>(a, smem, m0, n0);
+}
+
+template <class GD, class GR>
+struct SharedGeo {
+    static_assert(GD::BM == GR::BM && GD::BN == GR::BN && GD::NT == GR::NT && GD::WGN == GR::WGN &&
+                      GD::KS == GR::KS,
+                  "both paths share the workgroup tile");
+    static constexpr int SMEM = GD::SMEM > GR::SMEM ? GD::SMEM : GR::SMEM;
+};
+
+template <class GD, class GR, bool TRANS_B, bool VEC>
+__global__ __launch_bounds__(GD::NT) __attribute__((amdgpu_waves_per_eu(GD::OCC)))
+void sgemm_mfma_kernel(GemmArgs a)
+{
+    __shared__ __attribute__((aligned(1024))) float smem[SharedGeo<GD, GR>::SMEM];
+    if (gridDim.y > 1) {
+        // k-split partial pass: this split's k-range and partial-product slice.
+        const int s = blockIdx.y, k0 = s * a.k_split;
+        a.A += k0;
+        a.B += TRANS_B ? (int64_t)k0 : (int64_t)k0 * a.ldb;
+        a.K = min(a.k_split, a.K - k0);
+        a.C += (int64_t)s * a.c_split_stride;
+    }
+    const int nbm = (a.M + GD::BM - 1) / GD::BM, nbn = (a.N + GD::BN - 1) / GD::BN;
+    int tile_m, tile_n;
+    map_tile(blockIdx.x, nbm, nbn, tile_m, tile_n);
+    mfma_tile<GD, GR, TRANS_B, VEC>(a, smem, tile_m * GD::BM, tile_n * GD::BN);
+}
+
+// A uniform value the compiler cannot see through (an empty asm that claims to
+// rewrite the scalar register holding it).
+__device__ __forceinline__ int64_t opaque(int64_t v)
+{
+    asm volatile("" : "+s"(v));
+    return v;
+}
+
+// Stream-K: the k-iterations of all output tiles, one LDS stage of k each, in
+// tile order (group_order) and k order within a tile.  Workgroups below sk.dp
+// take whole tiles (XCD-remapped, as the plain kernel); the sk.workers after
+// them split the iterations of the last sk.tiles tiles evenly, each a
+// contiguous range, so every CU gets the same share of the work whatever the
+// tile count (Osama et al., "Stream-K: Work-centric Parallel Decomposition for
+// Dense Matrix-Matrix Multiplication on the GPU").  A range is cut into pieces
+// at tile boundaries; each piece runs the ordinary tile code on its sub-range
+// of k with the operand pointers moved to the tile's corner.  A piece that is
+// a whole tile is finished in place; any other piece writes its raw partial
+// product to the worker's slot and the fix-up kernel completes the tile.  No
+// workgroup ever waits for another.
+template <class GD, class GR, bool TRANS_B, bool VEC>
+__global__ __launch_bounds__(GD::NT) __attribute__((amdgpu_waves_per_eu(GD::OCC)))
+void sgemm_mfma_sk_kernel(GemmArgs a, SkArgs sk)
+{
+    __shared__ __attribute__((aligned(1024))) float smem[SharedGeo<GD, GR>::SMEM];
+    const int nbm = (a.M + GD::BM - 1) / GD::BM, nbn = (a.N + GD::BN - 1) / GD::BN;
+    const int iters = sk.iters;
+    const int bid = blockIdx.x;
+    int w = -1;
+    int64_t it, end;
+    if (bid < sk.dp) {
+        it = (int64_t)xcd_remap(bid, sk.dp) * iters;
+        end = it + iters;
+    } else {
+        const int P = sk.workers, raw = bid - sk.dp;
+        w = (P & 7) == 0 ? (raw & 7) * (P >> 3) + (raw >> 3) : raw;
+        const int64_t S = (int64_t)sk.sk_tiles * iters, base = (int64_t)sk.dp * iters;
+        it = base + (int64_t)w * S / P;
+        end = base + (int64_t)(w + 1) * S / P;
+    }
+    const int64_t first = it;
+    while (it < end) {
+        const int t = (int)(it / iters);
+        const int kb = (int)(it - (int64_t)t * iters);
+        const int ke = (int)min((int64_t)iters, kb + (end - it));
+        int tm, tn;
+        group_order(t, nbm, nbn, tm, tn);
+        const int m0 = tm * GD::BM, n0 = tn * GD::BN;
+        const int k0 = kb * GD::KT, k1 = min(a.K, ke * GD::KT);
+        GemmArgs b = a;
+        // The tile code's per-lane offsets depend only on the leading
+        // dimensions and the lane; hidden from the compiler here, they are
+        // recomputed per piece instead of being hoisted out of the loop and
+        // held in registers across it (which spilled).
+        b.lda = opaque(a.lda);
+        b.ldb = opaque(a.ldb);
+        b.ldc = opaque(a.ldc);
+        b.A = a.A + (int64_t)m0 * a.lda + k0;
+        b.B = TRANS_B ? a.B + (int64_t)n0 * a.ldb + k0 : a.B + (int64_t)k0 * a.ldb + n0;
+        b.M = a.M - m0;
+        b.N = a.N - n0;
+        b.K = k1 - k0;
+        if (kb == 0 && ke == iters) {
+            b.C = a.C + (int64_t)m0 * a.ldc + n0;
+        } else {
+            b.C = sk.ws + (int64_t)(2 * w + (it == first ? 0 : 1)) * (GD::BM * GD::BN);
+            b.ldc = GD::BN;
+            b.alpha = 1.0f;
+            b.beta = 0.0f;
+        }
+        if (it != first)
+            __syncthreads();  // the previous piece's last LDS reads are done
+        mfma_tile<GD, GR, TRANS_B, VEC>(b, smem, 0, 0);
+        it += ke - kb;
+    }
+}
+
+// Stream-K fix-up: workgroup (j, y) completes rows [16y, 16y + 16) of the j-th
+// stream-K tile when more than one worker shared it, adding the pieces in
+// worker (= k) order: C <- alpha * sum + beta * C (C not read when beta == 0).
+// Worker w's range starts at floor(w*S/P), so the worker holding iteration x
+// is floor(((x + 1)*P - 1) / S); its piece of tile j sits in slot 0 if the
+// range starts inside or at the start of the tile, else in slot 1.
+template <int BM, int BN, bool VEC>
+__global__ __launch_bounds__(256) void sgemm_sk_fixup_kernel(GemmArgs a, SkArgs sk)
+{
+    constexpr int ROWS = 16, C4 = BN / 4, RPP = 256 / C4;
+    const int j = blockIdx.x, iters = sk.iters, P = sk.workers;
+    const int64_t S = (int64_t)sk.sk_tiles * iters;
+    const int64_t lo = (int64_t)j * iters, hi = lo + iters - 1;
+    const int w_lo = (int)(((lo + 1) * P - 1) / S), w_hi = (int)(((hi + 1) * P - 1) / S);
+    if (w_lo == w_hi)
+        return;  // one worker covered the tile and wrote C itself
+    const int nbm = (a.M + BM - 1) / BM, nbn = (a.N + BN - 1) / BN;
+    int tm, tn;
+    group_order(sk.dp + j, nbm, nbn, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int c = 4 * (threadIdx.x % C4);
+    const int col = n0 + c;
+    if (col >= a.N)
+        return;
+    const bool vec = VEC && col + 4 <= a.N;
+#pragma unroll
+    for (int pass = 0; pass < ROWS / RPP; ++pass) {
+        const int r = blockIdx.y * ROWS + pass * RPP + (int)threadIdx.x / C4;
+        const int row = m0 + r;
+        if (row >= a.M)
+            continue;
+        f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int w = w_lo; w <= w_hi; ++w) {
+            const int slot = 2 * w + (lo <= (int64_t)w * S / P ? 0 : 1);
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(sk.ws + (int64_t)slot * (BM * BN) + r * BN + c);
+            sum += v;
+        }
+        float *cp = a.C + (int64_t)row * a.ldc + col;
+        if (vec) {
+            f32x4 o = a.alpha * sum;
+            if (a.beta != 0.0f) {
+                const f32x4 old = *reinterpret_cast<const f32x4 *>(cp);
+                for (int e = 0; e < 4; ++e)
+                    o[e] = fmaf(a.alpha, sum[e], a.beta * old[e]);
+            }
+            *reinterpret_cast<f32x4 *>(cp) = o;
+        } else {
+            for (int e = 0; e < 4 && col + e < a.N; ++e)
+                cp[e] = a.beta != 0.0f ? fmaf(a.alpha, sum[e], a.beta * cp[e]) : a.alpha * sum[e];
+        }
+    }
 }
 
 TileShape tile_shape(int kid)
@@ -774,6 +941,54 @@ static void launch_cfg(const GemmArgs &a, bool transB, bool vec, hipStream_t str
         else
             sgemm_mfma_kernel<GDN, GRN, false, false><<<grid, block, 0, stream>>>(a);
     }
+}
+
+template <int BM, int BN, int BKD, int BKR, int WGM, int WGN, int OCC, int KS>
+static void launch_sk_cfg(const GemmArgs &a, const SkArgs &sk, bool transB, bool vec, hipStream_t stream)
+{
+    const dim3 grid((unsigned)(sk.dp + sk.workers)), block(64 * WGM * WGN * KS);
+    typedef Geo<BM, BN, BKD, WGM, WGN, OCC, true, KS, true> GDT;
+    typedef Geo<BM, BN, BKR, WGM, WGN, OCC, true, KS, true> GRT;
+    typedef Geo<BM, BN, BKD, WGM, WGN, OCC, false, KS, true> GDN;
+    typedef Geo<BM, BN, BKR, WGM, WGN, OCC, false, KS, true> GRN;
+    if (transB) {
+        if (vec)
+            sgemm_mfma_sk_kernel<GDT, GRT, true, true><<<grid, block, 0, stream>>>(a, sk);
+        else
+            sgemm_mfma_sk_kernel<GDT, GRT, true, false><<<grid, block, 0, stream>>>(a, sk);
+    } else {
+        if (vec)
+            sgemm_mfma_sk_kernel<GDN, GRN, false, true><<<grid, block, 0, stream>>>(a, sk);
+        else
+            sgemm_mfma_sk_kernel<GDN, GRN, false, false><<<grid, block, 0, stream>>>(a, sk);
+    }
+    if (sk.sk_tiles > 0) {
+        const dim3 fgrid((unsigned)sk.sk_tiles, BM / 16);
+        const bool cvec = (reinterpret_cast<uintptr_t>(a.C) & 15) == 0 && (a.ldc & 3) == 0;
+        if (cvec)
+            sgemm_sk_fixup_kernel<BM, BN, true><<<fgrid, dim3(256), 0, stream>>>(a, sk);
+        else
+            sgemm_sk_fixup_kernel<BM, BN, false><<<fgrid, dim3(256), 0, stream>>>(a, sk);
+    }
+}
+
+int mfma_stage_k(int kid)
+{
+    switch (kid) {
+    case KID_MFMA_L: return 32;
+    case KID_MFMA_M: return 64;
+    default: return 0;
+    }
+}
+
+hipError_t launch_mfma_sk(const GemmArgs &a, const SkArgs &sk, int kid, bool transB, bool vec, hipStream_t stream)
+{
+    switch (kid) {
+    case KID_MFMA_L: launch_sk_cfg<256, 256, 32, 16, 4, 2, 2, 1>(a, sk, transB, vec, stream); break;
+    case KID_MFMA_M: launch_sk_cfg<128, 128, 32, 32, 2, 2, 2, 2>(a, sk, transB, vec, stream); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_mfma(const GemmArgs &a, int kid, bool transB, bool vec, hipStream_t stream, int splits)

@@ -263,6 +263,8 @@ const char *kernel_label(int kid)
     case KID_MFMA_L: return "mfma_256x256x32_w4x2";
     case KID_MFMA_M: return "mfma_128x128x32_w2x2_ks2";
     case KID_MFMA_S: return "mfma_64x64x32_w2x2";
+    case KID_MFMA_L_SK: return "mfma_256x256x32_w4x2_streamk";
+    case KID_MFMA_M_SK: return "mfma_128x128x32_w2x2_ks2_streamk";
     case KID_MFMA_LP_F16: return "mfma_lp_f16_256x256x32_w4x2";
     case KID_MFMA_LP_BF16: return "mfma_lp_bf16_256x256x32_w4x2";
     case KID_MFMA_LP_F16_S: return "mfma_lp_f16_64x64x32_w2x1";
@@ -440,6 +442,206 @@ int run_split(int64_t splits_req, int64_t M, int64_t N, int64_t K, float alpha, 
     return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
 }
 
+// ---- stream-K -------------------------------------------------------------
+
+constexpr int64_t kSkWorkers = 256;  // one stream-K workgroup per CU (both tiles hold a CU)
+
+struct SkPlan {
+    Plan base;             // the plain call's validation and plan
+    int kid = KID_NONE;    // KID_MFMA_L_SK or KID_MFMA_M_SK; KID_NONE: the plain path runs
+    int tile_kid = KID_NONE;
+    SkArgs sk = {};
+    int64_t bytes = 0;     // workspace: two slots per worker
+};
+
+// Schedule of the tile `kid` (KID_MFMA_L or KID_MFMA_M): the whole waves of
+// tiles run data-parallel, the remaining tiles (all of them when there are
+// fewer than 256) are shared out by k-iteration over up to 256 workers.
+SkPlan sk_schedule(const Plan &base, int kid, int64_t M, int64_t N, int64_t K)
+{
+    SkPlan sp;
+    sp.base = base;
+    sp.tile_kid = kid;
+    sp.kid = kid == KID_MFMA_L ? KID_MFMA_L_SK : KID_MFMA_M_SK;
+    const TileShape t = tile_shape(kid);
+    const int64_t tiles = ceil_div(M, t.bm) * ceil_div(N, t.bn);
+    const int64_t iters = ceil_div(K, (int64_t)mfma_stage_k(kid));
+    const int64_t rem = tiles % kSkWorkers;
+    const int64_t dp = tiles - rem;
+    const int64_t workers = rem == 0 ? 0 : (rem * iters < kSkWorkers ? rem * iters : kSkWorkers);
+    sp.sk.ws = nullptr;
+    sp.sk.dp = (int)dp;
+    sp.sk.sk_tiles = (int)rem;
+    sp.sk.workers = (int)workers;
+    sp.sk.iters = (int)iters;
+    sp.bytes = 2 * workers * t.bm * t.bn * (int64_t)sizeof(float);
+    sp.base.tiles_m = ceil_div(M, t.bm);
+    sp.base.tiles_n = ceil_div(N, t.bn);
+    return sp;
+}
+
+// Modelled times in microseconds.  The plain call runs at its tile model's
+// rate; the stream-K schedule keeps every CU busy at the tile's own rate on
+// the padded tile area (143 TFLOP/s for 256 x 256, 133 for 128 x 128, as
+// measured under stream-K on MI355X), plus the fix-up: 6 us of launch and
+// tail, and every piece written and read back once at ~5 TB/s.  On the 24
+// shapes of the tile sweep the choice this makes between the plain call and
+// the two stream-K tiles came within 1.5% of the fastest every time.
+double plain_time_us(int64_t M, int64_t N, int64_t K)
+{
+    const int kid = choose_mfma(M, N);
+    return 2.0 * (double)M * (double)N * (double)K / (mfma_rate(kid, M, N) * 1e6);
+}
+
+double sk_time_us(const SkPlan &sp, int64_t K)
+{
+    const TileShape t = tile_shape(sp.tile_kid);
+    const double tiles = (double)(sp.base.tiles_m * sp.base.tiles_n);
+    const double rate = sp.tile_kid == KID_MFMA_L ? 143.0 : 133.0;
+    const double compute = tiles * t.bm * t.bn * 2.0 * (double)K / (rate * 1e6);
+    const double pieces = sp.sk.sk_tiles > 0 ? (double)(sp.sk.workers + sp.sk.sk_tiles) : 0.0;
+    const double fix = pieces > 0 ? 6.0 + pieces * t.bm * t.bn * 4.0 * 2.0 / 5e6 : 0.0;
+    return compute + fix;
+}
+
+// tile_req: 0 = the faster modelled tile, 256 or 128 = that tile.
+SkPlan make_sk_plan(int tile_req, int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
+                    const float *B, int64_t ldb, int transB, float beta, const float *C, int64_t ldc)
+{
+    const Plan base = make_plan(SGEMM_ALGO_AUTO, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc);
+    SkPlan sp;
+    sp.base = base;
+    if (tile_req != 0 && tile_req != 256 && tile_req != 128) {
+        sp.base.status = SGEMM_ERR_INVALID_VALUE;
+        sp.base.kid = KID_NONE;
+        return sp;
+    }
+    const bool mfma = base.kid == KID_MFMA_L || base.kid == KID_MFMA_M || base.kid == KID_MFMA_S;
+    if (base.status != SGEMM_OK || !mfma)
+        return sp;  // errors, quick returns and the product-free cases are the plain call's
+    if (tile_req == 256)
+        sp = sk_schedule(base, KID_MFMA_L, M, N, K);
+    else if (tile_req == 128)
+        sp = sk_schedule(base, KID_MFMA_M, M, N, K);
+    else {
+        const SkPlan l = sk_schedule(base, KID_MFMA_L, M, N, K), m = sk_schedule(base, KID_MFMA_M, M, N, K);
+        sp = sk_time_us(l, K) <= sk_time_us(m, K) ? l : m;
+    }
+    const int64_t blocks = (int64_t)sp.sk.dp + sp.sk.workers;
+    if (blocks * threads_per_block(sp.tile_kid) > kMaxWorkItems || blocks == 0) {
+        sp.base.status = SGEMM_ERR_INVALID_VALUE;
+        sp.kid = KID_NONE;
+        sp.base.kid = KID_NONE;
+    }
+    return sp;
+}
+
+// Workspace checks shared by the stream-K and k-split calls.
+int check_workspace(const void *ws, int64_t ws_bytes, int64_t need, int64_t M, int64_t N, int64_t K,
+                    const float *A, int64_t lda, const float *B, int64_t ldb, int transB, const float *C,
+                    int64_t ldc)
+{
+    if (ws == nullptr || ws_bytes < need)
+        return SGEMM_ERR_INVALID_VALUE;
+    const int64_t a_bytes = span_bytes(M, K, lda);
+    const int64_t b_bytes = span_bytes(transB ? N : K, transB ? K : N, ldb);
+    const int64_t c_bytes = span_bytes(M, N, ldc);
+    if (overlaps(ws, need, A, a_bytes) || overlaps(ws, need, B, b_bytes) || overlaps(ws, need, C, c_bytes))
+        return SGEMM_ERR_ALIAS;
+    return SGEMM_OK;
+}
+
+int launch_sk_plan(const SkPlan &sp, int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
+                   const float *B, int64_t ldb, float beta, float *C, int64_t ldc, void *ws, void *stream)
+{
+    const int dev_status = check_device();
+    if (dev_status != SGEMM_OK)
+        return dev_status;
+    GemmArgs a;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.lda = lda;
+    a.ldb = ldb;
+    a.ldc = ldc;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.alpha = alpha;
+    a.beta = beta;
+    const int64_t off_limit = ((int64_t)1 << 31) / 256;
+    a.flags = (lda < off_limit && ldb < off_limit) ? GEMM_FLAG_DIRECT : 0;
+    a.k_split = 0;
+    a.c_split_stride = 0;
+    SkArgs sk = sp.sk;
+    sk.ws = static_cast<float *>(ws);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    const hipError_t e = launch_mfma_sk(a, sk, sp.tile_kid, sp.base.transB, sp.base.vec, s);
+    return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
+}
+
+int run_sk(int tile_req, int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
+           const float *B, int64_t ldb, int transB, float beta, float *C, int64_t ldc, void *ws, int64_t ws_bytes,
+           void *stream)
+{
+    if (ws_bytes < 0)
+        return SGEMM_ERR_INVALID_VALUE;
+    const SkPlan sp = make_sk_plan(tile_req, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc);
+    if (sp.base.status != SGEMM_OK)
+        return sp.base.status;
+    if (sp.kid == KID_NONE)
+        return run(SGEMM_ALGO_AUTO, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, stream);
+    const int ws_status = check_workspace(ws, ws_bytes, sp.bytes, M, N, K, A, lda, B, ldb, transB, C, ldc);
+    if (ws_status != SGEMM_OK && sp.bytes > 0)
+        return ws_status;
+    return launch_sk_plan(sp, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, ws, stream);
+}
+
+// What sgemm_f32_ws does: the k-split when its rule splits; otherwise stream-K
+// when the model puts it at least 1% ahead of the plain call; otherwise the
+// plain call.  `method`: 0 plain, 1 k-split, 2 stream-K.
+struct WsChoice {
+    int method = 0;
+    SplitPlan split;
+    SkPlan sk;
+};
+
+WsChoice ws_auto(int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda, const float *B,
+                 int64_t ldb, int transB, float beta, const float *C, int64_t ldc)
+{
+    WsChoice c;
+    c.split = make_split_plan(0, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, nullptr, 0, false);
+    if (c.split.base.status != SGEMM_OK)
+        return c;
+    if (c.split.splits > 1) {
+        c.method = 1;
+        return c;
+    }
+    c.sk = make_sk_plan(0, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc);
+    if (c.sk.base.status == SGEMM_OK && c.sk.kid != KID_NONE && c.sk.sk.sk_tiles > 0 &&
+        sk_time_us(c.sk, K) < 0.99 * plain_time_us(M, N, K))
+        c.method = 2;
+    return c;
+}
+
+int run_ws_auto(int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda, const float *B,
+                int64_t ldb, int transB, float beta, float *C, int64_t ldc, void *ws, int64_t ws_bytes, void *stream)
+{
+    if (ws_bytes < 0)
+        return SGEMM_ERR_INVALID_VALUE;
+    const WsChoice c = ws_auto(M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc);
+    if (c.method == 2) {
+        const int st = check_workspace(ws, ws_bytes, c.sk.bytes, M, N, K, A, lda, B, ldb, transB, C, ldc);
+        if (st == SGEMM_ERR_ALIAS)
+            return st;
+        if (st == SGEMM_OK)
+            return launch_sk_plan(c.sk, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, ws, stream);
+        return run(SGEMM_ALGO_AUTO, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, stream);
+    }
+    return run_split(0, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, ws, ws_bytes, stream);
+}
+
 // Mixed precision: the FP32 call's validation and quick returns; the product
 // runs the 16-bit MFMA kernel.
 Plan make_lowp_plan(int precision, int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
@@ -582,8 +784,58 @@ int sgemm_f32_ws(int64_t M, int64_t N, int64_t K, float alpha, const float *A, i
                  int64_t ldb, int transB, float beta, float *C, int64_t ldc, void *workspace,
                  int64_t workspace_bytes, void *stream)
 {
-    return sgemm::run_split(0, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, workspace, workspace_bytes,
-                            stream);
+    return sgemm::run_ws_auto(M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, workspace, workspace_bytes,
+                              stream);
+}
+
+int sgemm_f32_ws_plan(int64_t M, int64_t N, int64_t K, int transB, int *method, int *kernel_id,
+                      int64_t *workspace_bytes)
+{
+    const float *A = reinterpret_cast<const float *>((uintptr_t)1 << 40);
+    const float *B = reinterpret_cast<const float *>((uintptr_t)1 << 50);
+    const float *C = reinterpret_cast<const float *>((uintptr_t)1 << 58);
+    const int64_t lda = K > 1 ? K : 1, ldc = N > 1 ? N : 1;
+    const int64_t ldb = transB == 1 ? lda : ldc;
+    const sgemm::WsChoice c = sgemm::ws_auto(M, N, K, 1.0f, A, lda, B, ldb, transB, 0.0f, C, ldc);
+    const int st = c.split.base.status;
+    if (method)
+        *method = st == SGEMM_OK ? c.method : 0;
+    if (kernel_id)
+        *kernel_id = c.method == 2 ? c.sk.kid : c.split.kid;
+    if (workspace_bytes)
+        *workspace_bytes = c.method == 2 ? c.sk.bytes : (c.method == 1 ? c.split.bytes : 0);
+    return st;
+}
+
+int sgemm_f32_streamk_plan(int tile, int64_t M, int64_t N, int64_t K, int transB, int *kernel_id,
+                           int64_t *dp_tiles, int64_t *sk_tiles, int64_t *workers, int64_t *workspace_bytes)
+{
+    const float *A = reinterpret_cast<const float *>((uintptr_t)1 << 40);
+    const float *B = reinterpret_cast<const float *>((uintptr_t)1 << 50);
+    const float *C = reinterpret_cast<const float *>((uintptr_t)1 << 58);
+    const int64_t lda = K > 1 ? K : 1, ldc = N > 1 ? N : 1;
+    const int64_t ldb = transB == 1 ? lda : ldc;
+    const sgemm::SkPlan sp = sgemm::make_sk_plan(tile, M, N, K, 1.0f, A, lda, B, ldb, transB, 0.0f, C, ldc);
+    const bool sk = sp.base.status == SGEMM_OK && sp.kid != sgemm::KID_NONE;
+    if (kernel_id)
+        *kernel_id = sk ? sp.kid : sp.base.kid;
+    if (dp_tiles)
+        *dp_tiles = sk ? sp.sk.dp : 0;
+    if (sk_tiles)
+        *sk_tiles = sk ? sp.sk.sk_tiles : 0;
+    if (workers)
+        *workers = sk ? sp.sk.workers : 0;
+    if (workspace_bytes)
+        *workspace_bytes = sk ? sp.bytes : 0;
+    return sp.base.status;
+}
+
+int sgemm_f32_streamk(int tile, int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
+                      const float *B, int64_t ldb, int transB, float beta, float *C, int64_t ldc, void *workspace,
+                      int64_t workspace_bytes, void *stream)
+{
+    return sgemm::run_sk(tile, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, workspace, workspace_bytes,
+                         stream);
 }
 
 int sgemm_f32_splitk(int64_t splits, int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,

@@ -23,6 +23,24 @@ struct GemmArgs {
     int64_t c_split_stride;
 };
 
+// Stream-K schedule of one MFMA launch over a T-tile grid whose tiles each
+// take `iters` k-iterations (one LDS stage of k each).  The first `dp`
+// workgroups take one whole tile each, as the plain kernel does; the next
+// `workers` workgroups share the k-iterations of the remaining sk_tiles
+// tiles, worker w taking iterations [w*S/workers, (w+1)*S/workers) of the
+// S = sk_tiles*iters that follow the data-parallel tiles.  A worker writes a
+// tile it covers whole straight into C; a piece of a tile goes into one of
+// its two workspace slots (slot 0 for its first piece, 1 for its last), each
+// BM x BN floats with row pitch BN, and the fix-up kernel adds a split tile's
+// pieces in worker order and applies the epilogue.
+struct SkArgs {
+    float *ws;
+    int dp;
+    int workers;
+    int sk_tiles;
+    int iters;
+};
+
 // The MFMA kernel may stage interior tiles with direct global->LDS loads, whose
 // per-lane source offsets are 32-bit: set when 256 rows of A (and of B) span
 // fewer than 2^31 elements.
@@ -40,6 +58,8 @@ enum KernelId : int {
     KID_MFMA_L = 40,        // 256 x 256 macro tile, 8 wavefronts
     KID_MFMA_M = 41,        // 128 x 128, 8 wavefronts: 2 x 2 over the tile x 2 over k
     KID_MFMA_S = 42,        // 64 x 64, 4 wavefronts
+    KID_MFMA_L_SK = 43,     // KID_MFMA_L under a stream-K schedule (+ fix-up kernel)
+    KID_MFMA_M_SK = 44,     // KID_MFMA_M under a stream-K schedule (+ fix-up kernel)
     KID_MFMA_LP_F16 = 60,   // mixed precision, operands rounded to fp16, 256 x 256
     KID_MFMA_LP_BF16 = 61,  // the same with bf16
     KID_MFMA_LP_F16_S = 62, // mixed precision, fp16, 64 x 64 (few output tiles)
@@ -59,6 +79,11 @@ hipError_t launch_naive_wg(const GemmArgs &a, bool transB, hipStream_t stream);
 hipError_t launch_tiled(const GemmArgs &a, bool transB, bool pad, hipStream_t stream);
 hipError_t launch_regblock(const GemmArgs &a, bool transB, bool vec, hipStream_t stream);
 hipError_t launch_mfma(const GemmArgs &a, int kid, bool transB, bool vec, hipStream_t stream, int splits = 1);
+// Stream-K launch of the 256 x 256 (KID_MFMA_L) or 128 x 128 (KID_MFMA_M)
+// tile, then the fix-up of its split tiles (nothing when sk.sk_tiles == 0).
+// `iters` must be ceil(K / mfma_stage_k(kid)).
+hipError_t launch_mfma_sk(const GemmArgs &a, const SkArgs &sk, int kid, bool transB, bool vec, hipStream_t stream);
+int mfma_stage_k(int kid);
 // Mixed precision: operands rounded to fp16 (bf16 = false) or bf16 while staged.
 hipError_t launch_mfma_lp(const GemmArgs &a, bool large, bool bf16, bool transB, bool vec, hipStream_t stream);
 TileShape lp_tile_shape(bool large);

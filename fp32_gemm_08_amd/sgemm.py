@@ -32,8 +32,9 @@ PRECISION = {"fp16": 1, "bf16": 2}
 
 EXPORTS = ("sgemm_f32", "sgemm_f32_algo", "sgemm_f32_lowp", "sgemm_f32_lowp_plan", "sgemm_f32_plan",
            "sgemm_f32_splitk", "sgemm_f32_splitk_plan",
-           "sgemm_f32_status_string", "sgemm_f32_transpose", "sgemm_f32_transpose_algo",
-           "sgemm_f32_transpose_plan", "sgemm_f32_version", "sgemm_f32_ws")
+           "sgemm_f32_status_string", "sgemm_f32_streamk", "sgemm_f32_streamk_plan", "sgemm_f32_transpose",
+           "sgemm_f32_transpose_algo", "sgemm_f32_transpose_plan", "sgemm_f32_version", "sgemm_f32_ws",
+           "sgemm_f32_ws_plan")
 
 _lock = threading.Lock()
 _lib = None
@@ -79,6 +80,14 @@ def load():
         lib.sgemm_f32_splitk_plan.restype = ci
         lib.sgemm_f32_splitk_plan.argtypes = [i64, i64, i64, i64, ci, ctypes.POINTER(i64), ctypes.POINTER(ci),
                                               ctypes.POINTER(i64)]
+        lib.sgemm_f32_ws_plan.restype = ci
+        lib.sgemm_f32_ws_plan.argtypes = [i64, i64, i64, ci, ctypes.POINTER(ci), ctypes.POINTER(ci),
+                                          ctypes.POINTER(i64)]
+        lib.sgemm_f32_streamk.restype = ci
+        lib.sgemm_f32_streamk.argtypes = [ci] + ws_args
+        lib.sgemm_f32_streamk_plan.restype = ci
+        lib.sgemm_f32_streamk_plan.argtypes = [ci, i64, i64, i64, ci, ctypes.POINTER(ci), ctypes.POINTER(i64),
+                                               ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64)]
         tr_args = [i64, i64, vp, i64, vp, i64, vp]
         lib.sgemm_f32_transpose.restype = ci
         lib.sgemm_f32_transpose.argtypes = tr_args
@@ -155,6 +164,33 @@ def sgemm_f32_splitk_plan(splits, M, N, K, transB=0):
     return st, su.value, kid.value, nb.value
 
 
+def sgemm_f32_ws_plan(M, N, K, transB=0):
+    """Host-only query of what sgemm_f32_ws does: (status, method, kernel_id,
+    workspace_bytes); method 0 = plain, 1 = k-split, 2 = stream-K."""
+    method = ctypes.c_int(0)
+    kid = ctypes.c_int(0)
+    nb = ctypes.c_int64(0)
+    st = load().sgemm_f32_ws_plan(M, N, K, transB, ctypes.byref(method), ctypes.byref(kid), ctypes.byref(nb))
+    return st, method.value, kid.value, nb.value
+
+
+def sgemm_f32_streamk(tile, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, workspace, workspace_bytes,
+                      stream=0) -> int:
+    """C <- alpha*A*op(B) + beta*C under a stream-K schedule (tile 0 = the
+    library's choice, 256 or 128).  Returns the status code."""
+    return load().sgemm_f32_streamk(tile, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, workspace,
+                                    workspace_bytes, stream)
+
+
+def sgemm_f32_streamk_plan(tile, M, N, K, transB=0):
+    """Host-only query: (status, kernel_id, dp_tiles, sk_tiles, workers, workspace_bytes)."""
+    kid = ctypes.c_int(0)
+    dp, skt, wk, nb = (ctypes.c_int64(0) for _ in range(4))
+    st = load().sgemm_f32_streamk_plan(tile, M, N, K, transB, ctypes.byref(kid), ctypes.byref(dp), ctypes.byref(skt),
+                                       ctypes.byref(wk), ctypes.byref(nb))
+    return st, kid.value, dp.value, skt.value, wk.value, nb.value
+
+
 def sgemm_f32_transpose(rows, cols, src, ld_src, dst, ld_dst, stream=0) -> int:
     """dst <- src^T (AUTO algorithm).  Returns the status code."""
     return load().sgemm_f32_transpose(rows, cols, src, ld_src, dst, ld_dst, stream)
@@ -210,7 +246,7 @@ def _ld(t):
 
 
 def gemm(A, B, C, alpha=1.0, beta=0.0, trans_b=False, algo="auto", stream=None, workspace=None, splits=0,
-         precision=None):
+         precision=None, streamk=None):
     """C <- alpha*A*op(B) + beta*C on torch float32 CUDA tensors, in place; returns C.
 
     A is (M, K), B is (K, N) or, with trans_b, (N, K); C is (M, N).  Each may be a
@@ -218,7 +254,8 @@ def gemm(A, B, C, alpha=1.0, beta=0.0, trans_b=False, algo="auto", stream=None, 
     dimension.  Runs on ``stream`` (a torch stream) or torch's current stream.
     With ``workspace`` (a contiguous device tensor) the product may split k over
     several workgroups per tile (``splits`` = 0: the library's choice, else that
-    count; ``algo`` is then not used).  With ``precision`` ("fp16" or "bf16")
+    count; ``algo`` is then not used; ``streamk`` = 0, 256 or 128 runs the
+    stream-K schedule with the library's tile or that one).  With ``precision`` ("fp16" or "bf16")
     the operands are rounded to that format and multiplied by the 16-bit matrix
     cores with FP32 sums (sgemm_f32_lowp).
     """
@@ -248,7 +285,12 @@ def gemm(A, B, C, alpha=1.0, beta=0.0, trans_b=False, algo="auto", stream=None, 
             nbytes = workspace.numel() * workspace.element_size()
             args = (M, N, K, float(alpha), A.data_ptr(), ld(A), B.data_ptr(), ld(B), int(bool(trans_b)),
                     float(beta), C.data_ptr(), ld(C), workspace.data_ptr(), nbytes, s)
-            st = sgemm_f32_splitk(int(splits), *args) if splits else sgemm_f32_ws(*args)
+            if streamk is not None:
+                st = sgemm_f32_streamk(int(streamk), *args)
+            elif splits:
+                st = sgemm_f32_splitk(int(splits), *args)
+            else:
+                st = sgemm_f32_ws(*args)
     _check(st)
     return C
 

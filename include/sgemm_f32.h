@@ -304,9 +304,10 @@ int sgemm_f32_splitk_plan(int64_t splits, int64_t M, int64_t N, int64_t K, int t
                           int64_t *splits_used, int *kernel_id, int64_t *workspace_bytes);
 
 /*
- * sgemm_f32 with a workspace: splits k as sgemm_f32_splitk_plan(0, ...) reports
- * when workspace_bytes is at least the size it reports; otherwise (including
- * workspace == NULL) it runs exactly as sgemm_f32.
+ * sgemm_f32 with a workspace: runs the k-split or the stream-K schedule below
+ * as sgemm_f32_ws_plan reports, when workspace_bytes is at least the size it
+ * reports; otherwise (including workspace == NULL) it runs exactly as
+ * sgemm_f32.
  */
 int sgemm_f32_ws(int64_t M, int64_t N, int64_t K, float alpha,
                  const float *A, int64_t lda, const float *B, int64_t ldb, int transB,
@@ -322,6 +323,56 @@ int sgemm_f32_splitk(int64_t splits, int64_t M, int64_t N, int64_t K, float alph
                      const float *A, int64_t lda, const float *B, int64_t ldb, int transB,
                      float beta, float *C, int64_t ldc,
                      void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * Stream-K.  With T output tiles and 256 CUs, a plain launch runs ceil(T/256)
+ * waves of tiles and leaves CUs idle in the last one (T = 324 tiles of
+ * 256 x 256 keep only 68 CUs busy in their second wave).  The stream-K
+ * schedule (Osama et al., "Stream-K: Work-centric Parallel Decomposition for
+ * Dense Matrix-Matrix Multiplication on the GPU") keeps the whole waves as
+ * they are and deals the k-iterations of the remaining tiles (all of them when
+ * T < 256) out evenly over up to 256 workgroups, each a contiguous run that may
+ * start and end inside a tile.  A workgroup that covers a whole tile writes it
+ * to C; every other piece of a tile is a raw FP32 partial product in the
+ * workspace, and a fix-up kernel adds a tile's pieces in k order and applies
+ * C <- alpha * sum + beta*C (C not read when beta == 0).  The operation, its
+ * accuracy contract and its determinism are those of the k-split above (a
+ * sum of K products split into partial sums, in a fixed order).
+ *
+ * `tile`: 0 = the library's choice from its cost model, 256 = the 256 x 256
+ * tile, 128 = the 128 x 128 tile (anything else: SGEMM_ERR_INVALID_VALUE).
+ * Workspace: a DEVICE buffer owned by the caller, at least
+ * 2 * workers * tile_rows * tile_cols * 4 bytes (sgemm_f32_streamk_plan
+ * reports it; 0 when T is a multiple of 256 and the schedule is the plain
+ * one), with the same rules as the k-split workspace (any contents, not
+ * overlapping A, B or C, ordered on one stream).  Too small: SGEMM_ERR_INVALID_VALUE.
+ * Quick returns, product-free cases and argument errors are sgemm_f32's.
+ */
+int sgemm_f32_streamk(int tile, int64_t M, int64_t N, int64_t K, float alpha,
+                      const float *A, int64_t lda, const float *B, int64_t ldb, int transB,
+                      float beta, float *C, int64_t ldc,
+                      void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * Host-only query for sgemm_f32_streamk: the kernel id (43: 256 x 256
+ * stream-K, 44: 128 x 128 stream-K; the plain call's id for quick returns and
+ * product-free cases), the tiles run data-parallel, the tiles shared out, the
+ * stream-K workgroups and the workspace bytes.  Output pointers may be NULL.
+ */
+int sgemm_f32_streamk_plan(int tile, int64_t M, int64_t N, int64_t K, int transB, int *kernel_id,
+                           int64_t *dp_tiles, int64_t *sk_tiles, int64_t *workers,
+                           int64_t *workspace_bytes);
+
+/*
+ * Host-only query of what sgemm_f32_ws does with a large enough workspace:
+ * *method = 1 (k-split) when sgemm_f32_splitk_plan(0, ...) splits; otherwise
+ * 2 (stream-K) when the library's cost model expects stream-K to be at least
+ * 1% faster than the plain call; otherwise 0 (plain).  Also the kernel id and
+ * the workspace bytes that method needs (0 for the plain call).  With a
+ * smaller workspace sgemm_f32_ws runs the plain call.
+ */
+int sgemm_f32_ws_plan(int64_t M, int64_t N, int64_t K, int transB, int *method, int *kernel_id,
+                      int64_t *workspace_bytes);
 
 /* Static, NUL-terminated text for a status code (unknown codes included). */
 const char *sgemm_f32_status_string(int status);
