@@ -512,14 +512,15 @@ def main():
     ap.add_argument("--op", choices=("gemm", "transpose", "splitk"), default="gemm",
                     help="splitk: table of the k-split path over split counts (no JSON line)")
     ap.add_argument("--config", default="c4_4096",
-                    help="workload name (GEMM: c1_128 ... c5_tall; transpose: t_4096 ...)")
+                    help="workload name (GEMM: c1_128 ... c5_tall, k_* long-k, s_* stream-K; transpose: t_4096 ...)")
     ap.add_argument("--algo", default="auto")
     ap.add_argument("--precision", choices=("fp32", "fp16", "bf16"), default="fp32",
                     help="GEMM: fp16/bf16 run sgemm_f32_lowp (operands rounded to that format, FP32 sums), "
                          "reported against the dense fp16/bf16 matrix-core peak")
     ap.add_argument("--workspace", action="store_true",
-                    help="GEMM: call sgemm_f32_ws with the workspace its plan asks for (k-split when the "
-                         "output tiles are too few; a step is then the partial pass plus the reduction)")
+                    help="GEMM: call sgemm_f32_ws with the workspace its plan asks for (k-split when the output tiles "
+                         "are too few, stream-K when their last wave is partial; a step then includes the "
+                         "reduction or fix-up kernel)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -590,12 +591,20 @@ def main():
         if st != 0:
             raise SystemExit(f"plan failed: {lib.sgemm_f32_status_string(st)}")
     if args.workspace and not lowp:
-        _, splits, skid, ws_bytes = lib.sgemm_f32_splitk_plan(0, M, N, K, int(case.trans_b))
-        if splits > 1:
+        _, method, wkid, ws_bytes = lib.sgemm_f32_ws_plan(M, N, K, int(case.trans_b))
+        if method == 1:
+            _, splits, skid, ws_bytes = lib.sgemm_f32_splitk_plan(0, M, N, K, int(case.trans_b))
             ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device=dev)
             kid = skid
             kname = f"k-split x{splits}: mfma_64x64x32_w2x2 partial pass + splitk_reduce"
             tm, tn = -(-M // 64) * splits, -(-N // 64)
+        elif method == 2:
+            _, kid, dp, skt, wk, ws_bytes = lib.sgemm_f32_streamk_plan(0, M, N, K, int(case.trans_b))
+            ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device=dev)
+            tile = 256 if kid == 43 else 128
+            kname = (f"stream-K {tile}x{tile}: {dp} data-parallel tiles + {skt} tiles over {wk} workgroups "
+                     f"+ sk_fixup")
+            tm, tn = dp + wk, 1
 
     def step():
         if lowp:
@@ -634,7 +643,7 @@ def main():
     value = K_steps * flop / wall / 1e12
     kern_avg = span / K_steps
     achieved = flop / kern_avg / 1e12
-    mfma = kid in (40, 41, 42, 60, 61, 62, 63)
+    mfma = kid in (40, 41, 42, 43, 44, 60, 61, 62, 63)
     peak = HALF_MFMA_PEAK_TFLOPS if lowp else FP32_MFMA_PEAK_TFLOPS if mfma else FP32_VALU_PEAK_TFLOPS
     log(f"{'step (both kernels)' if ws is not None else 'kernel'} {kname}: avg {kern_avg * 1e3:.4f} ms "
         f"over {K_steps} calls "

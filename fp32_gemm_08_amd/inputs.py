@@ -43,6 +43,15 @@ SPLITK_CONFIGS = {
     "k_64x64x65536": dict(M=64, N=64, K=65536, trans_b=False, alpha=1.0, beta=0.0, dist="uniform", seed=33),
 }
 
+# Products whose tile grid ends in a partial wave on 256 CUs (4608^3: 324
+# tiles of 256 x 256), where a caller workspace lets the stream-K schedule
+# share the last tiles' k-iterations over every CU.
+STREAMK_CONFIGS = {
+    "s_4608": dict(M=4608, N=4608, K=4608, trans_b=False, alpha=1.0, beta=0.0, dist="uniform", seed=51),
+    "s_2304x2304x8192": dict(M=2304, N=2304, K=8192, trans_b=False, alpha=1.0, beta=0.0, dist="uniform", seed=52),
+    "s_3584_bt": dict(M=3584, N=3584, K=3584, trans_b=True, alpha=1.0, beta=1.0, dist="normal", seed=53),
+}
+
 
 @dataclass
 class Case:
@@ -112,7 +121,8 @@ def make_case(M, N, K, trans_b=False, alpha=1.0, beta=0.0, dist="uniform", seed=
 
 
 def make_config(name: str, **overrides) -> Case:
-    p = dict(CONFIGS[name] if name in CONFIGS else SPLITK_CONFIGS[name])
+    table = CONFIGS if name in CONFIGS else SPLITK_CONFIGS if name in SPLITK_CONFIGS else STREAMK_CONFIGS
+    p = dict(table[name])
     p.update(overrides)
     c = make_case(**p)
     c.meta["config"] = name
