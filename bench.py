@@ -590,6 +590,17 @@ def main():
                                                          case.ldc)
         if st != 0:
             raise SystemExit(f"plan failed: {lib.sgemm_f32_status_string(st)}")
+    if args.workspace and lowp:
+        st, lkid, ltm, ltn, ws_bytes = lib.sgemm_f32_lowp_ws_plan(lib.PRECISION[args.precision], M, N, K,
+                                                                   int(case.trans_b))
+        if ws_bytes > 0:
+            ws = torch.empty(ws_bytes // 4 + 1, dtype=torch.float32, device=dev)
+            kid, tm, tn = lkid, ltm, ltn
+            _, _, _, _, kname = lib.sgemm_f32_lowp_plan(lib.PRECISION[args.precision], M, N, K, case.alpha, pa,
+                                                        case.lda, pb, case.ldb, int(case.trans_b), case.beta, pc,
+                                                        case.ldc)
+            tile = 256 if kid in (64, 65) else 128
+            kname = f"two passes: rounding into the workspace + lp16 {args.precision} {tile}x{tile} GEMM"
     if args.workspace and not lowp:
         _, method, wkid, ws_bytes = lib.sgemm_f32_ws_plan(M, N, K, int(case.trans_b))
         if method == 1:
@@ -607,7 +618,11 @@ def main():
             tm, tn = dp + wk, 1
 
     def step():
-        if lowp:
+        if lowp and ws is not None:
+            s = lib.sgemm_f32_lowp_ws(lib.PRECISION[args.precision], M, N, K, case.alpha, pa, case.lda, pb,
+                                      case.ldb, int(case.trans_b), case.beta, pc, case.ldc, ws.data_ptr(), ws_bytes,
+                                      sp)
+        elif lowp:
             s = lib.sgemm_f32_lowp(lib.PRECISION[args.precision], M, N, K, case.alpha, pa, case.lda, pb, case.ldb,
                                    int(case.trans_b), case.beta, pc, case.ldc, sp)
         elif ws is not None:
@@ -643,7 +658,7 @@ def main():
     value = K_steps * flop / wall / 1e12
     kern_avg = span / K_steps
     achieved = flop / kern_avg / 1e12
-    mfma = kid in (40, 41, 42, 43, 44, 60, 61, 62, 63)
+    mfma = kid in (40, 41, 42, 43, 44, 60, 61, 62, 63, 64, 65, 66, 67)
     peak = HALF_MFMA_PEAK_TFLOPS if lowp else FP32_MFMA_PEAK_TFLOPS if mfma else FP32_VALU_PEAK_TFLOPS
     log(f"{'step (both kernels)' if ws is not None else 'kernel'} {kname}: avg {kern_avg * 1e3:.4f} ms "
         f"over {K_steps} calls "

@@ -30,40 +30,15 @@
 //   op(B) = B (stored K x N): 8 quads of k x BN/4 quads of n; each work-item
 //     loads 4 (k) x 4 (n) blocks (4 x 128 bits along n), converts, and writes
 //     them transposed: 4 n-rows x 4 k values (8 bytes each).
-// Edge tiles and the k tail load with masks and zero fill; misaligned operands
-// (base not 16-byte aligned or leading dimension not a multiple of 4) load
-// element by element.
+// Edge tiles and the k tail load with masks and zero fill, element by element
+// only for the chunks that leave the matrix; misaligned operands (base not
+// 16-byte aligned or leading dimension not a multiple of 4) load element by
+// element.
 #include "sgemm_internal.h"
+#include "lp_types.h"
 
 namespace sgemm {
 namespace {
-
-typedef float lp_f32x4 __attribute__((ext_vector_type(4)));
-typedef float lp_f32x16 __attribute__((ext_vector_type(16)));
-typedef _Float16 lp_h8 __attribute__((ext_vector_type(8)));
-typedef __bf16 lp_b8 __attribute__((ext_vector_type(8)));
-typedef _Float16 lp_h4 __attribute__((ext_vector_type(4)));
-typedef __bf16 lp_b4 __attribute__((ext_vector_type(4)));
-
-template <bool BF16> struct Lp;
-template <> struct Lp<false> {
-    typedef _Float16 T;
-    typedef lp_h8 V8;
-    typedef lp_h4 V4;
-    static __device__ __forceinline__ lp_f32x16 mma(V8 a, V8 b, lp_f32x16 c)
-    {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-    }
-};
-template <> struct Lp<true> {
-    typedef __bf16 T;
-    typedef lp_b8 V8;
-    typedef lp_b4 V4;
-    static __device__ __forceinline__ lp_f32x16 mma(V8 a, V8 b, lp_f32x16 c)
-    {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-    }
-};
 
 constexpr int LBK = 32;
 constexpr int LP_PITCH = LBK + 8;                      // 16-bit values per LDS row
@@ -115,7 +90,7 @@ struct LpStage {
     template <bool MASKED>
     static __device__ __forceinline__ void load8(float (&dst)[8], const float *p, bool row_ok, int k, int K)
     {
-        if (!MASKED && VEC) {
+        if (VEC && (!MASKED || (row_ok && k + 8 <= K))) {  // masks only where the chunk leaves the matrix
             const lp_f32x4 x0 = *reinterpret_cast<const lp_f32x4 *>(p);
             const lp_f32x4 x1 = *reinterpret_cast<const lp_f32x4 *>(p + 4);
 #pragma unroll
@@ -157,7 +132,7 @@ struct LpStage {
                 for (int j = 0; j < 4; ++j) {
                     const int k = k0 + 4 * kq + j;
                     const float *p = g.B + (int64_t)k * g.ldb + n;
-                    if (!MASKED && VEC) {
+                    if (VEC && (!MASKED || (k < g.K && n + 4 <= g.N))) {
                         const lp_f32x4 x = *reinterpret_cast<const lp_f32x4 *>(p);
 #pragma unroll
                         for (int q = 0; q < 4; ++q)
@@ -339,10 +314,11 @@ __global__ __launch_bounds__(Gm::NT) void sgemm_mfma_lp_kernel(GemmArgs g)
 
 }  // namespace
 
-// Measured on MI355X (bf16, 4096^3 ... 1024^3): the 256 x 256 tile is fastest
-// once it gives every CU a workgroup; below that the 64 x 64 tile (2 wavefronts,
-// up to 8 workgroups per CU) is, by 2x at 2048^3 and 3x at 1024^3.  128 x 256
-// and 128 x 128 tiles never led by more than 15%.
+// Measured on MI355X (bf16, 8192^3 ... 512^3): the 256 x 256 tile is fastest
+// once it keeps at least half the CUs busy (3584^3: 618 TFLOP/s against 309);
+// below that the 64 x 64 tile (2 wavefronts, up to 8 workgroups per CU) is,
+// by 2x at 2048^3 and 3x at 1024^3.  128 x 256 and 128 x 128 tiles never led
+// by more than 15%.
 typedef LpGeo<256, 256, 4, 2> LpL;   // 8 wavefronts of 64 x 128
 typedef LpGeo<64, 64, 2, 1> LpS;     // 2 wavefronts of 32 x 64
 

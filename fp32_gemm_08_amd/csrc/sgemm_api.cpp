@@ -269,6 +269,10 @@ const char *kernel_label(int kid)
     case KID_MFMA_LP_BF16: return "mfma_lp_bf16_256x256x32_w4x2";
     case KID_MFMA_LP_F16_S: return "mfma_lp_f16_64x64x32_w2x1";
     case KID_MFMA_LP_BF16_S: return "mfma_lp_bf16_64x64x32_w2x1";
+    case KID_LP16_F16: return "lp16_f16_256x256x32_w4x2_s4 (+ rounding pass)";
+    case KID_LP16_BF16: return "lp16_bf16_256x256x32_w4x2_s4 (+ rounding pass)";
+    case KID_LP16_F16_S: return "lp16_f16_128x128x32_w2x2_s4 (+ rounding pass)";
+    case KID_LP16_BF16_S: return "lp16_bf16_128x128x32_w2x2_s4 (+ rounding pass)";
     case KID_TRANSPOSE_NAIVE: return "transpose_naive_64x16";
     case KID_TRANSPOSE_LDS_PAD: return "transpose_lds_128x128_pad1";
     case KID_TRANSPOSE_LDS_NOPAD: return "transpose_lds_128x128_pad0";
@@ -655,9 +659,9 @@ Plan make_lowp_plan(int precision, int64_t M, int64_t N, int64_t K, float alpha,
     Plan p = make_plan(SGEMM_ALGO_AUTO, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc);
     if (p.status != SGEMM_OK || !(p.kid == KID_MFMA_L || p.kid == KID_MFMA_M || p.kid == KID_MFMA_S))
         return p;
-    // the 256 x 256 tile once it gives every CU a workgroup, else 64 x 64
+    // the 256 x 256 tile once it keeps at least half of the 256 CUs busy, else 64 x 64
     const TileShape tl = lp_tile_shape(true);
-    const bool large = ceil_div(M, tl.bm) * ceil_div(N, tl.bn) >= 256;
+    const bool large = ceil_div(M, tl.bm) * ceil_div(N, tl.bn) >= 128;
     const bool bf16 = precision == SGEMM_PREC_BF16;
     p.kid = large ? (bf16 ? KID_MFMA_LP_BF16 : KID_MFMA_LP_F16) : (bf16 ? KID_MFMA_LP_BF16_S : KID_MFMA_LP_F16_S);
     const TileShape t = lp_tile_shape(large);
@@ -700,6 +704,109 @@ int run_lowp(int precision, int64_t M, int64_t N, int64_t K, float alpha, const 
     const bool large = p.kid == KID_MFMA_LP_F16 || p.kid == KID_MFMA_LP_BF16;
     const bool bf16 = p.kid == KID_MFMA_LP_BF16 || p.kid == KID_MFMA_LP_BF16_S;
     const hipError_t e = launch_mfma_lp(a, large, bf16, p.transB, p.vec, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
+}
+
+// Two-pass mixed precision with a caller workspace: the one-pass call's
+// validation and quick returns; the two passes only where they measured
+// faster, with 256 x 256 tiles when there are at least 128 of them, else
+// 128 x 128.  `bytes` is what the workspace must hold.
+struct Lp16Plan {
+    Plan base;
+    int kid = KID_NONE;  // KID_LP16_*; KID_NONE: the one-pass call runs
+    bool large = false;
+    int64_t bytes = 0;
+};
+
+// forced: always the two passes (tile_req 0 = the tile rule below, 256 or 128
+// = that tile); otherwise only where they measured faster.
+Lp16Plan make_lp16_plan(bool forced, int tile_req, int precision, int64_t M, int64_t N, int64_t K, float alpha,
+                        const float *A, int64_t lda, const float *B, int64_t ldb, int transB, float beta,
+                        const float *C, int64_t ldc)
+{
+    Lp16Plan lp;
+    lp.base = make_lowp_plan(precision, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc);
+    if (lp.base.status == SGEMM_OK && tile_req != 0 && tile_req != 256 && tile_req != 128) {
+        lp.base.status = SGEMM_ERR_INVALID_VALUE;
+        lp.base.kid = KID_NONE;
+        return lp;
+    }
+    const Plan &p = lp.base;
+    const bool product = p.kid == KID_MFMA_LP_F16 || p.kid == KID_MFMA_LP_BF16 || p.kid == KID_MFMA_LP_F16_S ||
+                         p.kid == KID_MFMA_LP_BF16_S;
+    if (p.status != SGEMM_OK || !product)
+        return lp;
+    // Measured on MI355X (bf16): the two passes beat the one-pass kernel from
+    // ~1e10 FLOPs (2048^3: 392 against 348 TFLOP/s, 8192^3: 933 against 687)
+    // and on smaller products with edge tiles or a k tail, which the rounding
+    // pass pads away (1000 x 1017 x 999: 65 against 46); below, the pass costs
+    // more than it saves (1024^3: 77 against 117).
+    const double flops = 2.0 * (double)M * (double)N * (double)K;
+    const bool ragged = (M % 64) != 0 || (N % 64) != 0 || (K % 32) != 0;
+    if (!forced && !(flops >= 1e10 || (flops >= 1e9 && ragged)))
+        return lp;
+    const bool bf16 = precision == SGEMM_PREC_BF16;
+    // 256 x 256 tiles once they keep at least half the CUs busy, else 128 x 128
+    // (2560^3: 483 against 346 TFLOP/s; 3000^3: 478 against 458)
+    const TileShape tl = lp16_tile_shape(true);
+    lp.large = tile_req == 0 ? ceil_div(M, tl.bm) * ceil_div(N, tl.bn) >= 128 : tile_req == 256;
+    const TileShape t = lp16_tile_shape(lp.large);
+    const int64_t tiles = ceil_div(M, t.bm) * ceil_div(N, t.bn);
+    if (tiles * (lp.large ? 512 : 256) > kMaxWorkItems || ceil_div(K, 32) * 32 > std::numeric_limits<int>::max()) {
+        if (forced) {
+            lp.base.status = SGEMM_ERR_INVALID_VALUE;
+            lp.base.kid = KID_NONE;
+        }
+        return lp;  // the one-pass call handles (or rejects) it
+    }
+    lp.kid = lp.large ? (bf16 ? KID_LP16_BF16 : KID_LP16_F16) : (bf16 ? KID_LP16_BF16_S : KID_LP16_F16_S);
+    lp.bytes = lp16_workspace_bytes(M, N, K, lp.large);
+    lp.base.tiles_m = ceil_div(M, t.bm);
+    lp.base.tiles_n = ceil_div(N, t.bn);
+    return lp;
+}
+
+int run_lowp_ws(bool forced, int tile_req, int precision, int64_t M, int64_t N, int64_t K, float alpha,
+                const float *A, int64_t lda, const float *B, int64_t ldb, int transB, float beta, float *C,
+                int64_t ldc, void *ws, int64_t ws_bytes, void *stream)
+{
+    if (ws_bytes < 0)
+        return SGEMM_ERR_INVALID_VALUE;
+    const Lp16Plan lp =
+        make_lp16_plan(forced, tile_req, precision, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc);
+    if (lp.base.status != SGEMM_OK)
+        return lp.base.status;
+    if (lp.kid == KID_NONE)  // quick returns, product-free cases, or the one-pass call is faster
+        return run_lowp(precision, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, stream);
+    if (ws == nullptr || ws_bytes < lp.bytes) {
+        if (forced)
+            return SGEMM_ERR_INVALID_VALUE;
+        return run_lowp(precision, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, stream);
+    }
+    const int ws_status = check_workspace(ws, ws_bytes, lp.bytes, M, N, K, A, lda, B, ldb, transB, C, ldc);
+    if (ws_status != SGEMM_OK)
+        return ws_status;
+    const int dev_status = check_device();
+    if (dev_status != SGEMM_OK)
+        return dev_status;
+    GemmArgs a;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.lda = lda;
+    a.ldb = ldb;
+    a.ldc = ldc;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.flags = 0;
+    a.k_split = 0;
+    a.c_split_stride = 0;
+    (void)hipGetLastError();
+    const bool bf16 = precision == SGEMM_PREC_BF16;
+    const hipError_t e = launch_lp16(a, lp.large, bf16, lp.base.transB, ws, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
 }
 
@@ -805,6 +912,56 @@ int sgemm_f32_ws_plan(int64_t M, int64_t N, int64_t K, int transB, int *method, 
     if (workspace_bytes)
         *workspace_bytes = c.method == 2 ? c.sk.bytes : (c.method == 1 ? c.split.bytes : 0);
     return st;
+}
+
+int sgemm_f32_lowp_ws(int precision, int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
+                      const float *B, int64_t ldb, int transB, float beta, float *C, int64_t ldc, void *workspace,
+                      int64_t workspace_bytes, void *stream)
+{
+    return sgemm::run_lowp_ws(false, 0, precision, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, workspace,
+                              workspace_bytes, stream);
+}
+
+int sgemm_f32_lowp_2pass(int precision, int tile, int64_t M, int64_t N, int64_t K, float alpha, const float *A,
+                         int64_t lda, const float *B, int64_t ldb, int transB, float beta, float *C, int64_t ldc,
+                         void *workspace, int64_t workspace_bytes, void *stream)
+{
+    return sgemm::run_lowp_ws(true, tile, precision, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, workspace,
+                              workspace_bytes, stream);
+}
+
+static int lowp_ws_plan(bool forced, int tile, int precision, int64_t M, int64_t N, int64_t K, int transB,
+                        int *kernel_id, int64_t *tiles_m, int64_t *tiles_n, int64_t *workspace_bytes)
+{
+    const float *A = reinterpret_cast<const float *>((uintptr_t)1 << 40);
+    const float *B = reinterpret_cast<const float *>((uintptr_t)1 << 50);
+    const float *C = reinterpret_cast<const float *>((uintptr_t)1 << 58);
+    const int64_t lda = K > 1 ? K : 1, ldc = N > 1 ? N : 1;
+    const int64_t ldb = transB == 1 ? lda : ldc;
+    const sgemm::Lp16Plan lp =
+        sgemm::make_lp16_plan(forced, tile, precision, M, N, K, 1.0f, A, lda, B, ldb, transB, 0.0f, C, ldc);
+    const bool two = lp.base.status == SGEMM_OK && lp.kid != sgemm::KID_NONE;
+    if (kernel_id)
+        *kernel_id = two ? lp.kid : lp.base.kid;
+    if (tiles_m)
+        *tiles_m = lp.base.kid == sgemm::KID_NONE ? 0 : lp.base.tiles_m;
+    if (tiles_n)
+        *tiles_n = lp.base.kid == sgemm::KID_NONE ? 0 : lp.base.tiles_n;
+    if (workspace_bytes)
+        *workspace_bytes = two ? lp.bytes : 0;
+    return lp.base.status;
+}
+
+int sgemm_f32_lowp_ws_plan(int precision, int64_t M, int64_t N, int64_t K, int transB, int *kernel_id,
+                           int64_t *tiles_m, int64_t *tiles_n, int64_t *workspace_bytes)
+{
+    return lowp_ws_plan(false, 0, precision, M, N, K, transB, kernel_id, tiles_m, tiles_n, workspace_bytes);
+}
+
+int sgemm_f32_lowp_2pass_plan(int precision, int tile, int64_t M, int64_t N, int64_t K, int transB, int *kernel_id,
+                              int64_t *tiles_m, int64_t *tiles_n, int64_t *workspace_bytes)
+{
+    return lowp_ws_plan(true, tile, precision, M, N, K, transB, kernel_id, tiles_m, tiles_n, workspace_bytes);
 }
 
 int sgemm_f32_streamk_plan(int tile, int64_t M, int64_t N, int64_t K, int transB, int *kernel_id,

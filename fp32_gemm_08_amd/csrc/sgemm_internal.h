@@ -64,6 +64,10 @@ enum KernelId : int {
     KID_MFMA_LP_BF16 = 61,  // the same with bf16
     KID_MFMA_LP_F16_S = 62, // mixed precision, fp16, 64 x 64 (few output tiles)
     KID_MFMA_LP_BF16_S = 63,
+    KID_LP16_F16 = 64,      // two-pass mixed precision (rounding pass + 16-bit GEMM), fp16, 256 x 256
+    KID_LP16_BF16 = 65,
+    KID_LP16_F16_S = 66,    // the same with 128 x 128 tiles
+    KID_LP16_BF16_S = 67,
 };
 
 // Tile geometry of each kernel (rows x cols of C per workgroup).
@@ -86,6 +90,21 @@ hipError_t launch_mfma_sk(const GemmArgs &a, const SkArgs &sk, int kid, bool tra
 int mfma_stage_k(int kid);
 // Mixed precision: operands rounded to fp16 (bf16 = false) or bf16 while staged.
 hipError_t launch_mfma_lp(const GemmArgs &a, bool large, bool bf16, bool transB, bool vec, hipStream_t stream);
+
+// Two-pass mixed precision (rounding pass into the workspace, then the GEMM on
+// 16-bit operands): 256 x 256 tiles when `large`, else 128 x 128.
+struct Lp16Args {
+    const void *A16;
+    const void *B16;
+    float *C;
+    int64_t ldk, ldc;
+    int M, N, Kp;
+    float alpha, beta;
+    int tiles_m, tiles_n;
+};
+TileShape lp16_tile_shape(bool large);
+int64_t lp16_workspace_bytes(int64_t M, int64_t N, int64_t K, bool large);
+hipError_t launch_lp16(const GemmArgs &a, bool large, bool bf16, bool transB, void *ws, hipStream_t stream);
 TileShape lp_tile_shape(bool large);
 // C <- alpha * sum_{s<splits} W[s*stride + i*N + j] + beta*C (C not read when beta == 0).
 hipError_t launch_splitk_reduce(const float *W, int splits, int64_t stride, int M, int N, float alpha, float beta,

@@ -30,7 +30,9 @@ TRANSPOSE_ALGO = {"auto": 0, "naive": 1, "lds": 2, "lds_nopad": 3, "narrow": 4}
 # Symbols declared in include/sgemm_f32.h.
 PRECISION = {"fp16": 1, "bf16": 2}
 
-EXPORTS = ("sgemm_f32", "sgemm_f32_algo", "sgemm_f32_lowp", "sgemm_f32_lowp_plan", "sgemm_f32_plan",
+EXPORTS = ("sgemm_f32", "sgemm_f32_algo", "sgemm_f32_lowp", "sgemm_f32_lowp_2pass", "sgemm_f32_lowp_2pass_plan",
+           "sgemm_f32_lowp_plan", "sgemm_f32_lowp_ws",
+           "sgemm_f32_lowp_ws_plan", "sgemm_f32_plan",
            "sgemm_f32_splitk", "sgemm_f32_splitk_plan",
            "sgemm_f32_status_string", "sgemm_f32_streamk", "sgemm_f32_streamk_plan", "sgemm_f32_transpose",
            "sgemm_f32_transpose_algo", "sgemm_f32_transpose_plan", "sgemm_f32_version", "sgemm_f32_ws",
@@ -80,6 +82,16 @@ def load():
         lib.sgemm_f32_splitk_plan.restype = ci
         lib.sgemm_f32_splitk_plan.argtypes = [i64, i64, i64, i64, ci, ctypes.POINTER(i64), ctypes.POINTER(ci),
                                               ctypes.POINTER(i64)]
+        lib.sgemm_f32_lowp_ws.restype = ci
+        lib.sgemm_f32_lowp_ws.argtypes = [ci] + ws_args
+        lib.sgemm_f32_lowp_2pass.restype = ci
+        lib.sgemm_f32_lowp_2pass.argtypes = [ci, ci] + ws_args
+        lib.sgemm_f32_lowp_2pass_plan.restype = ci
+        lib.sgemm_f32_lowp_2pass_plan.argtypes = [ci, ci, i64, i64, i64, ci, ctypes.POINTER(ci),
+                                                  ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64)]
+        lib.sgemm_f32_lowp_ws_plan.restype = ci
+        lib.sgemm_f32_lowp_ws_plan.argtypes = [ci, i64, i64, i64, ci, ctypes.POINTER(ci), ctypes.POINTER(i64),
+                                               ctypes.POINTER(i64), ctypes.POINTER(i64)]
         lib.sgemm_f32_ws_plan.restype = ci
         lib.sgemm_f32_ws_plan.argtypes = [i64, i64, i64, ci, ctypes.POINTER(ci), ctypes.POINTER(ci),
                                           ctypes.POINTER(i64)]
@@ -162,6 +174,39 @@ def sgemm_f32_splitk_plan(splits, M, N, K, transB=0):
     nb = ctypes.c_int64(0)
     st = load().sgemm_f32_splitk_plan(splits, M, N, K, transB, ctypes.byref(su), ctypes.byref(kid), ctypes.byref(nb))
     return st, su.value, kid.value, nb.value
+
+
+def sgemm_f32_lowp_ws(precision, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, workspace, workspace_bytes,
+                      stream=0) -> int:
+    """Mixed precision with a workspace: a rounding pass into it, then the
+    16-bit GEMM (the one-pass call when the workspace is too small)."""
+    return load().sgemm_f32_lowp_ws(precision, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, workspace,
+                                    workspace_bytes, stream)
+
+
+def sgemm_f32_lowp_ws_plan(precision, M, N, K, transB=0):
+    """Host-only query: (status, kernel_id, tiles_m, tiles_n, workspace_bytes)."""
+    kid = ctypes.c_int(0)
+    tm, tn, nb = (ctypes.c_int64(0) for _ in range(3))
+    st = load().sgemm_f32_lowp_ws_plan(precision, M, N, K, transB, ctypes.byref(kid), ctypes.byref(tm),
+                                       ctypes.byref(tn), ctypes.byref(nb))
+    return st, kid.value, tm.value, tn.value, nb.value
+
+
+def sgemm_f32_lowp_2pass(precision, tile, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, workspace,
+                         workspace_bytes, stream=0) -> int:
+    """The two-pass mixed-precision call at any size (tile 0, 256 or 128)."""
+    return load().sgemm_f32_lowp_2pass(precision, tile, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc,
+                                       workspace, workspace_bytes, stream)
+
+
+def sgemm_f32_lowp_2pass_plan(precision, tile, M, N, K, transB=0):
+    """Host-only query: (status, kernel_id, tiles_m, tiles_n, workspace_bytes)."""
+    kid = ctypes.c_int(0)
+    tm, tn, nb = (ctypes.c_int64(0) for _ in range(3))
+    st = load().sgemm_f32_lowp_2pass_plan(precision, tile, M, N, K, transB, ctypes.byref(kid), ctypes.byref(tm),
+                                          ctypes.byref(tn), ctypes.byref(nb))
+    return st, kid.value, tm.value, tn.value, nb.value
 
 
 def sgemm_f32_ws_plan(M, N, K, transB=0):
@@ -257,7 +302,8 @@ def gemm(A, B, C, alpha=1.0, beta=0.0, trans_b=False, algo="auto", stream=None, 
     count; ``algo`` is then not used; ``streamk`` = 0, 256 or 128 runs the
     stream-K schedule with the library's tile or that one).  With ``precision`` ("fp16" or "bf16")
     the operands are rounded to that format and multiplied by the 16-bit matrix
-    cores with FP32 sums (sgemm_f32_lowp).
+    cores with FP32 sums (sgemm_f32_lowp; with ``workspace``, sgemm_f32_lowp_ws:
+    a rounding pass into the workspace, then the GEMM on 16-bit operands).
     """
     import torch  # plumbing only: device memory and streams
 
@@ -272,10 +318,14 @@ def gemm(A, B, C, alpha=1.0, beta=0.0, trans_b=False, algo="auto", stream=None, 
     s = (stream if stream is not None else torch.cuda.current_stream(C.device)).cuda_stream
     with torch.cuda.device(C.device):
         if precision is not None:
-            if workspace is not None:
-                raise ValueError("the mixed-precision path takes no workspace")
-            st = sgemm_f32_lowp(PRECISION[precision], M, N, K, float(alpha), A.data_ptr(), ld(A), B.data_ptr(),
-                                ld(B), int(bool(trans_b)), float(beta), C.data_ptr(), ld(C), s)
+            args = (PRECISION[precision], M, N, K, float(alpha), A.data_ptr(), ld(A), B.data_ptr(), ld(B),
+                    int(bool(trans_b)), float(beta), C.data_ptr(), ld(C))
+            if workspace is None:
+                st = sgemm_f32_lowp(*args, s)
+            else:
+                if not workspace.is_cuda or not workspace.is_contiguous():
+                    raise ValueError("workspace must be a contiguous device tensor")
+                st = sgemm_f32_lowp_ws(*args, workspace.data_ptr(), workspace.numel() * workspace.element_size(), s)
         elif workspace is None:
             st = sgemm_f32_algo(_algo_id(algo), M, N, K, float(alpha), A.data_ptr(), ld(A), B.data_ptr(), ld(B),
                                 int(bool(trans_b)), float(beta), C.data_ptr(), ld(C), s)

@@ -257,13 +257,61 @@ int sgemm_f32_lowp(int precision, int64_t M, int64_t N, int64_t K, float alpha,
                    float beta, float *C, int64_t ldc, void *stream);
 
 /* Host-only planning query for sgemm_f32_lowp, the counterpart of sgemm_f32_plan.
- * The kernel takes 256 x 256 output tiles when there are at least 256 of them
- * (one per compute unit), else 64 x 64 tiles; tiles_m / tiles_n count them. */
+ * The kernel takes 256 x 256 output tiles when there are at least 128 of them
+ * (half the compute units), else 64 x 64 tiles; tiles_m / tiles_n count them. */
 int sgemm_f32_lowp_plan(int precision, int64_t M, int64_t N, int64_t K, float alpha,
                         const float *A, int64_t lda, const float *B, int64_t ldb, int transB,
                         float beta, const float *C, int64_t ldc,
                         int *kernel_id, int64_t *tiles_m, int64_t *tiles_n,
                         char *name, int name_len);
+
+/*
+ * Mixed precision with a caller workspace: the same operation, rounding and
+ * accuracy contract as sgemm_f32_lowp, in two passes.  A rounding pass writes
+ * r(A) (M x K) and r(op(B)) (N x K, op(B) = B transposed on the way) into the
+ * workspace as k-contiguous 16-bit rows, zero-padded to whole output tiles
+ * and to a multiple of 32 in k; the GEMM then stages those 16-bit tiles
+ * straight from memory into LDS (the one-pass kernel re-reads the FP32
+ * operands and converts them inside its k-loop).  The FP32 sums run in the
+ * same k order as the one-pass kernel's, so for a given tile size the two
+ * calls give the same bits.
+ *
+ * Workspace: a DEVICE buffer owned by the caller, at least the bytes
+ * sgemm_f32_lowp_ws_plan reports (2 * K' * (M' + N') plus alignment, M' and
+ * N' rounded up to the tile, K' to 32), not overlapping A, B or C
+ * (SGEMM_ERR_ALIAS), ordered on one stream with its other uses; its contents
+ * on return are undefined.  With a smaller workspace (or NULL) the call runs
+ * exactly as sgemm_f32_lowp.  Everything else (validation, quick returns,
+ * asynchrony) is sgemm_f32_lowp's.
+ */
+int sgemm_f32_lowp_ws(int precision, int64_t M, int64_t N, int64_t K, float alpha,
+                      const float *A, int64_t lda, const float *B, int64_t ldb, int transB,
+                      float beta, float *C, int64_t ldc,
+                      void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Host-only query for sgemm_f32_lowp_ws: the kernel id (64/65: fp16/bf16 with
+ * 256 x 256 tiles, chosen when there are at least 128 of them; 66/67: 128 x
+ * 128 tiles; otherwise the one-pass call's id: the two passes run for products
+ * of at least 1e10 FLOPs, or 1e9 when M or N is not a multiple of 64 or K of
+ * 32, where they measured faster), the output tiles and the workspace bytes
+ * (0 when the one-pass call runs).  Output pointers may be NULL. */
+int sgemm_f32_lowp_ws_plan(int precision, int64_t M, int64_t N, int64_t K, int transB, int *kernel_id,
+                           int64_t *tiles_m, int64_t *tiles_n, int64_t *workspace_bytes);
+
+/* The two passes whatever the size (`tile`: 0 = the rule above, 256 or 128 =
+ * that tile; anything else SGEMM_ERR_INVALID_VALUE), for callers that want
+ * them and for testing them at every shape.  A workspace smaller than
+ * sgemm_f32_lowp_2pass_plan reports is SGEMM_ERR_INVALID_VALUE. */
+int sgemm_f32_lowp_2pass(int precision, int tile, int64_t M, int64_t N, int64_t K, float alpha,
+                         const float *A, int64_t lda, const float *B, int64_t ldb, int transB,
+                         float beta, float *C, int64_t ldc,
+                         void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Host-only query for sgemm_f32_lowp_2pass, with the outputs of
+ * sgemm_f32_lowp_ws_plan. */
+int sgemm_f32_lowp_2pass_plan(int precision, int tile, int64_t M, int64_t N, int64_t K, int transB,
+                              int *kernel_id, int64_t *tiles_m, int64_t *tiles_n,
+                              int64_t *workspace_bytes);
 
 /*
  * k-split with a caller workspace.  A product whose 64 x 64 output tiles are

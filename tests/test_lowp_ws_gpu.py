@@ -1,0 +1,200 @@
+"""GPU parity of the two-pass mixed-precision calls (a rounding pass into the
+workspace, then the GEMM on 16-bit operands): sgemm_f32_lowp_2pass with each
+tile forced, and sgemm_f32_lowp_ws, which picks one or two passes.
+
+Against the oracle on the rounded operands, the bar of the one-pass call:
+|D - D~| <= 4*K*2^-24*S~ + 1e-6.  Against the one-pass call itself: the same
+bits, since both round each operand once with the same rule and add the
+16-k matrix-core products of every output element in the same k order (zero
+padding adds exact zeros).  The workspace carries canaries before and after
+the planned bytes, and C canary rows and padding.
+"""
+import numpy as np
+import pytest
+
+import fp32_gemm_08_amd as lib
+from fp32_gemm_08_amd.inputs import make_case, make_config
+from oracle import check, gemm_lowp_rows
+
+from gpu_helpers import CANARY, GUARD_ROWS, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+W_CANARY = np.float32(-1234.5)
+W_TAIL = 1024
+PRECS = ["fp16", "bf16"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    assert lib.sgemm_f32_version()
+
+
+def run(case, prec, ws=True, ws_bytes=None, a_offset=0, ldc_pad=0, ws_offset=4, c_fill=np.nan, tile=None):
+    """One call of sgemm_f32_lowp_2pass (tile given), sgemm_f32_lowp_ws (ws) or
+    sgemm_f32_lowp; returns (status, D, plan)."""
+    import torch
+
+    dev = torch.device("cuda", 0)
+    M, N, K = case.M, case.N, case.K
+    t = int(case.trans_b)
+    if tile is not None:
+        plan = lib.sgemm_f32_lowp_2pass_plan(lib.PRECISION[prec], tile, M, N, K, t)
+    else:
+        plan = lib.sgemm_f32_lowp_ws_plan(lib.PRECISION[prec], M, N, K, t)
+    assert plan[0] == 0
+    need = plan[4]
+    ws_bytes = need if ws_bytes is None else ws_bytes
+    ldc = case.ldc + ldc_pad
+    g = GUARD_ROWS
+    full = np.full((M + 2 * g, ldc), CANARY, dtype=np.float32)
+    full[g:g + M, :N] = case.C[:, :N] if case.C is not None else c_fill
+    dA = torch.from_numpy(np.concatenate([np.zeros(a_offset, np.float32), case.A.ravel()])).to(dev)
+    dB = torch.from_numpy(case.B.ravel().copy()).to(dev)
+    dC = torch.from_numpy(full.ravel().copy()).to(dev)
+    n_ws = ws_offset + max(ws_bytes, 0) // 4 + W_TAIL
+    dW = torch.full((n_ws,), float(W_CANARY), dtype=torch.float32, device=dev)
+    s = torch.cuda.current_stream(dev)
+    say(f"lowp_ws {prec} ws={ws} tile={tile} plan={plan} M={M} N={N} K={K} transB={t} alpha={case.alpha} beta={case.beta} "
+        f"lda={case.lda} ldb={case.ldb} ldc={ldc} ws_bytes={ws_bytes} a_offset={a_offset}")
+    args = (lib.PRECISION[prec], M, N, K, case.alpha, dA.data_ptr() + 4 * a_offset, case.lda, dB.data_ptr(),
+            case.ldb, t, case.beta, dC.data_ptr() + 4 * g * ldc, ldc)
+    if tile is not None:
+        st = lib.sgemm_f32_lowp_2pass(args[0], tile, *args[1:], dW.data_ptr() + 4 * ws_offset, ws_bytes,
+                                      s.cuda_stream)
+    elif ws:
+        st = lib.sgemm_f32_lowp_ws(*args, dW.data_ptr() + 4 * ws_offset, ws_bytes, s.cuda_stream)
+    else:
+        st = lib.sgemm_f32_lowp(*args, s.cuda_stream)
+    torch.cuda.synchronize()
+    out = dC.cpu().numpy().reshape(M + 2 * g, ldc)
+    w = dW.cpu().numpy()
+    assert np.all(w[:ws_offset].view(np.uint32) == W_CANARY.view(np.uint32)), "write before the workspace"
+    assert np.all(w[ws_offset + max(ws_bytes, 0) // 4:].view(np.uint32) == W_CANARY.view(np.uint32)), \
+        "write past the planned workspace"
+    assert np.all(out[:g].view(np.uint32) == CANARY.view(np.uint32)), "write above C"
+    assert np.all(out[g + M:].view(np.uint32) == CANARY.view(np.uint32)), "write below C"
+    if ldc > N:
+        assert np.all(out[g:g + M, N:].view(np.uint32) == CANARY.view(np.uint32)), "write into C padding"
+    return st, out[g:g + M, :N], plan
+
+
+def assert_lowp_parity(case, prec, Dg, rows=None, what=""):
+    D, S, _ = gemm_lowp_rows(prec, case.M, case.N, case.K, case.alpha, case.A, case.B, case.trans_b, case.beta,
+                             case.C, rows=rows)
+    r = check(Dg if rows is None else Dg[rows], D, S, case.K)
+    say(f"{what} {prec}: max_abs={r['max_abs']:.3e} max_rho={r['max_rho']:.3f} fails={r['n_fail']}")
+    assert r["ok"], f"{what} {prec}: {r}"
+
+
+def same_bits(x, y):
+    return np.array_equal(np.ascontiguousarray(x).view(np.uint32), np.ascontiguousarray(y).view(np.uint32))
+
+
+TILES = [256, 128]
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("name", ["c1_128", "c2_1024", "c3_ragged_bt", "c5_512"])
+def test_configs_full(prec, name, tile):
+    case = make_config(name)
+    st, D, plan = run(case, prec, tile=tile)
+    assert st == 0 and plan[1] in (64, 65, 66, 67)
+    assert_lowp_parity(case, prec, D, what=name)
+    st1, D1, _ = run(case, prec, ws=False)
+    assert st1 == 0 and same_bits(D, D1)
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("name", ["c4_4096", "c5_2048", "c5_tall"])
+def test_configs_sampled(prec, name):
+    # sgemm_f32_lowp_ws: its own choice of passes and tile
+    case = make_config(name)
+    st, D, plan = run(case, prec)
+    assert st == 0 and plan[1] in (64, 65, 66, 67)
+    assert_lowp_parity(case, prec, D, rows=sample_rows(case.M, n=16, tile=256), what=name)
+    st1, D1, _ = run(case, prec, ws=False)
+    assert st1 == 0 and same_bits(D, D1)
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("shape", [(257, 255, 33, False, dict(lda=35)), (300, 270, 131, True, dict(ldb=140)),
+                                   (513, 1, 700, False, {}), (1, 700, 513, True, {}), (256, 256, 32, False, {}),
+                                   (1000, 1017, 999, False, {}), (2049, 2051, 517, True, {}), (64, 64, 1, False, {})])
+def test_edges_and_unaligned(prec, shape, tile):
+    M, N, K, tb, extra = shape
+    case = make_case(M, N, K, trans_b=tb, alpha=-0.75, beta=0.5, seed=M + N + K, **extra)
+    st, D, _ = run(case, prec, ldc_pad=3, tile=tile)
+    assert st == 0
+    assert_lowp_parity(case, prec, D, what=f"{M}x{N}x{K}")
+    st1, D1, _ = run(case, prec, ws=False, ldc_pad=3)
+    assert st1 == 0 and same_bits(D, D1)
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("tb", [False, True])
+def test_integers_bit_exact(prec, tb, tile):
+    case = make_case(300, 520, 1000, trans_b=tb, alpha=1.0, beta=1.0, dist="int2", seed=41)
+    st, D, _ = run(case, prec, tile=tile)
+    assert st == 0
+    Dref, _, _ = gemm_lowp_rows(prec, 300, 520, 1000, 1.0, case.A, case.B, tb, 1.0, case.C)
+    assert np.array_equal(D.astype(np.float64), Dref)
+
+
+@pytest.mark.parametrize("prec", PRECS)
+def test_misaligned_base_and_nan_c(prec):
+    case = make_case(400, 384, 260, alpha=2.0, beta=0.0, seed=43)
+    st, D, _ = run(case, prec, a_offset=1, c_fill=np.nan, tile=0)
+    assert st == 0 and np.all(np.isfinite(D))
+    assert_lowp_parity(case, prec, D, what="misaligned A, beta 0")
+
+
+def test_fp16_overflow_and_bf16_range():
+    case = make_case(64, 96, 40, seed=46)
+    case.A[:] = np.float32(1.0)
+    case.B[:] = np.float32(1.0)
+    case.A[5, 7] = np.float32(1e5)
+    st, D16, _ = run(case, "fp16", tile=0)
+    assert st == 0 and np.all(np.isposinf(D16[5])) and np.all(D16[np.arange(64) != 5] == 40.0)
+    st, Db, _ = run(case, "bf16", tile=0)
+    assert st == 0 and np.all(Db[5] == 99840.0 + 39.0)
+
+
+def test_ws_small_workspace_runs_one_pass():
+    case = make_case(2048, 2048, 2048, seed=47)
+    need = lib.sgemm_f32_lowp_ws_plan(2, 2048, 2048, 2048, 0)[4]
+    assert need > 0
+    st, D, plan = run(case, "bf16", ws_bytes=need - 256)
+    assert st == 0
+    st1, D1, _ = run(case, "bf16", ws=False)
+    assert same_bits(D, D1)
+
+
+def test_2pass_small_workspace_rejected():
+    case = make_case(700, 600, 500, seed=49)
+    need = lib.sgemm_f32_lowp_2pass_plan(2, 0, 700, 600, 500, 0)[4]
+    st, D, _ = run(case, "bf16", ws_bytes=need - 256, tile=0, c_fill=7.0)
+    assert st == 1 and np.all(D == 7.0)
+
+
+def plan_bytes(case):
+    return lib.sgemm_f32_lowp_2pass_plan(2, 0, case.M, case.N, case.K, int(case.trans_b))[4]
+
+
+def test_torch_wrapper():
+    import torch
+
+    dev = torch.device("cuda", 0)
+    case = make_case(320, 256, 192, trans_b=True, alpha=1.25, seed=48)
+    A, B = torch.from_numpy(case.A).to(dev), torch.from_numpy(case.B).to(dev)
+    C = torch.empty(320, 256, device=dev)
+    W = torch.empty(1 << 26, dtype=torch.uint8, device=dev)
+    lib.gemm(A, B, C, alpha=1.25, trans_b=True, precision="bf16", workspace=W)
+    torch.cuda.synchronize()
+    assert_lowp_parity(case, "bf16", C.cpu().numpy(), what="wrapper")
