@@ -76,31 +76,17 @@ __device__ __forceinline__ void q_load(const void *src, unsigned char *lds)
 }
 
 // Wait until at most N of this wavefront's direct loads are outstanding and
-// all its LDS reads are done, then meet the other wavefronts.  The asm is a
-// compiler memory barrier too, so no LDS access moves across it.
+// all its LDS reads are done, then meet the other wavefronts.  The wait is
+// the s_waitcnt builtin (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt
+// 6:4 left at 7, lgkmcnt 11:8 = 0), so the compiler knows which reads have
+// completed and does not wait for them again; the barrier is an asm with a
+// memory clobber, so no memory access moves across it.
 template <int N>
 __device__ __forceinline__ void q_wait_barrier()
 {
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-
-template <class Q>
-__device__ __forceinline__ void q_wait_ahead(int ahead)
-{
-    // ahead: stages requested after the one about to be read (0 .. S-2)
-    if constexpr (Q::S >= 4) {
-        if (ahead >= 2) {
-            q_wait_barrier<2 * Q::LOADS>();
-            return;
-        }
-    }
-    if constexpr (Q::S >= 3) {
-        if (ahead == 1) {
-            q_wait_barrier<Q::LOADS>();
-            return;
-        }
-    }
-    q_wait_barrier<0>();
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | ((N >> 4) << 14));
+    asm volatile("s_barrier" ::: "memory");
 }
 
 template <class Q, bool BF16>
@@ -130,14 +116,15 @@ __global__ __launch_bounds__(Q::NT) void lp16_gemm_kernel(Lp16Args g)
         const int r = 16 * (w * Q::NB + j) + lane / 4;
         pb[j] = static_cast<const T *>(g.B16) + (int64_t)(n0 + r) * g.ldk + 8 * ((lane & 3) ^ q_swz(r));
     }
-    auto issue = [&](int kt) {
-        unsigned char *st = smem + (kt % Q::S) * Q::STAGE;
+    // Request the k-tile `src` into the buffer of stage `slot`.
+    auto issue = [&](int src, int slot) {
+        unsigned char *st = smem + (slot % Q::S) * Q::STAGE;
 #pragma unroll
         for (int j = 0; j < Q::NA; ++j)
-            q_load(pa[j] + (int64_t)kt * QK, st + (w * Q::NA + j) * 1024);
+            q_load(pa[j] + (int64_t)src * QK, st + (w * Q::NA + j) * 1024);
 #pragma unroll
         for (int j = 0; j < Q::NB; ++j)
-            q_load(pb[j] + (int64_t)kt * QK, st + Q::BM * QROW + (w * Q::NB + j) * 1024);
+            q_load(pb[j] + (int64_t)src * QK, st + Q::BM * QROW + (w * Q::NB + j) * 1024);
     };
 
     lp_f32x16 acc[Q::FM][Q::FN];
@@ -164,40 +151,48 @@ __global__ __launch_bounds__(Q::NT) void lp16_gemm_kernel(Lp16Args g)
             fb[fn] = *reinterpret_cast<const V8 *>(bs + r * QROW + 16 * (c ^ q_swz(r)));
         }
     };
-    auto mma_step = [&](const V8 (&fa)[Q::FM], const V8 (&fb)[Q::FN]) {
+    // MFMAs of one 16-k step; `from` skips the first blocks (0 .. FM*FN).
+    auto mma_step = [&](const V8 (&fa)[Q::FM], const V8 (&fb)[Q::FN], int from, int to) {
 #pragma unroll
         for (int fm = 0; fm < Q::FM; ++fm)
 #pragma unroll
             for (int fn = 0; fn < Q::FN; ++fn)
-                acc[fm][fn] = Lp<BF16>::mma(fa[fm], fb[fn], acc[fm][fn]);
+                if (fm * Q::FN + fn >= from && fm * Q::FN + fn < to)
+                    acc[fm][fn] = Lp<BF16>::mma(fa[fm], fb[fn], acc[fm][fn]);
     };
 
-    // Pipeline: stages 0 .. S-2 requested up front.  Step kt: read the second
-    // 16-k fragments of stage kt, multiply the first; wait for stage kt+1 and
-    // meet the other wavefronts (everyone is then done with stage kt-1, whose
-    // buffer takes stage kt+S-1), read the first fragments of stage kt+1,
-    // multiply the second of stage kt.  LDS reads are always in flight under
-    // 8 MFMAs of the other fragment set.
+    // Pipeline: stages 0 .. S-2 requested up front.  Step kt (the first 16-k
+    // fragments of stage kt already in registers): one MFMA, then the reads of
+    // the second fragments, then the other MFMAs of the first; wait for stage
+    // kt+1 and meet the other wavefronts (everyone is then done with stage
+    // kt-1, whose buffer takes stage kt+S-1); read the first fragments of
+    // stage kt+1 and multiply the second of stage kt.  The LDS reads are in
+    // flight under MFMAs of the other fragment set.
+    //
+    // Every step requests one stage, past the end a repeat of the last one
+    // (into the free buffer of stage kt-1, never read again), so the number of
+    // loads in flight is the same at every wait, and every step runs the same
+    // branch-free code: the compiler then sees that the barrier's wait covered
+    // all earlier LDS reads and waits only for the newer ones.
     const int nk = g.Kp / QK;
+    constexpr int NF = Q::FM * Q::FN;
 #pragma unroll
     for (int st = 0; st < Q::S - 1; ++st)
-        if (st < nk)
-            issue(st);
+        issue(min(st, nk - 1), st);
     V8 fa0[Q::FM], fb0[Q::FN], fa1[Q::FM], fb1[Q::FN];
-    q_wait_ahead<Q>(min(nk - 1, Q::S - 2));
+    q_wait_barrier<(Q::S - 2) * Q::LOADS>();
     read_frags(0, 0, fa0, fb0);
     for (int kt = 0; kt < nk; ++kt) {
+        mma_step(fa0, fb0, 0, 1);
+        __builtin_amdgcn_sched_barrier(0);
         read_frags(kt, 1, fa1, fb1);
         __builtin_amdgcn_sched_barrier(0);
-        mma_step(fa0, fb0);
-        if (kt + 1 < nk) {
-            q_wait_ahead<Q>(min(nk - 2 - kt, Q::S - 3));
-            if (kt + Q::S - 1 < nk)
-                issue(kt + Q::S - 1);
-            read_frags(kt + 1, 0, fa0, fb0);
-        }
+        mma_step(fa0, fb0, 1, NF);
+        q_wait_barrier<(Q::S - 3) * Q::LOADS>();  // stage kt+1 has landed
+        issue(min(kt + Q::S - 1, nk - 1), kt + Q::S - 1);
+        read_frags(kt + 1, 0, fa0, fb0);
         __builtin_amdgcn_sched_barrier(0);
-        mma_step(fa1, fb1);
+        mma_step(fa1, fb1, 0, NF);
     }
 
     // Epilogue: D = alpha * acc + beta * C, masked to M x N (C not read when
