@@ -1,9 +1,10 @@
 // Mixed-precision GEMM in two passes, for callers that lend a workspace:
 //
-//   1. rounding pass: A -> A16 (Mp x Kp) and op(B) -> B16 (Np x Kp), both
-//      k-contiguous 16-bit (fp16 or bf16, round to nearest, ties to even) and
-//      zero-padded to whole tiles in m / n and to a multiple of 32 in k; op(B) = B
-//      is transposed on the way through an LDS tile;
+//   1. rounding pass: A -> A16 and op(B) -> B16, 16-bit (fp16 or bf16, round
+//      to nearest, ties to even), zero-padded to whole tiles in m / n and to a
+//      multiple of 32 in k, and stored k-tile major: slab s holds k values
+//      [32s, 32s+32) of every row, 64 bytes per row, rows one after another
+//      (op(B) = B is transposed on the way through an LDS tile);
 //   2. GEMM on the 16-bit operands: D = alpha * A16 * B16^T + beta * C, FP32
 //      sums on the matrix cores.
 //
@@ -17,12 +18,15 @@
 //
 // GEMM tile: BM x BN output, WGM x WGN wavefronts of (BM/WGM) x (BN/WGN), each
 // a grid of 32 x 32 blocks (lp_types.h has the lane layout).  One stage holds
-// 32 k of BM rows of A16 and BN rows of B16: 64 bytes per row, stored as 1 KB
+// 32 k of BM rows of A16 and BN rows of B16 -- in the slab layout, one
+// contiguous 64 * BM (and 64 * BN) bytes of memory -- stored in LDS as 1 KB
 // blocks of 16 rows whose four 16-byte chunks are XOR-permuted by
 // ((r >> 1) ^ (r >> 2)) & 3, so that the 16-byte fragment reads of 8 (or 16)
 // consecutive rows at one chunk touch distinct banks.  A wavefront fills a 1 KB
 // block with one global_load_lds_dwordx4 (lane i -> row i/4, physical chunk
-// i%4).  S stages rotate: stage kt+S-1 is requested while stage kt is
+// i%4) from 1 KB of contiguous memory.  (Rows k-contiguous over the whole K,
+// where each load used 64 bytes of sixteen 128-byte lines, measured 4-5%
+// slower: 1059 against 1108 TFLOP/s at 4096^3.)  S stages rotate: stage kt+S-1 is requested while stage kt is
 // multiplied, and each k-step waits only for the next stage (s_waitcnt on
 // the count of loads still allowed in flight, then a barrier); the fragment
 // reads of one 16-k step run under the MFMAs of the previous one.
@@ -51,7 +55,7 @@ struct QGeo {
     static constexpr int STAGE = (BM + BN) * QROW;                // bytes
     static_assert(WM % 32 == 0 && WN % 32 == 0, "whole 32 x 32 blocks");
     static_assert(NA * 16 * NW == BM && NB * 16 * NW == BN, "every wavefront loads whole blocks");
-    static_assert(S >= 3 && S <= 4 && S * STAGE <= 160 * 1024, "three buffers in use per step, all in the LDS");
+    static_assert(S >= 3 && S * STAGE <= 160 * 1024, "three buffers in use per step, all in the LDS");
     static_assert((S - 2) * LOADS <= 63, "vmcnt range");
 };
 
@@ -109,22 +113,22 @@ __global__ __launch_bounds__(Q::NT) void lp16_gemm_kernel(Lp16Args g)
 #pragma unroll
     for (int j = 0; j < Q::NA; ++j) {
         const int r = 16 * (w * Q::NA + j) + lane / 4;
-        pa[j] = static_cast<const T *>(g.A16) + (int64_t)(m0 + r) * g.ldk + 8 * ((lane & 3) ^ q_swz(r));
+        pa[j] = static_cast<const T *>(g.A16) + (int64_t)(m0 + r) * QK + 8 * ((lane & 3) ^ q_swz(r));
     }
 #pragma unroll
     for (int j = 0; j < Q::NB; ++j) {
         const int r = 16 * (w * Q::NB + j) + lane / 4;
-        pb[j] = static_cast<const T *>(g.B16) + (int64_t)(n0 + r) * g.ldk + 8 * ((lane & 3) ^ q_swz(r));
+        pb[j] = static_cast<const T *>(g.B16) + (int64_t)(n0 + r) * QK + 8 * ((lane & 3) ^ q_swz(r));
     }
     // Request the k-tile `src` into the buffer of stage `slot`.
     auto issue = [&](int src, int slot) {
         unsigned char *st = smem + (slot % Q::S) * Q::STAGE;
 #pragma unroll
         for (int j = 0; j < Q::NA; ++j)
-            q_load(pa[j] + (int64_t)src * QK, st + (w * Q::NA + j) * 1024);
+            q_load(pa[j] + (int64_t)src * g.slab_a, st + (w * Q::NA + j) * 1024);
 #pragma unroll
         for (int j = 0; j < Q::NB; ++j)
-            q_load(pb[j] + (int64_t)src * QK, st + Q::BM * QROW + (w * Q::NB + j) * 1024);
+            q_load(pb[j] + (int64_t)src * g.slab_b, st + Q::BM * QROW + (w * Q::NB + j) * 1024);
     };
 
     lp_f32x16 acc[Q::FM][Q::FN];
@@ -239,8 +243,10 @@ __global__ __launch_bounds__(Q::NT) void lp16_gemm_kernel(Lp16Args g)
     }
 }
 
-// Rounding pass, k-contiguous source (A, or op(B) = B^T stored N x K): dst row
-// r, chunk of 8 at k <- r(src[r][k .. k+7]), zero past R rows and K columns.
+// Rounding pass, k-contiguous source (A, or op(B) = B^T stored N x K): item i
+// rounds the 8 values at k = 32*slab + 8*c of row r, i = (slab*Rp + r)*4 + c,
+// so consecutive items write consecutive 16-byte chunks of the slab layout;
+// zero past R rows and K columns.
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(256) void lp16_round_rows(const float *src, int64_t ld, int R, int K, void *dst_,
                                                        int Rp, int Kp)
@@ -248,10 +254,12 @@ __global__ __launch_bounds__(256) void lp16_round_rows(const float *src, int64_t
     typedef typename Lp<BF16>::T T;
     typedef typename Lp<BF16>::V8 V8;
     T *dst = static_cast<T *>(dst_);
-    const int cpr = Kp / 8;
-    const int64_t total = (int64_t)Rp * cpr;
+    const int64_t total = (int64_t)Rp * (Kp / 8);
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-        const int r = (int)(i / cpr), k = 8 * (int)(i % cpr);
+        const int c = (int)(i & 3);
+        const int64_t rs = i >> 2;
+        const int r = (int)(rs % Rp), slab = (int)(rs / Rp);
+        const int k = QK * slab + 8 * c;
         float x[8];
         const float *p = src + (int64_t)r * ld + k;
         if (VEC && r < R && k + 8 <= K) {
@@ -271,12 +279,13 @@ __global__ __launch_bounds__(256) void lp16_round_rows(const float *src, int64_t
 #pragma unroll
         for (int q = 0; q < 8; ++q)
             v[q] = (T)x[q];
-        *reinterpret_cast<V8 *>(dst + (int64_t)r * Kp + k) = v;
+        *reinterpret_cast<V8 *>(dst + i * 8) = v;
     }
 }
 
-// Rounding pass for op(B) = B (stored K x N): dst[n][k] <- r(B[k][n]) through a
-// 64 x 64 LDS tile (rows read along n, written along k), zero past K and N.
+// Rounding pass for op(B) = B (stored K x N): element (n, k) of the slab layout
+// <- r(B[k][n]) through a 64 x 64 LDS tile (rows read along n, written along
+// k), zero past K and N.
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(256) void lp16_round_transpose(const float *B, int64_t ldb, int K, int N, void *dst_,
                                                             int Np, int Kp)
@@ -308,17 +317,19 @@ __global__ __launch_bounds__(256) void lp16_round_transpose(const float *B, int6
             t[nc + q][kr] = (T)x[q];
     }
     __syncthreads();
+    // two slabs of 64 rows x 4 chunks; consecutive work-items write
+    // consecutive 16-byte chunks of a slab
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int e = threadIdx.x + 256 * i;
-        const int nr = e / 8, kc = 8 * (e % 8);
-        const int n = n0 + nr, k = k0 + kc;
+        const int sl = e / 256, nr = (e / 4) % 64, c = e % 4;
+        const int n = n0 + nr, k = k0 + QK * sl + 8 * c;
         if (n < Np && k < Kp) {
             V8 v;
 #pragma unroll
             for (int q = 0; q < 8; ++q)
-                v[q] = t[nr][kc + q];
-            *reinterpret_cast<V8 *>(dst + (int64_t)n * Kp + k) = v;
+                v[q] = t[nr][QK * sl + 8 * c + q];
+            *reinterpret_cast<V8 *>(dst + ((int64_t)(k / QK) * Np + n) * QK + 8 * c) = v;
         }
     }
 }
@@ -361,8 +372,8 @@ static void round_rows(const float *src, int64_t ld, int R, int K, void *dst, in
 
 TileShape lp16_tile_shape(bool large) { return large ? TileShape{QL::BM, QL::BN} : TileShape{QS::BM, QS::BN}; }
 
-// Layout of the workspace: A16 (Mp x Kp) at 0, B16 (Np x Kp) after it, each
-// starting on a 256-byte boundary.
+// Layout of the workspace: A16 (Kp/32 slabs of Mp x 32) at 0, B16 (Kp/32
+// slabs of Np x 32) after it, each starting on a 256-byte boundary.
 int64_t lp16_workspace_bytes(int64_t M, int64_t N, int64_t K, bool large)
 {
     const TileShape t = lp16_tile_shape(large);
@@ -401,7 +412,8 @@ hipError_t launch_lp16(const GemmArgs &a, bool large, bool bf16, bool transB, vo
     g.A16 = A16;
     g.B16 = B16;
     g.C = a.C;
-    g.ldk = Kp;
+    g.slab_a = Mp * QK;
+    g.slab_b = Np * QK;
     g.ldc = a.ldc;
     g.M = a.M;
     g.N = a.N;

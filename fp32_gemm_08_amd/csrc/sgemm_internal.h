@@ -94,10 +94,11 @@ hipError_t launch_mfma_lp(const GemmArgs &a, bool large, bool bf16, bool transB,
 // Two-pass mixed precision (rounding pass into the workspace, then the GEMM on
 // 16-bit operands): 256 x 256 tiles when `large`, else 128 x 128.
 struct Lp16Args {
-    const void *A16;
-    const void *B16;
+    const void *A16;   // Kp/32 slabs of Mp rows x 32 values
+    const void *B16;   // Kp/32 slabs of Np rows x 32 values
     float *C;
-    int64_t ldk, ldc;
+    int64_t slab_a, slab_b;  // values per slab: Mp*32, Np*32
+    int64_t ldc;
     int M, N, Kp;
     float alpha, beta;
     int tiles_m, tiles_n;
