@@ -192,6 +192,39 @@ def sweep(algos=("naive", "naive_wg", "lds_tiled", "lds_tiled_nopad", "regblock"
     return rows
 
 
+def oracle_table(target_s=8.0):
+    """Time the FP64 oracle (reported only, not a target) on every GEMM workload
+    with all the host's threads: whole products where they take a few seconds,
+    otherwise a sample of whole output rows sized to about ``target_s``; plus
+    single-thread times for the two smallest workloads."""
+    import numpy as np
+
+    import oracle
+    from fp32_gemm_08_amd.inputs import CONFIGS, make_config
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    print(f"| workload | threads | rows timed | seconds | GFLOP/s |")
+    print("|---|---|---|---|---|")
+    for name in CONFIGS:
+        case = make_config(name)
+        M, N, K = case.M, case.N, case.K
+        runs = [threads] + ([1] if name in ("c1_128", "c2_1024") else [])
+        for th in runs:
+            rng = np.random.default_rng(7)
+            rows = np.sort(rng.choice(M, size=min(M, th), replace=False))
+            t0 = time.perf_counter()
+            oracle.gemm_rows(M, N, K, case.alpha, case.A, case.B, case.trans_b, case.beta, case.C, rows=rows,
+                             nthreads=th)
+            per_row = (time.perf_counter() - t0) / len(rows) * th
+            n_rows = min(M, max(th, int(target_s * th / max(per_row, 1e-9)) // th * th))
+            rows = np.arange(M) if n_rows >= M else np.sort(rng.choice(M, size=n_rows, replace=False))
+            t0 = time.perf_counter()
+            _, _, used = oracle.gemm_rows(M, N, K, case.alpha, case.A, case.B, case.trans_b, case.beta, case.C,
+                                          rows=rows, nthreads=th)
+            t = time.perf_counter() - t0
+            print(f"| {name} {M}x{N}x{K} | {used} | {len(rows)} of {M} | {t:.2f} | "
+                  f"{2.0 * len(rows) * N * K / t / 1e9:.2f} |", flush=True)
+
+
 # Shapes for the MFMA tile-choice table: squares from 768 to 8192 and
 # rectangles whose tile counts fall just above or below a multiple of 256.
 TILE_SWEEP_SHAPES = [(n, n, n) for n in (768, 1024, 1280, 1536, 2048, 2560, 3072, 3584, 4096, 4608, 5120, 6144,
@@ -528,6 +561,8 @@ def main():
                     help="transpose: also time one source/destination pair repeated (cache-resident context)")
     ap.add_argument("--sweep", action="store_true",
                     help="time every algorithm on every workload and print a table (no JSON line)")
+    ap.add_argument("--oracle-table", action="store_true",
+                    help="time the FP64 oracle on every GEMM workload (CPU only, reported, no JSON line)")
     ap.add_argument("--tile-sweep", action="store_true",
                     help="time each fixed MFMA tile, AUTO and torch.mm over a spread of shapes (no JSON line)")
     args = ap.parse_args()
@@ -537,6 +572,10 @@ def main():
         print("bench.py measures one GPU only: there is no multi-GPU path (the GEMM would shard by "
               "rows of C with B replicated on every GPU). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.oracle_table:
+        oracle_table()
+        return
 
     import torch
 
