@@ -15,7 +15,7 @@
 //
 // Workgroup tile 256 x 256, 8 wavefronts as 4 (m) x 2 (n), each 64 x 128 =
 // 2 x 4 blocks of 32 x 32 (128 FP32 accumulators per lane), or for products
-// with fewer than 256 such tiles 64 x 64 with 2 wavefronts of 32 x 64.  k-tiles
+// with fewer than 128 such tiles 64 x 64 with 2 wavefronts of 32 x 64.  k-tiles
 // of 32.  LDS holds both operands k-contiguous as 16-bit values, A as
 // As[BM][40] and op(B) as Bs[BN][40] (n-major): 32 values per row plus 8 of padding, an
 // 80-byte pitch, so the 16-byte operand reads of 16 consecutive rows fall on
