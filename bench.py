@@ -477,10 +477,11 @@ def sweep_transpose():
 SPLITK_SHAPES = [("c1_128", None), ("c5_512", None), ("c2_1024", None), ("c3_ragged_bt", None),
                  ("768^3", (768, 768, 768)), ("1024x1024x4096", (1024, 1024, 4096)),
                  ("512x512x8192", (512, 512, 8192)), ("256x256x8192", (256, 256, 8192)),
-                 ("64x64x65536", (64, 64, 65536)), ("c5_2048", None)]
+                 ("256x256x32768", (256, 256, 32768)), ("512x256x16384", (512, 256, 16384)),
+                 ("384x384x8192", (384, 384, 8192)), ("64x64x65536", (64, 64, 65536)), ("c5_2048", None)]
 
 
-def sweep_splitk(splits_list=(1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 0)):
+def sweep_splitk(splits_list=(1, 2, 3, 4, 6, 7, 8, 12, 14, 16, 24, 32, 48, 64, 0)):
     """Time the k-split path for several split counts on the small and long-k
     workloads (both kernels, average over back-to-back calls)."""
     import torch

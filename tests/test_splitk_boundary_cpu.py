@@ -25,8 +25,11 @@ def built():
     ((1024, 1024, 1024), (1, KID_S, 0)),          # 256 tiles of 64 x 64
     ((512, 512, 512), (4, KID_S, 4 * 512 * 512 * 4)),
     ((768, 768, 768), (1, KID_S, 0)),              # 144 tiles: over half the CUs busy already
-    ((512, 512, 8192), (4, KID_S, 4 * 512 * 512 * 4)),
-    ((256, 256, 8192), (16, KID_S, 16 * 256 * 256 * 4)),
+    ((512, 512, 8192), (8, KID_S, 8 * 512 * 512 * 4)),       # two workgroups per CU, 1024 of k each
+    ((256, 256, 8192), (16, KID_S, 16 * 256 * 256 * 4)),     # two per CU would leave only 256 of k
+    ((256, 256, 32768), (32, KID_S, 32 * 256 * 256 * 4)),
+    ((512, 256, 16384), (16, KID_S, 16 * 512 * 256 * 4)),
+    ((384, 384, 8192), (7, KID_S, 7 * 384 * 384 * 4)),       # 36 tiles: 14 splits would get 585 of k
     ((64, 64, 65536), (64, KID_S, 64 * 64 * 64 * 4)),
     ((128, 128, 128), (1, KID_S, 0)),             # k too short to split at 256 per split
 ])

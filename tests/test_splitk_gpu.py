@@ -87,7 +87,7 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("splits", [2, 3, 5, 8, 16])
+@pytest.mark.parametrize("splits", [2, 3, 5, 8, 12, 16, 64])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"{s[0]}x{s[1]}x{s[2]}{'T' if s[3] else ''}")
 def test_split_parity(oracle_lib, shape, splits):
     M, N, K, tb, alpha, beta, extra = shape
