@@ -320,6 +320,93 @@ def transpose_cpu_baseline(src, rows, cols, D_gpu_host, target_s):
     }
 
 
+MFMA_PROBE_FLOP_PER_TRIP = 4 * 8 * 4096.0   # per workgroup: 4 wavefronts x 8 MFMAs x 4096 FLOP
+
+
+def probe_clock(lib, torch, dev, stream, workgroups=512, trips=2000, launches=3):
+    """Shader clock (MHz) right after the timed steps, read inside a kernel: the
+    library's matrix-core probe counts shader cycles against the constant
+    100 MHz counter on every workgroup.  (The driver's sysfs clock table lags
+    by about half a second, so it misreports a ~0.1 s run.)"""
+    sink = torch.empty(workgroups * 256, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(workgroups * 2, dtype=torch.int64, device=dev)
+    for _ in range(launches):
+        st = lib.sgemm_f32_mfma_probe(workgroups, trips, sink.data_ptr(), clocks.data_ptr(), stream.cuda_stream)
+        if st != 0:
+            return None
+    torch.cuda.synchronize()
+    c = clocks.cpu().view(workgroups, 2).double()
+    mhz = 100.0 * c[:, 0] / c[:, 1]
+    return {"mean": round(mhz.mean().item(), 1), "min": round(mhz.min().item(), 1),
+            "max": round(mhz.max().item(), 1),
+            "source": "shader cycles / 100 MHz ticks inside the library's MFMA probe, launched right after "
+                      "the timed steps (each workgroup's wavefront 0)"}
+
+
+def bench_mfma_ceiling(args):
+    """The FP32 matrix-core rate the device sustains with register operands
+    only (no memory traffic), against the published 157.3 TFLOP/s."""
+    import torch
+
+    import fp32_gemm_08_amd as lib
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream(dev)
+    workgroups, trips = 512, 20000      # 2 workgroups per CU: 2 wavefronts on every SIMD
+    sink = torch.empty(workgroups * 256, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(workgroups * 2, dtype=torch.int64, device=dev)
+
+    def launch():
+        st = lib.sgemm_f32_mfma_probe(workgroups, trips, sink.data_ptr(), clocks.data_ptr(), stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(lib.sgemm_f32_status_string(st))
+
+    for _ in range(max(args.warmup // 10, 5)):
+        launch()
+    torch.cuda.synchronize()
+    steps = max(args.steps // 5, 5)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    avg = e0.elapsed_time(e1) * 1e-3 / steps
+    flop = workgroups * trips * MFMA_PROBE_FLOP_PER_TRIP
+    c = clocks.cpu().view(workgroups, 2).double()
+    mhz = 100.0 * c[:, 0] / c[:, 1]
+    out = {
+        "metric": "FP32 matrix-core sustained TFLOP/s (register-only MFMA probe), 1 GPU",
+        "value": round(steps * flop / wall / 1e12, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "higher_is_better": True,
+        "kernel_avg_ms": round(avg * 1e3, 4),
+        "achieved": round(flop / avg / 1e12, 2), "peak": FP32_MFMA_PEAK_TFLOPS,
+        "frac": round(flop / avg / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
+        "config": {"workload": f"{workgroups} workgroups x 4 wavefronts x {trips * 8} v_mfma_f32_32x32x2_f32, "
+                               "random register operands", "flop_per_launch": flop},
+        "shader_clock_mhz": {"mean": round(mhz.mean().item(), 1), "min": round(mhz.min().item(), 1),
+                             "max": round(mhz.max().item(), 1)},
+        "device": device_record(torch, dev),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def device_record(torch, dev, clock=None):
+    """What the run ran on: device, compute units, memory, HIP/ROCm versions and
+    the shader clock read right after the timed steps."""
+    p = torch.cuda.get_device_properties(dev)
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    return {"arch": getattr(p, "gcnArchName", None), "name": p.name, "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2**30, 1), "hip": torch.version.hip, "rocm": rocm,
+            "shader_clock_mhz": clock}
+
+
 def _transpose_timed(lib, torch, algo_id, rows, cols, pairs, steps, warmup, stream):
     """Back-to-back transposes rotating over ``pairs``; returns (event span, wall)."""
     sp = stream.cuda_stream
@@ -379,6 +466,7 @@ def bench_transpose(args):
     if st != 0:
         raise SystemExit(f"plan failed: {lib.sgemm_f32_status_string(st)}")
     span, wall = _transpose_timed(lib, torch, algo, rows, cols, pairs, args.steps, args.warmup, stream)
+    clock = probe_clock(lib, torch, dev, stream)
     nbytes = 8.0 * rows * cols            # one read and one write of every element
     kern_avg = span / args.steps
     achieved = nbytes / kern_avg / 1e9
@@ -423,6 +511,7 @@ def bench_transpose(args):
             "kernel_avg_ms": round(kern_avg * 1e3, 5),
             "algorithmic_bytes_per_launch": nbytes,
         },
+        "device": device_record(torch, dev, clock),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -564,6 +653,9 @@ def main():
                     help="time every algorithm on every workload and print a table (no JSON line)")
     ap.add_argument("--oracle-table", action="store_true",
                     help="time the FP64 oracle on every GEMM workload (CPU only, reported, no JSON line)")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="time the library's register-only MFMA probe: the FP32 matrix-core rate the device "
+                         "sustains and its shader clock (one JSON line)")
     ap.add_argument("--tile-sweep", action="store_true",
                     help="time each fixed MFMA tile, AUTO and torch.mm over a spread of shapes (no JSON line)")
     args = ap.parse_args()
@@ -582,6 +674,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.mfma_ceiling:
+        bench_mfma_ceiling(args)
         return
     if args.op == "splitk":
         sweep_splitk()
@@ -693,6 +788,7 @@ def main():
     e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clock = probe_clock(lib, torch, dev, stream)
     span = e_start.elapsed_time(e_end) * 1e-3
     flop = 2.0 * M * N * K
     value = K_steps * flop / wall / 1e12
@@ -746,6 +842,7 @@ def main():
             "kernel_avg_ms": round(kern_avg * 1e3, 4),
             "algorithmic_flop_per_launch": flop,
         },
+        "device": device_record(torch, dev, clock),
         "cpu_baseline": None,
     }
     traffic = read_traffic() if (args.config == "c4_4096" and kid == 40) else None

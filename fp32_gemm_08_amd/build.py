@@ -22,7 +22,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsgemm_f32.so")
 
 SOURCES = ["sgemm_api.cpp", "k_naive.hip", "k_tiled.hip", "k_regblock.hip", "k_mfma.hip", "k_mfma_lp.hip", "k_lp16.hip", "k_splitk.hip",
-           "k_transpose.hip"]
+           "k_transpose.hip", "k_probe.hip"]
 ARCH = "gfx950"
 
 

@@ -4,6 +4,7 @@
 #include "sgemm_f32.h"
 #include "sgemm_internal.h"
 #include "transpose_internal.h"
+#include "probe_internal.h"
 
 #include <atomic>
 #include <cmath>
@@ -1087,5 +1088,21 @@ const char *sgemm_f32_status_string(int status)
 }
 
 const char *sgemm_f32_version(void) { return "sgemm_f32 0.1.0 (gfx950)"; }
+
+int sgemm_f32_mfma_probe(int64_t workgroups, int64_t trips, float *sink, unsigned long long *clocks, void *stream)
+{
+    if (workgroups < 1 || workgroups > (int64_t{1} << 20) || trips < 1 || trips > (int64_t{1} << 24) ||
+        sink == nullptr || clocks == nullptr)
+        return SGEMM_ERR_INVALID_VALUE;
+    if (sgemm::overlaps(sink, workgroups * 256 * (int64_t)sizeof(float), clocks,
+                        workgroups * 2 * (int64_t)sizeof(unsigned long long)))
+        return SGEMM_ERR_ALIAS;
+    const int dev_status = sgemm::check_device();
+    if (dev_status != SGEMM_OK)
+        return dev_status;
+    const hipError_t e = sgemm::launch_mfma_probe((int)workgroups, (int)trips, sink, clocks,
+                                                  reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
+}
 
 }  // extern "C"

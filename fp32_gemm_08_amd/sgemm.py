@@ -34,7 +34,7 @@ EXPORTS = ("sgemm_f32", "sgemm_f32_algo", "sgemm_f32_lowp", "sgemm_f32_lowp_2pas
            "sgemm_f32_lowp_plan", "sgemm_f32_lowp_ws",
            "sgemm_f32_lowp_ws_plan", "sgemm_f32_plan",
            "sgemm_f32_splitk", "sgemm_f32_splitk_plan",
-           "sgemm_f32_status_string", "sgemm_f32_streamk", "sgemm_f32_streamk_plan", "sgemm_f32_transpose",
+           "sgemm_f32_mfma_probe", "sgemm_f32_status_string", "sgemm_f32_streamk", "sgemm_f32_streamk_plan", "sgemm_f32_transpose",
            "sgemm_f32_transpose_algo", "sgemm_f32_transpose_plan", "sgemm_f32_version", "sgemm_f32_ws",
            "sgemm_f32_ws_plan")
 
@@ -112,6 +112,8 @@ def load():
         lib.sgemm_f32_status_string.argtypes = [ci]
         lib.sgemm_f32_version.restype = ctypes.c_char_p
         lib.sgemm_f32_version.argtypes = []
+        lib.sgemm_f32_mfma_probe.restype = ci
+        lib.sgemm_f32_mfma_probe.argtypes = [i64, i64, vp, vp, vp]
         _lib = lib
         return lib
 
@@ -262,6 +264,13 @@ def sgemm_f32_status_string(status: int) -> str:
 
 def sgemm_f32_version() -> str:
     return load().sgemm_f32_version().decode()
+
+
+def sgemm_f32_mfma_probe(workgroups, trips, sink, clocks, stream=0) -> int:
+    """Measurement aid: workgroups * 4 wavefronts each issue trips * 8 FP32
+    MFMAs (4096 FLOP each) on register operands; clocks receives (shader
+    cycles, 100 MHz ticks) per workgroup.  Returns the status code."""
+    return load().sgemm_f32_mfma_probe(workgroups, trips, sink, clocks, stream)
 
 
 def _check(status):

@@ -430,6 +430,33 @@ const char *sgemm_f32_status_string(int status);
 /* Static, NUL-terminated library version string. */
 const char *sgemm_f32_version(void);
 
+/*
+ * Measurement aid, not part of the GEMM: the FP32 matrix-core rate the device
+ * sustains and the shader clock it runs at.  The roofline of the GEMM is the
+ * matrix cores' peak ("CUDA矩阵乘法性能优化实战：从朴素内核到寄存器分块与Nsight剖析",
+ * section 1.2, places a kernel against the peak rate and the ridge point); the
+ * published figure is a clock times a unit count, and the Baidu Cloud page on
+ * naive versus 2-D tiled matrix multiplication (its migration advice on
+ * performance evaluation) asks for measurement on the target hardware rather
+ * than conclusions from theory alone.  It launches `workgroups` workgroups of
+ * four wavefronts; each wavefront issues trips * 8 v_mfma_f32_32x32x2_f32 on
+ * random operands in registers (4096 FLOP each; no memory traffic but the
+ * final stores), so one call performs workgroups * 4 * trips * 8 * 4096 FLOP.
+ * Wavefront 0 of workgroup w writes its elapsed shader cycles to clocks[2w] and
+ * elapsed ticks of the constant 100 MHz counter to clocks[2w+1] (shader clock
+ * in MHz = 100 * clocks[2w] / clocks[2w+1]); every work-item writes one float
+ * of its sums to sink (keeps the work live; the values carry no meaning).
+ *
+ * sink: DEVICE buffer of workgroups * 256 floats; clocks: DEVICE buffer of
+ * workgroups * 2 uint64; both owned by the caller, not overlapping
+ * (SGEMM_ERR_ALIAS).  workgroups in 1..2^20, trips in 1..2^24, else
+ * SGEMM_ERR_INVALID_VALUE (checked before any HIP call).  Enqueued on `stream`;
+ * SGEMM_ERR_NO_DEVICE / SGEMM_ERR_UNSUPPORTED_ARCH / SGEMM_ERR_LAUNCH as
+ * sgemm_f32.
+ */
+int sgemm_f32_mfma_probe(int64_t workgroups, int64_t trips, float *sink, unsigned long long *clocks,
+                         void *stream);
+
 #ifdef __cplusplus
 }
 #endif

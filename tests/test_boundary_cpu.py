@@ -201,3 +201,15 @@ def test_wave_per_output_has_no_grid_limit():
     # the kernel loops over outputs: 2^17 x 2^17 outputs are still accepted
     n = 1 << 17
     assert plan(algo=6, M=n, N=n, K=1, lda=1, ldb=n, ldc=n, C=1 << 50)[:2] == (OK, KID_NAIVE_WG)
+
+
+@pytest.mark.parametrize("wg,trips,sink,clocks,status", [
+    (0, 10, PA, PB, INVALID), (-1, 10, PA, PB, INVALID), ((1 << 20) + 1, 10, PA, PB, INVALID),
+    (4, 0, PA, PB, INVALID), (4, (1 << 24) + 1, PA, PB, INVALID),
+    (4, 10, 0, PB, INVALID), (4, 10, PA, 0, INVALID),
+    (4, 10, PA, PA + 4 * 256 * 4 - 8, ALIAS),      # clocks inside the sink
+    (4, 10, PB + 16, PB, ALIAS),                   # sink starts inside the clocks
+])
+def test_mfma_probe_rejects_bad_arguments(wg, trips, sink, clocks, status):
+    # every case is refused on the host, before any HIP call
+    assert lib.sgemm_f32_mfma_probe(wg, trips, sink, clocks, 0) == status
