@@ -760,7 +760,10 @@ Lp16Plan make_lp16_plan(bool forced, int tile_req, int precision, int64_t M, int
     lp.large = tile_req == 0 ? ceil_div(M, tl.bm) * ceil_div(N, tl.bn) >= 128 : tile_req == 256;
     const TileShape t = lp16_tile_shape(lp.large);
     const int64_t tiles = ceil_div(M, t.bm) * ceil_div(N, t.bn);
-    if (tiles * (lp.large ? 512 : 256) > kMaxWorkItems || ceil_div(K, 32) * 32 > std::numeric_limits<int>::max()) {
+    // the rounding transpose of op(B) = B launches ceil(K / 64) workgroup rows
+    // (a grid's y extent is at most 65535)
+    if (tiles * (lp.large ? 512 : 256) > kMaxWorkItems || ceil_div(K, 32) * 32 > std::numeric_limits<int>::max() ||
+        ceil_div(K, 64) > 65535) {
         if (forced) {
             lp.base.status = SGEMM_ERR_INVALID_VALUE;
             lp.base.kid = KID_NONE;

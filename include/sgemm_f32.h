@@ -293,15 +293,17 @@ int sgemm_f32_lowp_ws(int precision, int64_t M, int64_t N, int64_t K, float alph
  * 256 x 256 tiles, chosen when there are at least 128 of them; 66/67: 128 x
  * 128 tiles; otherwise the one-pass call's id: the two passes run for products
  * of at least 1e10 FLOPs, or 1e9 when M or N is not a multiple of 64 or K of
- * 32, where they measured faster), the output tiles and the workspace bytes
- * (0 when the one-pass call runs).  Output pointers may be NULL. */
+ * 32, where they measured faster, and K <= 64 * 65535 = 4,194,240; longer K
+ * runs the one-pass call), the output tiles and the workspace bytes (0 when
+ * the one-pass call runs).  Output pointers may be NULL. */
 int sgemm_f32_lowp_ws_plan(int precision, int64_t M, int64_t N, int64_t K, int transB, int *kernel_id,
                            int64_t *tiles_m, int64_t *tiles_n, int64_t *workspace_bytes);
 
 /* The two passes whatever the size (`tile`: 0 = the rule above, 256 or 128 =
  * that tile; anything else SGEMM_ERR_INVALID_VALUE), for callers that want
  * them and for testing them at every shape.  A workspace smaller than
- * sgemm_f32_lowp_2pass_plan reports is SGEMM_ERR_INVALID_VALUE. */
+ * sgemm_f32_lowp_2pass_plan reports, or K above 4,194,240, is
+ * SGEMM_ERR_INVALID_VALUE. */
 int sgemm_f32_lowp_2pass(int precision, int tile, int64_t M, int64_t N, int64_t K, float alpha,
                          const float *A, int64_t lda, const float *B, int64_t ldb, int transB,
                          float beta, float *C, int64_t ldc,

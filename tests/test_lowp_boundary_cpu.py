@@ -134,3 +134,14 @@ def test_2pass_small_workspace():
                                     need - 1, 0) == INVALID
     assert lib.sgemm_f32_lowp_2pass(2, 0, 300, 200, 50, 1.0, PA, 50, PB, 200, 0, 0.0, PC, 200, 0,
                                     need, 0) == INVALID
+
+
+def test_two_passes_stop_at_the_grid_limit_in_k():
+    # the rounding transpose launches ceil(K / 64) workgroup rows, at most 65535
+    kmax = 64 * 65535
+    st, kid, _, _, need = lib.sgemm_f32_lowp_ws_plan(2, 2048, 2048, kmax, 0)
+    assert st == OK and kid == KID_Q_BF16_S and need > 0
+    st, kid, _, _, need = lib.sgemm_f32_lowp_ws_plan(2, 2048, 2048, kmax + 1, 0)
+    assert st == OK and kid == KID_LP_BF16_S and need == 0      # the one-pass call
+    assert lib.sgemm_f32_lowp_2pass_plan(2, 0, 256, 256, kmax + 1, 0)[0] == INVALID
+    assert lib.sgemm_f32_lowp_2pass_plan(2, 0, 256, 256, kmax, 0)[0] == OK
