@@ -323,6 +323,18 @@ def transpose_cpu_baseline(src, rows, cols, D_gpu_host, target_s):
 MFMA_PROBE_FLOP_PER_TRIP = 4 * 8 * 4096.0   # per workgroup: 4 wavefronts x 8 MFMAs x 4096 FLOP
 
 
+def per_call_times(torch, stream, call, n=20):
+    """n calls, each between its own pair of events on the launch stream (the
+    gap an event adds stays outside every span): sorted seconds per call."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return sorted(e0.elapsed_time(e1) * 1e-3 for e0, e1 in evs)
+
+
 def probe_clock(lib, torch, dev, stream, workgroups=512, trips=2000, launches=3):
     """Shader clock (MHz) right after the timed steps, read inside a kernel: the
     library's matrix-core probe counts shader cycles against the constant
@@ -788,6 +800,7 @@ def main():
     e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    per_call = per_call_times(torch, stream, step)
     clock = probe_clock(lib, torch, dev, stream)
     span = e_start.elapsed_time(e_end) * 1e-3
     flop = 2.0 * M * N * K
@@ -841,6 +854,11 @@ def main():
             "traffic": None,
             "kernel_avg_ms": round(kern_avg * 1e3, 4),
             "algorithmic_flop_per_launch": flop,
+            # after the timed steps: 20 more calls, each between its own events
+            "per_call": {"calls": len(per_call), "median_ms": round(per_call[len(per_call) // 2] * 1e3, 4),
+                         "best_ms": round(per_call[0] * 1e3, 4),
+                         "median_tflops": round(flop / per_call[len(per_call) // 2] / 1e12, 3),
+                         "best_tflops": round(flop / per_call[0] / 1e12, 3)},
         },
         "device": device_record(torch, dev, clock),
         "cpu_baseline": None,
