@@ -5,10 +5,10 @@
 
 A step is one call of the C ABI (``sgemm_f32``) over the whole workload, inputs
 already resident in HBM.  The default workload is 4096x4096x4096, C = A*B,
-alpha=1, beta=0, A and B uniform[-1,1) from seed 3.  W untimed warm-up calls,
-then exactly K timed calls bracketed by device synchronisation (the defaults,
-200 and 100, let the engine clock settle first: the first ~30 calls of a cold
-GPU run measurably slower); the JSON line
+alpha=1, beta=0, A and B uniform[-1,1) from seed 3.  W untimed warm-up calls
+(default: at least 200 and at least 0.4 s of device time, so the engine clock
+has reached its loaded state; the line reports the count run), then exactly K
+timed calls (default 100) bracketed by device synchronisation; the JSON line
 on stdout carries the throughput, the dominant kernel's roofline position
 (its own average duration measured with events on the launch stream) and the
 FP64 CPU oracle's rate on a bounded sample of the same workload.
@@ -323,6 +323,30 @@ def transpose_cpu_baseline(src, rows, cols, D_gpu_host, target_s):
 MFMA_PROBE_FLOP_PER_TRIP = 4 * 8 * 4096.0   # per workgroup: 4 wavefronts x 8 MFMAs x 4096 FLOP
 
 
+WARMUP_MIN_CALLS = 200
+WARMUP_MIN_SECONDS = 0.4
+
+
+def warm_up(torch, call, warmup):
+    """Untimed calls before the timed ones.  With an explicit count, exactly
+    that many.  Without one (the default), at least WARMUP_MIN_CALLS and at
+    least WARMUP_MIN_SECONDS of device time: the engine clock takes a few
+    hundred milliseconds of load to reach its steady state (a 1024^3 step is
+    23 us, so 200 steps alone would leave it ~10% low).  Returns the count run."""
+    if warmup is not None:
+        for i in range(warmup):
+            call(i)
+        torch.cuda.synchronize()
+        return warmup
+    n, t0 = 0, time.perf_counter()
+    while n < WARMUP_MIN_CALLS or time.perf_counter() - t0 < WARMUP_MIN_SECONDS:
+        for _ in range(50):
+            call(n)
+            n += 1
+        torch.cuda.synchronize()          # the wall clock then tracks the device
+    return n
+
+
 def per_call_times(torch, stream, call, n=20):
     """n calls, each between its own pair of events on the launch stream (the
     gap an event adds stays outside every span): sorted seconds per call."""
@@ -372,7 +396,7 @@ def bench_mfma_ceiling(args):
         if st != 0:
             raise RuntimeError(lib.sgemm_f32_status_string(st))
 
-    for _ in range(max(args.warmup // 10, 5)):
+    for _ in range(max((args.warmup or 200) // 10, 5)):
         launch()
     torch.cuda.synchronize()
     steps = max(args.steps // 5, 5)
@@ -420,7 +444,8 @@ def device_record(torch, dev, clock=None):
 
 
 def _transpose_timed(lib, torch, algo_id, rows, cols, pairs, steps, warmup, stream):
-    """Back-to-back transposes rotating over ``pairs``; returns (event span, wall)."""
+    """Back-to-back transposes rotating over ``pairs``; returns (event span, wall,
+    warm-up calls run)."""
     sp = stream.cuda_stream
     R = len(pairs)
 
@@ -430,9 +455,7 @@ def _transpose_timed(lib, torch, algo_id, rows, cols, pairs, steps, warmup, stre
         if s != 0:
             raise RuntimeError(lib.sgemm_f32_status_string(s))
 
-    for k in range(warmup):
-        step(k)
-    torch.cuda.synchronize()
+    warmed = warm_up(torch, step, warmup)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -441,7 +464,7 @@ def _transpose_timed(lib, torch, algo_id, rows, cols, pairs, steps, warmup, stre
         step(k)
     e1.record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e-3, time.perf_counter() - t0
+    return e0.elapsed_time(e1) * 1e-3, time.perf_counter() - t0, warmed
 
 
 def _rotation(torch, src_host, rows, cols, dev, min_bytes=1 << 30):
@@ -469,7 +492,8 @@ def bench_transpose(args):
     algo = lib.TRANSPOSE_ALGO[algo_name]
     cfg = TRANSPOSE_CONFIGS[name]
     rows, cols = cfg["rows"], cfg["cols"]
-    log(f"bench transpose: config={name} algo={algo_name} steps={args.steps} warmup={args.warmup}")
+    log(f"bench transpose: config={name} algo={algo_name} steps={args.steps} "
+        f"warmup={args.warmup if args.warmup is not None else 'auto'}")
     src = make_transpose_config(name)
     pairs = _rotation(torch, src, rows, cols, dev)
     stream = torch.cuda.current_stream(dev)
@@ -477,7 +501,7 @@ def bench_transpose(args):
                                                           pairs[0][1].data_ptr(), rows)
     if st != 0:
         raise SystemExit(f"plan failed: {lib.sgemm_f32_status_string(st)}")
-    span, wall = _transpose_timed(lib, torch, algo, rows, cols, pairs, args.steps, args.warmup, stream)
+    span, wall, warmed = _transpose_timed(lib, torch, algo, rows, cols, pairs, args.steps, args.warmup, stream)
     clock = probe_clock(lib, torch, dev, stream)
     nbytes = 8.0 * rows * cols            # one read and one write of every element
     kern_avg = span / args.steps
@@ -488,7 +512,7 @@ def bench_transpose(args):
     if args.same_pair:
         # Context only: the same transpose repeated on one pair (source and
         # destination then stay in the Infinity Cache between calls).
-        span1, _ = _transpose_timed(lib, torch, algo, rows, cols, pairs[:1], args.steps, 20, stream)
+        span1, _, _ = _transpose_timed(lib, torch, algo, rows, cols, pairs[:1], args.steps, 20, stream)
         same_pair = round(nbytes / (span1 / args.steps) / 1e9, 1)
         log(f"one pair repeated: {span1 / args.steps * 1e6:.2f} us")
     D_host = pairs[0][1].cpu().numpy()
@@ -498,7 +522,7 @@ def bench_transpose(args):
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warmed,
         "ms_per_step": round(wall / args.steps * 1e3, 5),
         "higher_is_better": True,
         "scaling": "strong",
@@ -549,8 +573,8 @@ def sweep_transpose():
             a = lib.TRANSPOSE_ALGO[algo_name]
             _, _, _, kname = lib.sgemm_f32_transpose_plan(a, rows, cols, pairs[0][0].data_ptr(), cols,
                                                           pairs[0][1].data_ptr(), rows)
-            span, _ = _transpose_timed(lib, torch, a, rows, cols, pairs, 200, 100, stream)
-            span1, _ = _transpose_timed(lib, torch, a, rows, cols, pairs[:1], 200, 20, stream)
+            span, _, _ = _transpose_timed(lib, torch, a, rows, cols, pairs, 200, 100, stream)
+            span1, _, _ = _transpose_timed(lib, torch, a, rows, cols, pairs[:1], 200, 20, stream)
             t, t1 = span / 200, span1 / 200
             print(f"| {name} {rows}x{cols} | {algo_name} | {kname} | {len(pairs)} | {t * 1e6:.2f} | "
                   f"{nbytes / t / 1e9:.0f} | {100 * nbytes / t / 1e9 / HBM_PEAK_GBS:.1f} | {t1 * 1e6:.2f} | "
@@ -642,8 +666,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=200,
-                    help="untimed calls first; the clock needs ~0.1 s of load to reach its steady state")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed calls first (default: at least 200 and at least 0.4 s of device time, "
+                         "so the engine clock reaches its loaded state; the JSON line reports the count run)")
     ap.add_argument("--op", choices=("gemm", "transpose", "splitk"), default="gemm",
                     help="splitk: table of the k-split path over split counts (no JSON line)")
     ap.add_argument("--config", default="c4_4096",
@@ -713,7 +738,8 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda", 0)
-    log(f"bench: config={args.config} algo={args.algo} steps={args.steps} warmup={args.warmup}")
+    log(f"bench: config={args.config} algo={args.algo} steps={args.steps} "
+        f"warmup={args.warmup if args.warmup is not None else 'auto'}")
     case = make_config(args.config)
     M, N, K = case.M, case.N, case.K
     dA = torch.from_numpy(case.A).to(dev)
@@ -781,9 +807,7 @@ def main():
         if s != 0:
             raise RuntimeError(lib.sgemm_f32_status_string(s))
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warmed = warm_up(torch, lambda i: step(), args.warmup)
 
     # Timed region: exactly K back-to-back calls on one stream, events at its two
     # ends only (an event between launches inserts a gap of its own).  The
@@ -804,6 +828,7 @@ def main():
     clock = probe_clock(lib, torch, dev, stream)
     span = e_start.elapsed_time(e_end) * 1e-3
     flop = 2.0 * M * N * K
+    hbm_bytes = 4.0 * (M * K + K * N + M * N + (M * N if case.beta != 0.0 else 0))
     value = K_steps * flop / wall / 1e12
     kern_avg = span / K_steps
     achieved = flop / kern_avg / 1e12
@@ -828,7 +853,7 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": K_steps,
-        "warmup": args.warmup,
+        "warmup": warmed,
         "ms_per_step": round(wall / K_steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "strong",
@@ -854,6 +879,14 @@ def main():
             "traffic": None,
             "kernel_avg_ms": round(kern_avg * 1e3, 4),
             "algorithmic_flop_per_launch": flop,
+            # the same launches against the HBM roofline: compulsory bytes (A and B
+            # read once, C written once, and read once when beta != 0) over the
+            # average launch; the bound on the small shapes, whose FLOP per byte
+            # sits near the ridge (157.3 TFLOP/s / 8 TB/s = 19.7)
+            "hbm": {"algorithmic_bytes_per_launch": hbm_bytes,
+                    "flop_per_byte": round(flop / hbm_bytes, 2),
+                    "achieved_gbs": round(hbm_bytes / kern_avg / 1e9, 1), "peak_gbs": HBM_PEAK_GBS,
+                    "frac": round(hbm_bytes / kern_avg / 1e9 / HBM_PEAK_GBS, 4)},
             # after the timed steps: 20 more calls, each between its own events
             "per_call": {"calls": len(per_call), "median_ms": round(per_call[len(per_call) // 2] * 1e3, 4),
                          "best_ms": round(per_call[0] * 1e3, 4),
