@@ -172,6 +172,7 @@ def sweep(algos=("naive", "naive_wg", "lds_tiled", "lds_tiled_nopad", "regblock"
                 if s != 0:
                     raise RuntimeError(lib.sgemm_f32_status_string(s))
 
+            settle(torch, call, 0.2)
             for _ in range(max(2, reps // 4)):
                 call()
             e0 = torch.cuda.Event(enable_timing=True)
@@ -252,6 +253,7 @@ def sweep_tiles():
     g.manual_seed(11)
 
     def timeit(fn, reps):
+        settle(torch, fn, 0.2)
         for _ in range(max(3, reps // 5)):
             fn()
         e0 = torch.cuda.Event(enable_timing=True)
@@ -345,6 +347,20 @@ def warm_up(torch, call, warmup):
             n += 1
         torch.cuda.synchronize()          # the wall clock then tracks the device
     return n
+
+
+def settle(torch, call, seconds=0.3):
+    """Run `call` back to back for about `seconds` of device time, so that the
+    measurements that follow start at the engine clock of a loaded GPU (a pause
+    on the host, e.g. generating the next workload, lets it drop)."""
+    t0, batch = time.perf_counter(), 1
+    while True:
+        for _ in range(batch):
+            call()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return
+        batch = min(2 * batch, 64)        # one call first: some stages take a second per call
 
 
 def per_call_times(torch, stream, call, n=20):
@@ -645,6 +661,7 @@ def sweep_splitk(splits_list=(1, 2, 3, 4, 6, 7, 8, 12, 14, 16, 24, 32, 48, 64, 0
                     raise RuntimeError(lib.sgemm_f32_status_string(st))
 
             reps = int(max(10, min(300, 0.1 / max(flop / 60e12, 2e-6))))
+            settle(torch, call, 0.2)
             for _ in range(max(5, reps // 4)):
                 call()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
