@@ -672,7 +672,7 @@ def sweep_splitk(splits_list=(1, 2, 3, 4, 6, 7, 8, 12, 14, 16, 24, 32, 48, 64, 0
             e1.record(stream)
             torch.cuda.synchronize()
             t = e0.elapsed_time(e1) * 1e-3 / reps
-            kname = {40: "mfma 256x256", 41: "mfma 128x128 ks2", 42: "mfma 64x64"}.get(kid, str(kid))
+            kname = {40: "mfma 256x256", 41: "mfma 128x128 ks2", 42: "mfma 64x64", 45: "mfma 64x64 ks2"}.get(kid, str(kid))
             print(f"| {name} {M}x{N}x{K} | {sp if sp else 'auto'} | {used} | {kname} | {nb / 2**20:.1f} | "
                   f"{t * 1e6:.2f} | {flop / t / 1e12:.2f} |", flush=True)
         del dA, dB, dC, ws
@@ -849,7 +849,7 @@ def main():
     value = K_steps * flop / wall / 1e12
     kern_avg = span / K_steps
     achieved = flop / kern_avg / 1e12
-    mfma = kid in (40, 41, 42, 43, 44, 60, 61, 62, 63, 64, 65, 66, 67)
+    mfma = kid in (40, 41, 42, 43, 44, 45, 60, 61, 62, 63, 64, 65, 66, 67)
     peak = HALF_MFMA_PEAK_TFLOPS if lowp else FP32_MFMA_PEAK_TFLOPS if mfma else FP32_VALU_PEAK_TFLOPS
     log(f"{'step (both kernels)' if ws is not None else 'kernel'} {kname}: avg {kern_avg * 1e3:.4f} ms "
         f"over {K_steps} calls "

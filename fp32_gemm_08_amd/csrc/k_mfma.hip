@@ -911,7 +911,8 @@ TileShape tile_shape(int kid)
     switch (kid) {
     case KID_MFMA_L: return {256, 256};
     case KID_MFMA_M: return {128, 128};
-    case KID_MFMA_S: return {64, 64};
+    case KID_MFMA_S:
+    case KID_MFMA_S2: return {64, 64};
     case KID_REGBLOCK: return {128, 128};
     case KID_TILED_PAD:
     case KID_TILED_NOPAD: return {16, 16};
@@ -998,6 +999,7 @@ hipError_t launch_mfma(const GemmArgs &a, int kid, bool transB, bool vec, hipStr
     case KID_MFMA_L: launch_cfg<256, 256, 32, 16, 4, 2, 2, 1>(a, transB, vec, stream, splits); break;
     case KID_MFMA_M: launch_cfg<128, 128, 32, 32, 2, 2, 2, 2>(a, transB, vec, stream, splits); break;
     case KID_MFMA_S: launch_cfg<64, 64, 32, 32, 2, 2, 4, 1>(a, transB, vec, stream, splits); break;
+    case KID_MFMA_S2: launch_cfg<64, 64, 32, 32, 2, 2, 2, 2>(a, transB, vec, stream, splits); break;
 #else
     SGEMM_MFMA_EXPERIMENT
 #endif

@@ -76,6 +76,12 @@ double mfma_rate(int kid, int64_t M, int64_t N)
     return r * (tiles / 256.0) / c * ((double)M * (double)N / (tiles * t.bm * t.bn));
 }
 
+// The FP32 MFMA kernels of the plain call.
+bool is_mfma_f32(int kid)
+{
+    return kid == KID_MFMA_L || kid == KID_MFMA_M || kid == KID_MFMA_S || kid == KID_MFMA_S2;
+}
+
 int choose_mfma(int64_t M, int64_t N)
 {
     const int kids[3] = {KID_MFMA_L, KID_MFMA_M, KID_MFMA_S};
@@ -91,6 +97,16 @@ int choose_mfma(int64_t M, int64_t N)
             best_rate = r;
             best = kid;
         }
+    }
+    // Within the 64 x 64 tile, the 8-wavefront variant (k split two ways in
+    // the workgroup) measured 1.5-5% faster on MI355X except when the grid is
+    // 257 to 512 tiles: the 4-wavefront workgroups then all run at once, two
+    // per CU, where the 8-wavefront ones take a second, partial round (1280^3:
+    // 97 against 90 TFLOP/s; 3584^3: 115 against 121).
+    if (best == KID_MFMA_S) {
+        const int64_t tiles = ceil_div(M, 64) * ceil_div(N, 64);
+        if ((tiles <= 256 || tiles > 512) && tiles * 512 <= kMaxWorkItems)
+            best = KID_MFMA_S2;
     }
     return best;
 }
@@ -133,7 +149,7 @@ int64_t auto_splits(int64_t M, int64_t N, int64_t K)
 
 int threads_per_block(int kid)
 {
-    return (kid == KID_MFMA_L || kid == KID_MFMA_M) ? 512 : 256;
+    return (kid == KID_MFMA_L || kid == KID_MFMA_M || kid == KID_MFMA_S2) ? 512 : 256;
 }
 
 Plan make_plan(int algo, int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
@@ -271,6 +287,7 @@ const char *kernel_label(int kid)
     case KID_MFMA_L: return "mfma_256x256x32_w4x2";
     case KID_MFMA_M: return "mfma_128x128x32_w2x2_ks2";
     case KID_MFMA_S: return "mfma_64x64x32_w2x2";
+    case KID_MFMA_S2: return "mfma_64x64x32_w2x2_ks2";
     case KID_MFMA_L_SK: return "mfma_256x256x32_w4x2_streamk";
     case KID_MFMA_M_SK: return "mfma_128x128x32_w2x2_ks2_streamk";
     case KID_MFMA_LP_F16: return "mfma_lp_f16_256x256x32_w4x2";
@@ -378,7 +395,7 @@ SplitPlan make_split_plan(int64_t splits_req, int64_t M, int64_t N, int64_t K, f
     if (splits_req < 0 || splits_req > kMaxSplits || ws_bytes < 0)
         return fail(SGEMM_ERR_INVALID_VALUE);
     sp.kid = sp.base.kid;
-    const bool mfma = sp.base.kid == KID_MFMA_L || sp.base.kid == KID_MFMA_M || sp.base.kid == KID_MFMA_S;
+    const bool mfma = is_mfma_f32(sp.base.kid);
     if (sp.base.status != SGEMM_OK || !mfma)
         return sp;  // errors, quick returns and the product-free cases are the plain call's
     const int64_t want = splits_req == 0 ? auto_splits(M, N, K) : splits_req;
@@ -528,7 +545,7 @@ SkPlan make_sk_plan(int tile_req, int64_t M, int64_t N, int64_t K, float alpha, 
         sp.base.kid = KID_NONE;
         return sp;
     }
-    const bool mfma = base.kid == KID_MFMA_L || base.kid == KID_MFMA_M || base.kid == KID_MFMA_S;
+    const bool mfma = is_mfma_f32(base.kid);
     if (base.status != SGEMM_OK || !mfma)
         return sp;  // errors, quick returns and the product-free cases are the plain call's
     if (tile_req == 256)
@@ -665,7 +682,7 @@ Plan make_lowp_plan(int precision, int64_t M, int64_t N, int64_t K, float alpha,
         return p;
     }
     Plan p = make_plan(SGEMM_ALGO_AUTO, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc);
-    if (p.status != SGEMM_OK || !(p.kid == KID_MFMA_L || p.kid == KID_MFMA_M || p.kid == KID_MFMA_S))
+    if (p.status != SGEMM_OK || !is_mfma_f32(p.kid))
         return p;
     // the 256 x 256 tile once it keeps at least half of the 256 CUs busy, else 64 x 64
     const TileShape tl = lp_tile_shape(true);

@@ -19,7 +19,7 @@ HEADER = os.path.join(ROOT, "include", "sgemm_f32.h")
 OK, INVALID, ALIAS = 0, 1, 2
 KID_NONE, KID_SCALE, KID_NAIVE, KID_TILED, KID_TILED_NOPAD, KID_REG = 0, 1, 10, 20, 21, 30
 KID_NAIVE_WG = 11
-KID_L, KID_M, KID_S = 40, 41, 42
+KID_L, KID_M, KID_S, KID_S2 = 40, 41, 42, 45
 
 # Fake, well-separated "device" addresses: planning only compares ranges.
 PA, PB, PC = 1 << 32, 1 << 40, 1 << 44
@@ -151,11 +151,17 @@ def test_explicit_algorithms(algo, kid):
     ((8192, 8192, 8192), KID_L, (32, 32)),
     ((16384, 4096, 1024), KID_L, (64, 16)),
     ((2048, 2048, 2048), KID_M, (16, 16)),
-    ((1024, 1024, 1024), KID_S, (16, 16)),
-    ((1000, 1017, 999), KID_S, (16, 16)),
-    ((512, 512, 512), KID_S, (8, 8)),
-    ((128, 128, 128), KID_S, (2, 2)),
-    ((1, 1, 1), KID_S, (1, 1)),
+    # the 64 x 64 tile: 8 wavefronts (k split in two) unless the grid is 257..512 tiles
+    ((1024, 1024, 1024), KID_S2, (16, 16)),
+    ((1000, 1017, 999), KID_S2, (16, 16)),
+    ((512, 512, 512), KID_S2, (8, 8)),
+    ((128, 128, 128), KID_S2, (2, 2)),
+    ((1, 1, 1), KID_S2, (1, 1)),
+    ((1280, 1280, 1280), KID_S, (20, 20)),     # 400 tiles
+    ((512, 4096, 4096), KID_S, (8, 64)),       # 512 tiles
+    ((576, 4096, 1024), KID_S2, (9, 64)),      # 576 tiles
+    ((3584, 3584, 3584), KID_S2, (56, 56)),
+    ((4608, 4608, 4608), KID_S2, (72, 72)),
 ])
 def test_auto_tile_choice(shape, kid, tiles):
     M, N, K = shape

@@ -212,11 +212,15 @@ def test_mid_tile_integers_bit_exact(oracle_lib):
 # N, for each MFMA tile (forced with its fixed-tile algorithm).  Edge tiles stage directly with clamped rows
 # (op(B) = B^T, or op(B) = B with N % 4 == 0) or through masked registers
 # (op(B) = B with N % 4 != 0); K tails on some.
-TILE_ALGO = {40: "mfma_256", 41: "mfma_128", 42: "mfma_64"}
+# Kernel 45, the 64 x 64 tile as 8 wavefronts (two k-slices), runs where AUTO
+# picks the 64 x 64 tile on a grid of at most 256 (or over 512) tiles.
+TILE_ALGO = {40: "mfma_256", 41: "mfma_128", 42: "mfma_64", 45: "auto"}
 EDGE_SHAPES = [(1000, 1000, 1024, 0, 42), (1000, 1000, 1024, 1, 42), (1000, 1004, 999, 0, 42),
                (1003, 1001, 1000, 1, 42), (1001, 1003, 1000, 0, 42), (2000, 2052, 1000, 0, 41),
                (2001, 1999, 777, 1, 41), (3999, 4000, 512, 0, 40), (4000, 3998, 520, 1, 40),
-               (4001, 4003, 300, 0, 40)]
+               (4001, 4003, 300, 0, 40), (1000, 1000, 1024, 0, 45), (1000, 1000, 1024, 1, 45),
+               (1000, 1004, 999, 0, 45), (1003, 1001, 1000, 1, 45), (1001, 1003, 1000, 0, 45),
+               (2237, 2243, 509, 1, 45)]
 
 
 @pytest.mark.parametrize("shape", EDGE_SHAPES, ids=lambda s: "x".join(str(v) for v in s[:4]))
@@ -240,7 +244,8 @@ def test_edge_tiles_aligned(oracle_lib, shape):
 # off by one float): the 64x64 and 128x128 tiles stage them with 4-byte direct
 # loads (edges clamped per element), the 256x256 tile through masked registers.
 UNALIGNED_SHAPES = [(1000, 1017, 999, 1, 0, 42), (1001, 1003, 1000, 0, 0, 42), (1000, 1000, 1024, 0, 1, 42),
-                    (2001, 1999, 777, 1, 0, 41), (2048, 2050, 1001, 0, 1, 41), (3999, 4001, 501, 0, 0, 40)]
+                    (2001, 1999, 777, 1, 0, 41), (2048, 2050, 1001, 0, 1, 41), (3999, 4001, 501, 0, 0, 40),
+                    (1000, 1017, 999, 1, 0, 45), (1001, 1003, 1000, 0, 0, 45), (1000, 1000, 1024, 0, 1, 45)]
 
 
 @pytest.mark.parametrize("shape", UNALIGNED_SHAPES, ids=lambda s: "x".join(str(v) for v in s[:5]))
@@ -258,7 +263,7 @@ def test_unaligned_operands(oracle_lib, shape):
     assert_parity(Dg[rows, :N], D, S, K, f"unaligned {M}x{N}x{K} t{t} a_off={a_off}")
 
 
-@pytest.mark.parametrize("algo", ["mfma_256", "mfma_128", "mfma_64"])
+@pytest.mark.parametrize("algo", ["mfma_256", "mfma_128", "mfma_64", "auto"])
 @pytest.mark.parametrize("t", [0, 1])
 def test_unaligned_integers_bit_exact(oracle_lib, t, algo):
     case = make_case(1003, 1001, 999, trans_b=t, alpha=1.0, beta=1.0, dist="int2", seed=23)
@@ -268,7 +273,7 @@ def test_unaligned_integers_bit_exact(oracle_lib, t, algo):
     assert np.array_equal(Dg[:, :1001], D.astype(np.float32))
 
 
-@pytest.mark.parametrize("algo", ["mfma_256", "mfma_128", "mfma_64"])
+@pytest.mark.parametrize("algo", ["mfma_256", "mfma_128", "mfma_64", "auto"])
 @pytest.mark.parametrize("t", [0, 1])
 def test_edge_tiles_integers_bit_exact(oracle_lib, t, algo):
     case = make_case(1003, 1004, 1000, trans_b=t, alpha=1.0, beta=1.0, dist="int2", seed=19)
