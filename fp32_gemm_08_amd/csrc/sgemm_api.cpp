@@ -82,7 +82,7 @@ bool is_mfma_f32(int kid)
     return kid == KID_MFMA_L || kid == KID_MFMA_M || kid == KID_MFMA_S || kid == KID_MFMA_S2;
 }
 
-int choose_mfma(int64_t M, int64_t N)
+int choose_mfma(int64_t M, int64_t N, int64_t K)
 {
     const int kids[3] = {KID_MFMA_L, KID_MFMA_M, KID_MFMA_S};
     int best = KID_MFMA_L;
@@ -102,10 +102,12 @@ int choose_mfma(int64_t M, int64_t N)
     // the workgroup) measured 1.5-5% faster on MI355X except when the grid is
     // 257 to 512 tiles: the 4-wavefront workgroups then all run at once, two
     // per CU, where the 8-wavefront ones take a second, partial round (1280^3:
-    // 97 against 90 TFLOP/s; 3584^3: 115 against 121).
+    // 97 against 90 TFLOP/s; 3584^3: 115 against 121); and with K below 256,
+    // where each half has too few k-steps to pay for adding the halves (128^3:
+    // 4.4 against 4.7 us).
     if (best == KID_MFMA_S) {
         const int64_t tiles = ceil_div(M, 64) * ceil_div(N, 64);
-        if ((tiles <= 256 || tiles > 512) && tiles * 512 <= kMaxWorkItems)
+        if ((tiles <= 256 || tiles > 512) && K >= 256 && tiles * 512 <= kMaxWorkItems)
             best = KID_MFMA_S2;
     }
     return best;
@@ -203,7 +205,7 @@ Plan make_plan(int algo, int64_t M, int64_t N, int64_t K, float alpha, const flo
     case SGEMM_ALGO_LDS_TILED_NOPAD: p.kid = KID_TILED_NOPAD; break;
     case SGEMM_ALGO_REGBLOCK: p.kid = KID_REGBLOCK; break;
     case SGEMM_ALGO_MFMA:
-    case SGEMM_ALGO_AUTO: p.kid = choose_mfma(M, N); break;
+    case SGEMM_ALGO_AUTO: p.kid = choose_mfma(M, N, K); break;
     case SGEMM_ALGO_MFMA_256: p.kid = KID_MFMA_L; break;
     case SGEMM_ALGO_MFMA_128: p.kid = KID_MFMA_M; break;
     case SGEMM_ALGO_MFMA_64: p.kid = KID_MFMA_S; break;
@@ -518,7 +520,7 @@ SkPlan sk_schedule(const Plan &base, int kid, int64_t M, int64_t N, int64_t K)
 // the two stream-K tiles came within 1.5% of the fastest every time.
 double plain_time_us(int64_t M, int64_t N, int64_t K)
 {
-    const int kid = choose_mfma(M, N);
+    const int kid = choose_mfma(M, N, K);
     return 2.0 * (double)M * (double)N * (double)K / (mfma_rate(kid, M, N) * 1e6);
 }
 

@@ -101,8 +101,9 @@ typedef enum {
  *                    64 x 64 (4 wavefronts, up to 4 workgroups per CU).
  *   AUTO             MFMA with a tile chosen from the problem shape; where it picks
  *                    the 64 x 64 tile it runs it as 8 wavefronts (two k-slices of
- *                    4, kernel id 45) unless the grid is 257 to 512 tiles, where
- *                    the 4-wavefront kernel (id 42, as MFMA_64) is faster.
+ *                    4, kernel id 45) unless the grid is 257 to 512 tiles or K
+ *                    is below 256, where the 4-wavefront kernel (id 42, as
+ *                    MFMA_64) is faster.
  */
 typedef enum {
     SGEMM_ALGO_AUTO = 0,

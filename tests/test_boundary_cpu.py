@@ -151,12 +151,13 @@ def test_explicit_algorithms(algo, kid):
     ((8192, 8192, 8192), KID_L, (32, 32)),
     ((16384, 4096, 1024), KID_L, (64, 16)),
     ((2048, 2048, 2048), KID_M, (16, 16)),
-    # the 64 x 64 tile: 8 wavefronts (k split in two) unless the grid is 257..512 tiles
+    # the 64 x 64 tile: 8 wavefronts (k split in two) unless the grid is 257..512 tiles or K < 256
     ((1024, 1024, 1024), KID_S2, (16, 16)),
     ((1000, 1017, 999), KID_S2, (16, 16)),
     ((512, 512, 512), KID_S2, (8, 8)),
-    ((128, 128, 128), KID_S2, (2, 2)),
-    ((1, 1, 1), KID_S2, (1, 1)),
+    ((128, 128, 128), KID_S, (2, 2)),          # K < 256: the 4-wavefront kernel
+    ((1, 1, 1), KID_S, (1, 1)),
+    ((128, 128, 256), KID_S2, (2, 2)),
     ((1280, 1280, 1280), KID_S, (20, 20)),     # 400 tiles
     ((512, 4096, 4096), KID_S, (8, 64)),       # 512 tiles
     ((576, 4096, 1024), KID_S2, (9, 64)),      # 576 tiles

@@ -31,7 +31,7 @@ def built():
     ((512, 256, 16384), (16, KID_S, 16 * 512 * 256 * 4)),
     ((384, 384, 8192), (7, KID_S, 7 * 384 * 384 * 4)),       # 36 tiles: 14 splits would get 585 of k
     ((64, 64, 65536), (64, KID_S, 64 * 64 * 64 * 4)),
-    ((128, 128, 128), (1, KID_S2, 0)),            # k too short to split at 256 per split
+    ((128, 128, 128), (1, KID_S, 0)),             # k too short to split at 256 per split
 ])
 def test_auto_split_choice(shape, auto):
     st, used, kid, nbytes = lib.sgemm_f32_splitk_plan(0, *shape)
@@ -42,7 +42,7 @@ def test_explicit_split_geometry():
     # K = 100 in 8 splits: 32 per split (whole k-tiles) leaves 4 non-empty splits.
     assert lib.sgemm_f32_splitk_plan(8, 512, 512, 100)[:2] == (OK, 4)
     # K <= 32 cannot split.
-    assert lib.sgemm_f32_splitk_plan(4, 512, 512, 32)[1:] == (1, KID_S2, 0)   # the plain call's kernel
+    assert lib.sgemm_f32_splitk_plan(4, 512, 512, 32)[1:] == (1, KID_S, 0)    # the plain call's kernel
     # an explicit count splits any shape, always with the 64 x 64 partial tile
     assert lib.sgemm_f32_splitk_plan(4, 1024, 1024, 1024)[1:] == (4, KID_S, 4 * 1024 * 1024 * 4)
     assert lib.sgemm_f32_splitk_plan(16, 4096, 4096, 4096)[1:] == (16, KID_S, 16 * 4096 * 4096 * 4)
