@@ -395,6 +395,43 @@ def probe_clock(lib, torch, dev, stream, workgroups=512, trips=2000, launches=3)
                       "the timed steps (each workgroup's wavefront 0)"}
 
 
+def cu_scaling():
+    """The 256 x 256 MFMA kernel with one tile per busy CU: M = 256 .. 4096
+    (16 .. 256 tiles), N = K = 4096.  The same work per CU at every M, so a
+    time that does not grow with the busy CUs means the kernel is bound inside
+    each CU rather than by the memory system it shares."""
+    import torch
+
+    import fp32_gemm_08_amd as lib
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    print("| M | tiles = busy CUs | µs | TFLOP/s | per CU, % of 157.3/256 |")
+    print("|---|---|---|---|---|")
+    for M in (4096, 2048, 1024, 512, 256):
+        N = K = 4096
+        A = torch.rand(M, K, device=dev, generator=g) * 2 - 1
+        B = torch.rand(K, N, device=dev, generator=g) * 2 - 1
+        C = torch.empty(M, N, device=dev)
+
+        def call():
+            lib.gemm(A, B, C, algo="mfma_256")
+
+        settle(torch, call, 0.3)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(60):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / 60
+        per_cu = 2.0 * 256 * 256 * K / t / 1e12
+        print(f"| {M} | {(M // 256) * (N // 256)} | {t * 1e6:.1f} | {2.0 * M * N * K / t / 1e12:.1f} | "
+              f"{100 * per_cu / (FP32_MFMA_PEAK_TFLOPS / 256):.1f}% |", flush=True)
+        del A, B, C
+
+
 def bench_mfma_ceiling(args):
     """The FP32 matrix-core rate the device sustains with register operands
     only (no memory traffic), against the published 157.3 TFLOP/s."""
@@ -707,6 +744,8 @@ def main():
                     help="time every algorithm on every workload and print a table (no JSON line)")
     ap.add_argument("--oracle-table", action="store_true",
                     help="time the FP64 oracle on every GEMM workload (CPU only, reported, no JSON line)")
+    ap.add_argument("--cu-scaling", action="store_true",
+                    help="time the 256x256 MFMA kernel with 16..256 busy CUs, one tile each (table)")
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="time the library's register-only MFMA probe: the FP32 matrix-core rate the device "
                          "sustains and its shader clock (one JSON line)")
@@ -731,6 +770,9 @@ def main():
         return
     if args.mfma_ceiling:
         bench_mfma_ceiling(args)
+        return
+    if args.cu_scaling:
+        cu_scaling()
         return
     if args.op == "splitk":
         sweep_splitk()
