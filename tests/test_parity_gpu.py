@@ -240,6 +240,25 @@ def test_edge_tiles_aligned(oracle_lib, shape):
     assert_parity(Dg[rows, :N], D, S, K, f"edge {M}x{N}x{K} t{t}")
 
 
+# AUTO's 64 x 64 kernel switch: K below 256 keeps the 4-wavefront kernel (42),
+# from 256 the 8-wavefront one (45), whose two k-slices then split an odd
+# number of 32-wide k-tiles (K = 288: 9 tiles) or end in a k tail (K = 257).
+@pytest.mark.parametrize("shape", [(640, 640, 255, 0, 42), (640, 640, 256, 0, 45), (640, 640, 257, 1, 45),
+                                   (640, 644, 288, 0, 45), (1000, 1000, 1024, 1, 45)],
+                         ids=lambda s: "x".join(str(v) for v in s[:4]))
+def test_auto_64_kernel_switch(oracle_lib, shape):
+    M, N, K, t, want = shape
+    case = make_case(M, N, K, trans_b=t, alpha=1.25, beta=0.5, dist="normal", seed=K + 11)
+    st, kid, tm, tn, name = lib.sgemm_f32_plan(0, M, N, K, 1.0, 1 << 32, case.lda, 1 << 40, case.ldb, t, 0.5,
+                                              1 << 44, N)
+    assert kid == want, name
+    st, Dg = run_case(case, "auto", ldc_pad=4)
+    assert st == 0
+    rows = np.unique(np.concatenate([sample_rows(M, n=24, seed=K, tile=64), np.arange(M - 40, M)]))
+    D, S = oracle_rows(oracle_lib, case, rows)
+    assert_parity(Dg[rows, :N], D, S, K, f"auto {M}x{N}x{K} t{t} kernel {kid}")
+
+
 # Unaligned operands (leading dimension not a multiple of 4, or a base address
 # off by one float): the 64x64 and 128x128 tiles stage them with 4-byte direct
 # loads (edges clamped per element), the 256x256 tile through masked registers.
