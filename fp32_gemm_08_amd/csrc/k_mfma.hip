@@ -572,6 +572,46 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const f32x16 (&acc)[
         epilogue_rows<Gm, TRANS_B, FULL, false>(a, acc, m0, n0, ro);
 }
 
+// Old C of a wavefront that holds a single 32x32 block (the 64 x 64 tile): with
+// beta != 0 its 16 values per lane are read before the k-loop, so their
+// latency passes under the loop instead of following it at the end of the
+// tile, where nothing else would overlap it.  Larger tiles would hold 64 or 128
+// more registers for a tail that is a small share of their time, and keep the
+// batched loads of epilogue_rows.  The arithmetic is epilogue_rows'.
+template <class Gm>
+struct OldC {
+    static constexpr bool ON = Gm::FM * Gm::FN == 1;
+    float v[ON ? 16 : 1];
+
+    template <bool FULL>
+    __device__ __forceinline__ void load(const GemmArgs &a, int m0, int n0, const Role<Gm> &ro)
+    {
+        if constexpr (ON) {
+            const int col = n0 + ro.wn * Gm::WN + ro.l32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + ro.wm * Gm::WM + 8 * (r / 4) + 4 * ro.hi + (r % 4);
+                v[r] = (FULL || (row < a.M && col < a.N)) ? a.C[(int64_t)row * a.ldc + col] : 0.0f;
+            }
+        }
+    }
+
+    template <bool FULL>
+    __device__ __forceinline__ void epilogue(const GemmArgs &a, const f32x16 (&acc)[Gm::FM][Gm::FN], int m0, int n0,
+                                             const Role<Gm> &ro) const
+    {
+        if constexpr (ON) {
+            const int col = n0 + ro.wn * Gm::WN + ro.l32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + ro.wm * Gm::WM + 8 * (r / 4) + 4 * ro.hi + (r % 4);
+                if (FULL || (row < a.M && col < a.N))
+                    a.C[(int64_t)row * a.ldc + col] = fmaf(a.alpha, acc[0][0][r], a.beta * v[r]);
+            }
+        }
+    }
+};
+
 // One k-group of one stage: the first MFMA step runs on fragments read a whole
 // group earlier, before any new LDS traffic (so the wait in front of it never
 // covers fresh reads); then `next()` issues the next fragments (or the barrier
@@ -604,6 +644,10 @@ __device__ __forceinline__ void gemm_tile_regs(const GemmArgs &a, float *smem, i
     constexpr int G = Gm::G;
     const Role<Gm> ro;
     const int sl_off = ro.slice * Gm::SLICE;
+    OldC<Gm> oc;
+    const bool pre = OldC<Gm>::ON && a.beta != 0.0f && ro.slice == 0;
+    if (pre)
+        oc.template load<FULL>(a, m0, n0, ro);
 
     RegStage<Gm, TRANS_B, VEC> st;
     st.init(a, m0, n0);
@@ -648,8 +692,12 @@ __device__ __forceinline__ void gemm_tile_regs(const GemmArgs &a, float *smem, i
             });
         }
     }
-    if (reduce_slices<Gm>(acc, smem, ro))
-        epilogue<Gm, TRANS_B, FULL>(a, acc, m0, n0, ro);
+    if (reduce_slices<Gm>(acc, smem, ro)) {
+        if (pre)
+            oc.template epilogue<FULL>(a, acc, m0, n0, ro);
+        else
+            epilogue<Gm, TRANS_B, FULL>(a, acc, m0, n0, ro);
+    }
 }
 
 // Direct-staged k-loop for interior tiles with 16-byte aligned operands.
@@ -660,6 +708,10 @@ __device__ __forceinline__ void gemm_tile_direct(const GemmArgs &a, float *smem,
     const Role<Gm> ro;
     const int sl_off = ro.slice * Gm::SLICE;
     float *buf0 = smem, *buf1 = smem + Gm::STAGE;
+    OldC<Gm> oc;
+    const bool pre = OldC<Gm>::ON && a.beta != 0.0f && ro.slice == 0;
+    if (pre)
+        oc.template load<!EDGE>(a, m0, n0, ro);
 
     f32x16 acc[Gm::FM][Gm::FN];
     zero_acc<Gm>(acc);
@@ -713,8 +765,12 @@ __device__ __forceinline__ void gemm_tile_direct(const GemmArgs &a, float *smem,
             }
         }
     }
-    if (reduce_slices<Gm>(acc, smem, ro))
-        epilogue<Gm, TRANS_B, !EDGE>(a, acc, m0, n0, ro);
+    if (reduce_slices<Gm>(acc, smem, ro)) {
+        if (pre)
+            oc.template epilogue<!EDGE>(a, acc, m0, n0, ro);
+        else
+            epilogue<Gm, TRANS_B, !EDGE>(a, acc, m0, n0, ro);
+    }
 }
 
 // One output tile at (m0, n0): direct staging for interior tiles with aligned
