@@ -430,17 +430,3 @@ hipError_t launch_lp16(const GemmArgs &a, bool large, bool bf16, bool transB, vo
 }
 
 }  // namespace sgemm
-
-#ifdef SGEMM_LP16_EXPERIMENT
-// Experiment hook: the GEMM pass alone on operands already rounded.
-extern "C" int lp16_exp_gemm(int cfg, const sgemm::Lp16Args *g, int bf16, void *stream)
-{
-    using namespace sgemm;
-    hipStream_t s = (hipStream_t)stream;
-    switch (cfg) {
-    SGEMM_LP16_EXPERIMENT
-    default: return -1;
-    }
-    return (int)hipGetLastError();
-}
-#endif

@@ -1051,14 +1051,10 @@ hipError_t launch_mfma_sk(const GemmArgs &a, const SkArgs &sk, int kid, bool tra
 hipError_t launch_mfma(const GemmArgs &a, int kid, bool transB, bool vec, hipStream_t stream, int splits)
 {
     switch (kid) {
-#ifndef SGEMM_MFMA_EXPERIMENT
     case KID_MFMA_L: launch_cfg<256, 256, 32, 16, 4, 2, 2, 1>(a, transB, vec, stream, splits); break;
     case KID_MFMA_M: launch_cfg<128, 128, 32, 32, 2, 2, 2, 2>(a, transB, vec, stream, splits); break;
     case KID_MFMA_S: launch_cfg<64, 64, 32, 32, 2, 2, 4, 1>(a, transB, vec, stream, splits); break;
     case KID_MFMA_S2: launch_cfg<64, 64, 32, 32, 2, 2, 2, 2>(a, transB, vec, stream, splits); break;
-#else
-    SGEMM_MFMA_EXPERIMENT
-#endif
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
