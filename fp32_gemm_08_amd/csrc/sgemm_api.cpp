@@ -308,6 +308,17 @@ const char *kernel_label(int kid)
     }
 }
 
+// The code objects hold gfx950 code only.  `arch` is a device's
+// architecture name as HIP reports it: the processor, optionally followed by
+// target features after a ':' ("gfx950:sramecc+:xnack-").
+int arch_status(const char *arch)
+{
+    if (arch == nullptr)
+        return SGEMM_ERR_UNSUPPORTED_ARCH;
+    const size_t n = std::strcspn(arch, ":");
+    return (n == 6 && std::strncmp(arch, "gfx950", 6) == 0) ? SGEMM_OK : SGEMM_ERR_UNSUPPORTED_ARCH;
+}
+
 // 0 = unknown, 1 = gfx950, 2 = other architecture.
 std::atomic<int> g_arch[kMaxDevices];
 
@@ -323,7 +334,7 @@ int check_device()
         hipDeviceProp_t prop;
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
             return SGEMM_ERR_NO_DEVICE;
-        st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        st = arch_status(prop.gcnArchName) == SGEMM_OK ? 1 : 2;
         g_arch[dev].store(st, std::memory_order_release);
     }
     return st == 1 ? SGEMM_OK : SGEMM_ERR_UNSUPPORTED_ARCH;
@@ -367,6 +378,14 @@ int run(int algo, int64_t M, int64_t N, int64_t K, float alpha, const float *A, 
     default: e = launch_mfma(a, p.kid, p.transB, p.vec, s); break;
     }
     return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
+}
+
+// A workspace can hold `need` bytes and starts on a 16-byte boundary (the
+// stream-K fix-up and the two-pass GEMM read it with 128-bit accesses; the
+// k-split keeps the same rule).
+bool ws_fits(const void *ws, int64_t ws_bytes, int64_t need)
+{
+    return ws != nullptr && ws_bytes >= need && (reinterpret_cast<uintptr_t>(ws) & 15) == 0;
 }
 
 struct SplitPlan {
@@ -413,7 +432,7 @@ SplitPlan make_split_plan(int64_t splits_req, int64_t M, int64_t N, int64_t K, f
         sp.bytes = bytes;
         return sp;
     }
-    if (ws == nullptr || ws_bytes < bytes) {
+    if (!ws_fits(ws, ws_bytes, bytes)) {
         if (splits_req == 0)
             return sp;  // AUTO without room for the partials: the plain path
         return fail(SGEMM_ERR_INVALID_VALUE);
@@ -567,12 +586,12 @@ SkPlan make_sk_plan(int tile_req, int64_t M, int64_t N, int64_t K, float alpha, 
     return sp;
 }
 
-// Workspace checks shared by the stream-K and k-split calls.
+// Workspace checks shared by the stream-K, k-split and two-pass calls.
 int check_workspace(const void *ws, int64_t ws_bytes, int64_t need, int64_t M, int64_t N, int64_t K,
                     const float *A, int64_t lda, const float *B, int64_t ldb, int transB, const float *C,
                     int64_t ldc)
 {
-    if (ws == nullptr || ws_bytes < need)
+    if (!ws_fits(ws, ws_bytes, need))
         return SGEMM_ERR_INVALID_VALUE;
     const int64_t a_bytes = span_bytes(M, K, lda);
     const int64_t b_bytes = span_bytes(transB ? N : K, transB ? K : N, ldb);
@@ -808,7 +827,7 @@ int run_lowp_ws(bool forced, int tile_req, int precision, int64_t M, int64_t N, 
         return lp.base.status;
     if (lp.kid == KID_NONE)  // quick returns, product-free cases, or the one-pass call is faster
         return run_lowp(precision, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, stream);
-    if (ws == nullptr || ws_bytes < lp.bytes) {
+    if (!ws_fits(ws, ws_bytes, lp.bytes)) {
         if (forced)
             return SGEMM_ERR_INVALID_VALUE;
         return run_lowp(precision, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, stream);
@@ -1110,6 +1129,10 @@ const char *sgemm_f32_status_string(int status)
 }
 
 const char *sgemm_f32_version(void) { return "sgemm_f32 0.1.0 (gfx950)"; }
+
+int sgemm_f32_arch_status(const char *arch) { return sgemm::arch_status(arch); }
+
+int sgemm_f32_device_status(void) { return sgemm::check_device(); }
 
 int sgemm_f32_mfma_probe(int64_t workgroups, int64_t trips, float *sink, unsigned long long *clocks, void *stream)
 {

@@ -14,7 +14,10 @@ import ctypes
 import os
 import threading
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsgemm_f32.so")
+# SGEMM_F32_LIBRARY names another build of the same library (the LDS-poison
+# debug build, a host-sanitizer build); by default the in-tree one is loaded.
+LIB_PATH = os.environ.get("SGEMM_F32_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                               "libsgemm_f32.so")
 
 SGEMM_OK = 0
 SGEMM_ERR_INVALID_VALUE = 1
@@ -30,7 +33,7 @@ TRANSPOSE_ALGO = {"auto": 0, "naive": 1, "lds": 2, "lds_nopad": 3, "narrow": 4}
 # Symbols declared in include/sgemm_f32.h.
 PRECISION = {"fp16": 1, "bf16": 2}
 
-EXPORTS = ("sgemm_f32", "sgemm_f32_algo", "sgemm_f32_lowp", "sgemm_f32_lowp_2pass", "sgemm_f32_lowp_2pass_plan",
+EXPORTS = ("sgemm_f32", "sgemm_f32_algo", "sgemm_f32_arch_status", "sgemm_f32_device_status", "sgemm_f32_lowp", "sgemm_f32_lowp_2pass", "sgemm_f32_lowp_2pass_plan",
            "sgemm_f32_lowp_plan", "sgemm_f32_lowp_ws",
            "sgemm_f32_lowp_ws_plan", "sgemm_f32_plan",
            "sgemm_f32_splitk", "sgemm_f32_splitk_plan",
@@ -114,8 +117,26 @@ def load():
         lib.sgemm_f32_version.argtypes = []
         lib.sgemm_f32_mfma_probe.restype = ci
         lib.sgemm_f32_mfma_probe.argtypes = [i64, i64, vp, vp, vp]
+        lib.sgemm_f32_arch_status.restype = ci
+        lib.sgemm_f32_arch_status.argtypes = [ctypes.c_char_p]
+        lib.sgemm_f32_device_status.restype = ci
+        lib.sgemm_f32_device_status.argtypes = []
         _lib = lib
         return lib
+
+
+def sgemm_f32_arch_status(arch) -> int:
+    """Host-only: SGEMM_OK when the architecture name (bytes or str, or None)
+    is gfx950, else SGEMM_ERR_UNSUPPORTED_ARCH."""
+    if isinstance(arch, str):
+        arch = arch.encode()
+    return load().sgemm_f32_arch_status(arch)
+
+
+def sgemm_f32_device_status() -> int:
+    """The device check every call makes: SGEMM_OK, SGEMM_ERR_NO_DEVICE or
+    SGEMM_ERR_UNSUPPORTED_ARCH for the calling thread's current device."""
+    return load().sgemm_f32_device_status()
 
 
 def sgemm_f32(M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, stream=0) -> int:

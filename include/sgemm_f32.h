@@ -280,12 +280,12 @@ int sgemm_f32_lowp_plan(int precision, int64_t M, int64_t N, int64_t K, float al
  * same k order as the one-pass kernel's, so for a given tile size the two
  * calls give the same bits.
  *
- * Workspace: a DEVICE buffer owned by the caller, at least the bytes
- * sgemm_f32_lowp_ws_plan reports (2 * K' * (M' + N') plus alignment, M' and
- * N' rounded up to the tile, K' to 32), not overlapping A, B or C
+ * Workspace: a DEVICE buffer owned by the caller, 16-byte aligned, at least
+ * the bytes sgemm_f32_lowp_ws_plan reports (2 * K' * (M' + N') plus alignment,
+ * M' and N' rounded up to the tile, K' to 32), not overlapping A, B or C
  * (SGEMM_ERR_ALIAS), ordered on one stream with its other uses; its contents
- * on return are undefined.  With a smaller workspace (or NULL) the call runs
- * exactly as sgemm_f32_lowp.  Everything else (validation, quick returns,
+ * on return are undefined.  With a smaller or misaligned workspace (or NULL)
+ * the call runs exactly as sgemm_f32_lowp.  Everything else (validation, quick returns,
  * asynchrony) is sgemm_f32_lowp's.
  */
 int sgemm_f32_lowp_ws(int precision, int64_t M, int64_t N, int64_t K, float alpha,
@@ -306,8 +306,8 @@ int sgemm_f32_lowp_ws_plan(int precision, int64_t M, int64_t N, int64_t K, int t
 /* The two passes whatever the size (`tile`: 0 = the rule above, 256 or 128 =
  * that tile; anything else SGEMM_ERR_INVALID_VALUE), for callers that want
  * them and for testing them at every shape.  A workspace smaller than
- * sgemm_f32_lowp_2pass_plan reports, or K above 4,194,240, is
- * SGEMM_ERR_INVALID_VALUE. */
+ * sgemm_f32_lowp_2pass_plan reports or not 16-byte aligned, or K above
+ * 4,194,240, is SGEMM_ERR_INVALID_VALUE. */
 int sgemm_f32_lowp_2pass(int precision, int tile, int64_t M, int64_t N, int64_t K, float alpha,
                          const float *A, int64_t lda, const float *B, int64_t ldb, int transB,
                          float beta, float *C, int64_t ldc,
@@ -335,8 +335,8 @@ int sgemm_f32_lowp_2pass_plan(int precision, int tile, int64_t M, int64_t N, int
  * the unsplit kernel's.
  *
  * Workspace: a DEVICE buffer owned by the caller, at least splits*M*N*4 bytes
- * (sgemm_f32_splitk_plan reports the size), any alignment (16-byte aligned
- * with N % 4 == 0 lets the reduction use 128-bit accesses), not overlapping A,
+ * (sgemm_f32_splitk_plan reports the size), starting on a 16-byte boundary
+ * (every workspace of the library does; hipMalloc's are), not overlapping A,
  * B or C (SGEMM_ERR_ALIAS).  Its contents on entry are ignored and on return
  * undefined; it must stay allocated until the kernels enqueued on `stream`
  * have run.  Calls that share one workspace must be ordered on one stream.
@@ -362,8 +362,8 @@ int sgemm_f32_splitk_plan(int64_t splits, int64_t M, int64_t N, int64_t K, int t
 /*
  * sgemm_f32 with a workspace: runs the k-split or the stream-K schedule below
  * as sgemm_f32_ws_plan reports, when workspace_bytes is at least the size it
- * reports; otherwise (including workspace == NULL) it runs exactly as
- * sgemm_f32.
+ * reports and the workspace is 16-byte aligned; otherwise (including
+ * workspace == NULL) it runs exactly as sgemm_f32.
  */
 int sgemm_f32_ws(int64_t M, int64_t N, int64_t K, float alpha,
                  const float *A, int64_t lda, const float *B, int64_t ldb, int transB,
@@ -372,8 +372,8 @@ int sgemm_f32_ws(int64_t M, int64_t N, int64_t K, float alpha,
 
 /*
  * The same with an explicit split count (1..64; 1 runs the plain MFMA path).
- * A workspace smaller than sgemm_f32_splitk_plan(splits, ...) reports is
- * SGEMM_ERR_INVALID_VALUE.
+ * A workspace smaller than sgemm_f32_splitk_plan(splits, ...) reports, or not
+ * 16-byte aligned, is SGEMM_ERR_INVALID_VALUE.
  */
 int sgemm_f32_splitk(int64_t splits, int64_t M, int64_t N, int64_t K, float alpha,
                      const float *A, int64_t lda, const float *B, int64_t ldb, int transB,
@@ -400,8 +400,9 @@ int sgemm_f32_splitk(int64_t splits, int64_t M, int64_t N, int64_t K, float alph
  * Workspace: a DEVICE buffer owned by the caller, at least
  * 2 * workers * tile_rows * tile_cols * 4 bytes (sgemm_f32_streamk_plan
  * reports it; 0 when T is a multiple of 256 and the schedule is the plain
- * one), with the same rules as the k-split workspace (any contents, not
- * overlapping A, B or C, ordered on one stream).  Too small: SGEMM_ERR_INVALID_VALUE.
+ * one), with the same rules as the k-split workspace (16-byte aligned, any
+ * contents, not overlapping A, B or C, ordered on one stream).  Too small or
+ * misaligned: SGEMM_ERR_INVALID_VALUE.
  * Quick returns, product-free cases and argument errors are sgemm_f32's.
  */
 int sgemm_f32_streamk(int tile, int64_t M, int64_t N, int64_t K, float alpha,
@@ -425,7 +426,7 @@ int sgemm_f32_streamk_plan(int tile, int64_t M, int64_t N, int64_t K, int transB
  * 2 (stream-K) when the library's cost model expects stream-K to be at least
  * 1% faster than the plain call; otherwise 0 (plain).  Also the kernel id and
  * the workspace bytes that method needs (0 for the plain call).  With a
- * smaller workspace sgemm_f32_ws runs the plain call.
+ * smaller or misaligned workspace sgemm_f32_ws runs the plain call.
  */
 int sgemm_f32_ws_plan(int64_t M, int64_t N, int64_t K, int transB, int *method, int *kernel_id,
                       int64_t *workspace_bytes);
@@ -435,6 +436,25 @@ const char *sgemm_f32_status_string(int status);
 
 /* Static, NUL-terminated library version string. */
 const char *sgemm_f32_version(void);
+
+/*
+ * The device check every call makes before it enqueues work (the "no kernel
+ * image" case of "CUDA矩阵乘法性能优化实战：从朴素内核到寄存器分块与Nsight剖析",
+ * section 6.2: code built for one architecture does not run on another).
+ *
+ * sgemm_f32_arch_status: host-only, no HIP call.  `arch` is an architecture
+ * name as HIP reports it in hipDeviceProp_t::gcnArchName: a processor name,
+ * optionally followed by ':'-separated target features.  Returns SGEMM_OK when
+ * the processor is gfx950 (with any features), SGEMM_ERR_UNSUPPORTED_ARCH
+ * otherwise (NULL and the empty string included).
+ *
+ * sgemm_f32_device_status: the current HIP device of the calling thread:
+ * SGEMM_ERR_NO_DEVICE when there is none (no GPU, or none visible),
+ * SGEMM_ERR_UNSUPPORTED_ARCH when its architecture fails the check above,
+ * SGEMM_OK otherwise.  Enqueues nothing.
+ */
+int sgemm_f32_arch_status(const char *arch);
+int sgemm_f32_device_status(void);
 
 /*
  * Measurement aid, not part of the GEMM: the FP32 matrix-core rate the device

@@ -136,6 +136,13 @@ def test_2pass_small_workspace():
                                     need, 0) == INVALID
 
 
+@pytest.mark.parametrize("off", [4, 8, 12, 2])
+def test_2pass_misaligned_workspace(off):
+    # the GEMM pass stages the rounded operands with 16-byte loads
+    assert lib.sgemm_f32_lowp_2pass(2, 0, 300, 200, 50, 1.0, PA, 50, PB, 200, 0, 0.0, PC, 200, (1 << 46) + off,
+                                    1 << 30, 0) == INVALID
+
+
 def test_two_passes_stop_at_the_grid_limit_in_k():
     # the rounding transpose launches ceil(K / 64) workgroup rows, at most 65535
     kmax = 64 * 65535

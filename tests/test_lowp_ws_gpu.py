@@ -176,6 +176,20 @@ def test_ws_small_workspace_runs_one_pass():
     assert same_bits(D, D1)
 
 
+@pytest.mark.parametrize("off", [1, 2])
+def test_misaligned_workspace(off):
+    # the two passes need a 16-byte aligned workspace: sgemm_f32_lowp_ws runs
+    # the one-pass call instead, sgemm_f32_lowp_2pass rejects the call
+    case = make_case(2048, 2048, 2048, seed=50)
+    st, D, _ = run(case, "bf16", ws_offset=off)
+    assert st == 0
+    st1, D1, _ = run(case, "bf16", ws=False)
+    assert same_bits(D, D1)
+    small = make_case(700, 600, 500, seed=51)
+    st, D, _ = run(small, "bf16", tile=0, ws_offset=off, c_fill=7.0)
+    assert st == 1 and np.all(D == 7.0)
+
+
 def test_2pass_small_workspace_rejected():
     case = make_case(700, 600, 500, seed=49)
     need = lib.sgemm_f32_lowp_2pass_plan(2, 0, 700, 600, 500, 0)[4]

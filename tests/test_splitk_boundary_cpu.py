@@ -75,12 +75,19 @@ def test_invalid_calls(kw):
     assert call(**kw) == INVALID
 
 
-@pytest.mark.parametrize("kw", [dict(W=PA), dict(W=PC + 4), dict(W=PB - 2 * 512 * 512 * 4 + 4),
-                                dict(splits=None, W=PA + 8)])
+@pytest.mark.parametrize("kw", [dict(W=PA), dict(W=PC + 16), dict(W=PB - 2 * 512 * 512 * 4 + 16),
+                                dict(splits=None, W=PA + 16)])
 def test_workspace_alias(kw):
     # the 2-split partials need 2 * 512 * 512 * 4 bytes from W on
     kw.setdefault("splits", 2)
     assert call(**kw) == ALIAS
+
+
+@pytest.mark.parametrize("off", [4, 8, 12, 2])
+def test_workspace_misaligned(off):
+    # every workspace starts on a 16-byte boundary; an explicit split count
+    # with a misaligned one is an error (sgemm_f32_ws would run the plain call)
+    assert call(4, W=PW + off) == INVALID
 
 
 def test_quick_returns_touch_nothing():

@@ -126,11 +126,24 @@ def test_auto_with_and_without_workspace(oracle_lib):
     assert np.array_equal(D0.view(np.uint32), C.cpu().numpy().view(np.uint32))
 
 
-def test_misaligned_operands_and_workspace(oracle_lib):
+def test_misaligned_operands(oracle_lib):
     case = make_case(700, 333, 1500, trans_b=False, alpha=1.0, beta=0.0, seed=21, lda=1503)
-    st, D, used = run_split(case, 4, a_offset=1, ldc_pad=3, ws_offset=1)
+    st, D, used = run_split(case, 4, a_offset=1, ldc_pad=3, ws_offset=4)
     assert st == 0 and used == 4
     assert_parity(oracle_lib, case, D, "misaligned")
+
+
+def test_misaligned_workspace(oracle_lib):
+    # A workspace off a 16-byte boundary: the explicit split count is rejected
+    # before any launch (C and the workspace keep their canaries); the
+    # automatic call runs the plain kernel instead.
+    case = make_case(700, 333, 1500, trans_b=False, alpha=1.0, beta=0.0, seed=21)
+    st, D, _ = run_split(case, 4, ws_offset=1, c_fill=7.0)
+    assert st == 1 and np.all(D[:, :333] == 7.0)
+    assert lib.sgemm_f32_splitk_plan(0, 700, 333, 1500, 0)[1] > 1
+    st, D, _ = run_split(case, 0, ws_offset=3)
+    assert st == 0
+    assert_parity(oracle_lib, case, D, "misaligned workspace, plain call")
 
 
 def test_beta_zero_does_not_read_c(oracle_lib):

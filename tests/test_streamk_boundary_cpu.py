@@ -69,6 +69,13 @@ def test_workspace_too_small():
     assert call(tile=256, wb=0) == INVALID
 
 
+@pytest.mark.parametrize("off", [4, 8, 12, 1])
+def test_workspace_misaligned(off):
+    # the fix-up kernel reads the workspace with 128-bit loads
+    assert call(tile=256, W=PW + off, wb=256 * MB) == INVALID
+    assert call(tile=128, W=PW + off, wb=256 * MB) == INVALID
+
+
 @pytest.mark.parametrize("W", [PA + 64, PB + 64, PC + 64])
 def test_workspace_alias(W):
     assert call(tile=256, W=W, wb=256 * MB) == ALIAS

@@ -167,6 +167,18 @@ def test_streamk_full_waves_need_no_workspace(oracle_lib):
     assert_parity(oracle_lib, case, D, "streamk whole waves", rows=sample_rows(4096, n=8, seed=5, tile=128))
 
 
+def test_streamk_misaligned_workspace(oracle_lib):
+    # rejected before any launch; sgemm_f32_ws falls back to the plain call
+    case = make_case(1000, 1017, 999, trans_b=1, alpha=1.5, beta=-0.5, dist="uniform", seed=44)
+    st, D, _ = run_sk(case, 256, ws_offset=1)
+    assert st == 1 and np.array_equal(D[:, :1017], case.C[:, :1017])
+    big = make_case(4608, 4608, 1536, trans_b=0, alpha=1.0, beta=0.0, dist="uniform", seed=45)
+    assert lib.sgemm_f32_ws_plan(4608, 4608, 1536, 0)[1] == 2
+    st, D, _ = run_sk(big, 0, auto=True, ws_offset=2)
+    assert st == 0
+    assert_parity(oracle_lib, big, D, "ws auto, misaligned workspace", rows=sample_rows(4608, n=8, seed=4, tile=256))
+
+
 def test_streamk_small_workspace_rejected():
     import torch
 
