@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstring>
 #include <limits>
+#include <mutex>
 
 namespace sgemm {
 namespace {
@@ -492,6 +493,61 @@ int run_split(int64_t splits_req, int64_t M, int64_t N, int64_t K, float alpha, 
     return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
 }
 
+// ---- k-split on the library's static scratch --------------------------------
+
+// For callers that cannot allocate: the k-split partials go to this array
+// instead of a caller workspace.  Every GPU the library runs on holds its own
+// copy, at its own address, until the process ends.  In host code the name
+// stands for no device address: the kernels get the address that
+// hipGetSymbolAddress returns on the device, cached per device below.
+constexpr int64_t kScratchBytes = SGEMM_F32_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+std::mutex g_scratch_mu;
+float *g_scratch[kMaxDevices];  // per-device address of `scratch`, guarded by g_scratch_mu
+
+// Device address of `scratch` on the current device, looked up on the first
+// call on that device (which must be current and checked).
+int scratch_address(float **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return SGEMM_ERR_NO_DEVICE;
+    if (dev >= kMaxDevices)
+        return SGEMM_ERR_UNSUPPORTED_ARCH;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return SGEMM_ERR_LAUNCH;
+        g_scratch[dev] = static_cast<float *>(p);
+    }
+    *out = g_scratch[dev];
+    return SGEMM_OK;
+}
+
+int run_split_noalloc(int64_t splits_req, int64_t M, int64_t N, int64_t K, float alpha, const float *A,
+                      int64_t lda, const float *B, int64_t ldb, int transB, float beta, float *C, int64_t ldc,
+                      void *stream)
+{
+    const SplitPlan sp = make_split_plan(splits_req, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, nullptr,
+                                         0, false);
+    if (sp.base.status != SGEMM_OK)
+        return sp.base.status;
+    if (sp.splits <= 1)  // the plain call, which uses no scratch
+        return run(SGEMM_ALGO_AUTO, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, stream);
+    if (sp.bytes > kScratchBytes)
+        return SGEMM_ERR_SCRATCH_LIMIT;
+    const int dev_status = check_device();
+    if (dev_status != SGEMM_OK)
+        return dev_status;
+    float *ws = nullptr;
+    const int st = scratch_address(&ws);
+    if (st != SGEMM_OK)
+        return st;
+    return run_split(splits_req, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, ws, kScratchBytes, stream);
+}
+
 // ---- stream-K -------------------------------------------------------------
 
 constexpr int64_t kSkWorkers = 256;  // one stream-K workgroup per CU (both tiles hold a CU)
@@ -936,6 +992,13 @@ int sgemm_f32_splitk_plan(int64_t splits, int64_t M, int64_t N, int64_t K, int t
     return sp.base.status;
 }
 
+int sgemm_f32_splitk_noalloc(int64_t splits, int64_t M, int64_t N, int64_t K, float alpha, const float *A,
+                             int64_t lda, const float *B, int64_t ldb, int transB, float beta, float *C,
+                             int64_t ldc, void *stream)
+{
+    return sgemm::run_split_noalloc(splits, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, stream);
+}
+
 int sgemm_f32_ws(int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda, const float *B,
                  int64_t ldb, int transB, float beta, float *C, int64_t ldc, void *workspace,
                  int64_t workspace_bytes, void *stream)
@@ -1124,6 +1187,8 @@ const char *sgemm_f32_status_string(int status)
     case SGEMM_ERR_NO_DEVICE: return "SGEMM_ERR_NO_DEVICE: no HIP device is current";
     case SGEMM_ERR_UNSUPPORTED_ARCH: return "SGEMM_ERR_UNSUPPORTED_ARCH: device is not gfx950";
     case SGEMM_ERR_LAUNCH: return "SGEMM_ERR_LAUNCH: kernel launch failed";
+    case SGEMM_ERR_SCRATCH_LIMIT:
+        return "SGEMM_ERR_SCRATCH_LIMIT: the k-split partials need more than the library's 16 MiB static scratch";
     default: return "SGEMM: unknown status";
     }
 }

@@ -25,6 +25,8 @@ SGEMM_ERR_ALIAS = 2
 SGEMM_ERR_NO_DEVICE = 3
 SGEMM_ERR_UNSUPPORTED_ARCH = 4
 SGEMM_ERR_LAUNCH = 5
+SGEMM_ERR_SCRATCH_LIMIT = 6
+SCRATCH_BYTES = 16 << 20
 
 ALGO = {"auto": 0, "naive": 1, "lds_tiled": 2, "regblock": 3, "mfma": 4, "lds_tiled_nopad": 5, "naive_wg": 6,
         "mfma_256": 7, "mfma_128": 8, "mfma_64": 9}
@@ -36,7 +38,7 @@ PRECISION = {"fp16": 1, "bf16": 2}
 EXPORTS = ("sgemm_f32", "sgemm_f32_algo", "sgemm_f32_arch_status", "sgemm_f32_device_status", "sgemm_f32_lowp", "sgemm_f32_lowp_2pass", "sgemm_f32_lowp_2pass_plan",
            "sgemm_f32_lowp_plan", "sgemm_f32_lowp_ws",
            "sgemm_f32_lowp_ws_plan", "sgemm_f32_plan",
-           "sgemm_f32_splitk", "sgemm_f32_splitk_plan",
+           "sgemm_f32_splitk", "sgemm_f32_splitk_noalloc", "sgemm_f32_splitk_plan",
            "sgemm_f32_mfma_probe", "sgemm_f32_status_string", "sgemm_f32_streamk", "sgemm_f32_streamk_plan", "sgemm_f32_transpose",
            "sgemm_f32_transpose_algo", "sgemm_f32_transpose_plan", "sgemm_f32_version", "sgemm_f32_ws",
            "sgemm_f32_ws_plan")
@@ -82,6 +84,8 @@ def load():
         lib.sgemm_f32_ws.argtypes = ws_args
         lib.sgemm_f32_splitk.restype = ci
         lib.sgemm_f32_splitk.argtypes = [i64] + ws_args
+        lib.sgemm_f32_splitk_noalloc.restype = ci
+        lib.sgemm_f32_splitk_noalloc.argtypes = [i64] + gemm_args
         lib.sgemm_f32_splitk_plan.restype = ci
         lib.sgemm_f32_splitk_plan.argtypes = [i64, i64, i64, i64, ci, ctypes.POINTER(i64), ctypes.POINTER(ci),
                                               ctypes.POINTER(i64)]
@@ -188,6 +192,12 @@ def sgemm_f32_splitk(splits, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ld
     """The same with an explicit split count.  Returns the status."""
     return load().sgemm_f32_splitk(splits, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, workspace,
                                    workspace_bytes, stream)
+
+
+def sgemm_f32_splitk_noalloc(splits, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, stream=0) -> int:
+    """The k-split with its partials in the library's static device scratch
+    (no workspace argument, no allocation).  Returns the status."""
+    return load().sgemm_f32_splitk_noalloc(splits, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, stream)
 
 
 def sgemm_f32_splitk_plan(splits, M, N, K, transB=0):

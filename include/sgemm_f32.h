@@ -70,7 +70,8 @@ typedef enum {
     SGEMM_ERR_ALIAS = 2,
     SGEMM_ERR_NO_DEVICE = 3,
     SGEMM_ERR_UNSUPPORTED_ARCH = 4,
-    SGEMM_ERR_LAUNCH = 5
+    SGEMM_ERR_LAUNCH = 5,
+    SGEMM_ERR_SCRATCH_LIMIT = 6   /* only from sgemm_f32_splitk_noalloc */
 } sgemm_status;
 
 /*
@@ -379,6 +380,32 @@ int sgemm_f32_splitk(int64_t splits, int64_t M, int64_t N, int64_t K, float alph
                      const float *A, int64_t lda, const float *B, int64_t ldb, int transB,
                      float beta, float *C, int64_t ldc,
                      void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * The k-split for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): sgemm_f32_splitk
+ * with the partial products in the library's own static device scratch
+ * instead of a caller workspace.  The operation, the kernels, the result
+ * bits and the argument checks are sgemm_f32_splitk's with one addition:
+ * splits = 0 (which sgemm_f32_splitk rejects) takes the split count of the
+ * AUTO rule of sgemm_f32_ws, and runs the plain call where that rule does not
+ * split.  The call allocates and frees nothing and calls no allocating
+ * library routine.
+ *
+ * Scratch: SGEMM_F32_SCRATCH_BYTES (16 MiB) of device memory, one array per
+ * GPU the library runs on, held until the process ends; its address on a
+ * device is looked up on the first call there.  A split whose partials need
+ * more (sgemm_f32_splitk_plan reports the bytes; the AUTO rule never needs
+ * more than 8 MiB) returns SGEMM_ERR_SCRATCH_LIMIT before touching the
+ * device.  Every call on one GPU shares that GPU's array and leaves its
+ * contents behind (each call writes all of the partials it reads): calls that
+ * may overlap on one GPU -- on different streams, or from different threads
+ * without ordering -- race on it, and must be serialised by the caller.
+ */
+#define SGEMM_F32_SCRATCH_BYTES (16 << 20)
+int sgemm_f32_splitk_noalloc(int64_t splits, int64_t M, int64_t N, int64_t K, float alpha,
+                             const float *A, int64_t lda, const float *B, int64_t ldb, int transB,
+                             float beta, float *C, int64_t ldc, void *stream);
 
 /*
  * Stream-K.  With T output tiles and 256 CUs, a plain launch runs ceil(T/256)

@@ -47,7 +47,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert "gfx950" in lib.sgemm_f32_version()
-    for code in range(6):
+    for code in range(7):
         assert lib.sgemm_f32_status_string(code).startswith("SGEMM_")
     assert "unknown" in lib.sgemm_f32_status_string(99)
 

@@ -90,6 +90,41 @@ def test_workspace_misaligned(off):
     assert call(4, W=PW + off) == INVALID
 
 
+SCRATCH_LIMIT = 6
+
+
+def noalloc(splits, M=512, N=512, K=512, alpha=1.0, A=PA, B=PB, transB=0, beta=0.0, C=PC):
+    ldb = K if transB else N
+    return lib.sgemm_f32_splitk_noalloc(splits, M, N, K, alpha, A, K, B, ldb, transB, beta, C, N, 0)
+
+
+def test_noalloc_rejects_partials_beyond_the_scratch():
+    # 64 splits of 1024 x 1024 need 256 MiB; 5 of 1024 x 1024 need 20 MiB
+    assert noalloc(64, M=1024, N=1024, K=4096) == SCRATCH_LIMIT
+    assert noalloc(5, M=1024, N=1024, K=4096) == SCRATCH_LIMIT
+    assert lib.sgemm_f32_splitk_plan(4, 1024, 1024, 4096)[3] == lib.SCRATCH_BYTES   # 4 splits fit exactly
+    assert "16 MiB" in lib.sgemm_f32_status_string(SCRATCH_LIMIT)
+
+
+@pytest.mark.parametrize("kw", [dict(splits=-1), dict(splits=65), dict(splits=2, M=-1), dict(splits=2, A=0),
+                                dict(splits=2, transB=2)])
+def test_noalloc_invalid(kw):
+    assert noalloc(**kw) == INVALID
+
+
+def test_noalloc_alias_and_quick_returns():
+    assert noalloc(2, C=PA + 64) == ALIAS
+    assert noalloc(2, M=0) == OK and noalloc(0, alpha=0.0, beta=1.0) == OK
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 512, 512), (256, 256, 32768), (64, 64, 65536), (100, 700, 9000),
+                                   (2000, 60, 50000), (800, 800, 800), (1, 1, 1 << 20)])
+def test_auto_split_fits_the_scratch(M, N, K):
+    # the AUTO rule keeps splits x 64x64 tiles <= 512, i.e. at most 8 MiB of partials
+    st, used, _, need = lib.sgemm_f32_splitk_plan(0, M, N, K)
+    assert st == OK and need <= lib.SCRATCH_BYTES // 2
+
+
 def test_quick_returns_touch_nothing():
     # No launch happens for these, so fake addresses are safe.
     assert call(2, M=0) == OK and call(None, N=0, ldb=1, ldc=1) == OK
