@@ -49,6 +49,10 @@ namespace sgemm {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// Four floats in global memory at any 4-byte aligned address: 128-bit loads
+// through this type need no 16-byte alignment (the device runs with unaligned
+// access enabled for global memory).
+typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -116,22 +120,14 @@ __device__ __forceinline__ void map_tile(int bid, int nbm, int nbn, int &tm, int
     group_order(xcd_remap(bid, nbm * nbn), nbm, nbn, tm, tn);
 }
 
-// Four consecutive floats from p.  MASKED: elements at or beyond `limit` (or all
-// of them when !ok) read as zero.  VEC: one 128-bit load when all four are in.
-template <bool VEC, bool MASKED>
+// Four consecutive floats from p, one 128-bit load when all four are in.
+// MASKED: elements at or beyond `limit` (or all of them when !ok) read as zero.
+template <bool MASKED>
 __device__ __forceinline__ f32x4 load4(const float *p, bool ok, int first, int limit)
 {
     f32x4 v;
-    if (!MASKED) {
-        if (VEC) {
-            v = *reinterpret_cast<const f32x4 *>(p);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                v[e] = p[e];
-        }
-    } else if (VEC && ok && first + 4 <= limit) {
-        v = *reinterpret_cast<const f32x4 *>(p);
+    if (!MASKED || (ok && first + 4 <= limit)) {
+        v = *reinterpret_cast<const f32x4u *>(p);
     } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -289,7 +285,7 @@ __device__ __forceinline__ void mfma_group(f32x16 (&acc)[Gm::FM][Gm::FN], const 
 
 // Register staging of one LDS stage (KS k-tiles): masked (or, for interior
 // tiles and full stages, plain) loads into registers, then stores in LDS layout.
-template <class Gm, bool TRANS_B, bool VEC>
+template <class Gm, bool TRANS_B>
 struct RegStage {
     static constexpr int CA = Gm::CA, CB = Gm::CB, CPR = Gm::CPR, BN4 = Gm::BN / 4;
     const float *pa[CA];
@@ -339,13 +335,13 @@ struct RegStage {
         const int k0 = kt * Gm::KT;
 #pragma unroll
         for (int i = 0; i < CA; ++i)
-            ra[i] = load4<VEC, MASKED>(pa[i] + (int64_t)k0, m0 + ra_row[i] < a.M, k0 + ra_k[i], a.K);
+            ra[i] = load4<MASKED>(pa[i] + (int64_t)k0, m0 + ra_row[i] < a.M, k0 + ra_k[i], a.K);
 #pragma unroll
         for (int i = 0; i < CB; ++i) {
             if constexpr (TRANS_B)
-                rb[i] = load4<VEC, MASKED>(pb[i] + (int64_t)k0, n0 + rb_row[i] < a.N, k0 + rb_k[i], a.K);
+                rb[i] = load4<MASKED>(pb[i] + (int64_t)k0, n0 + rb_row[i] < a.N, k0 + rb_k[i], a.K);
             else
-                rb[i] = load4<VEC, MASKED>(pb[i] + (int64_t)k0 * a.ldb, k0 + rb_row[i] < a.K, n0 + rb_k[i], a.N);
+                rb[i] = load4<MASKED>(pb[i] + (int64_t)k0 * a.ldb, k0 + rb_row[i] < a.K, n0 + rb_k[i], a.N);
         }
     }
 
@@ -361,25 +357,27 @@ struct RegStage {
 };
 
 // Direct staging of full stages with global->LDS loads.  A wavefront
-// instruction fills one LDS block of BW floats, lane L writing float(s)
-// e = BW*block + W*L .. +W-1 of the stage's slice tile: W = 4 floats
-// (global_load_lds_dwordx4, 1 KB blocks) when the operands are 16-byte aligned,
-// W = 1 (global_load_lds_dword, 256-byte blocks) otherwise.  Each lane's
-// source follows from where its LDS float lies: in a k-contiguous tile (A, and
-// op(B) = B^T) float e is row e / BK, physical k-position e % BK, whose 4-float
-// chunk holds logical chunk (e % BK / 4) ^ swz(row); in the n-contiguous op(B) = B
-// tile it is row e / BN, column e % BN.  Sources are 32-bit float offsets from
-// the tile's first element, valid because the host allows this path only when
-// a tile's extent fits (rows x leading dimension < 2^31).
+// instruction (global_load_lds_dwordx4) fills one 1 KB LDS block, lane L
+// writing floats e = 256*block + 4L .. 4L+3 of the stage's slice tile.  Each
+// lane's source follows from where its LDS floats lie: in a k-contiguous tile
+// (A, and op(B) = B^T) float e is row e / BK, physical k-position e % BK, whose
+// 4-float chunk holds logical chunk (e % BK / 4) ^ swz(row); in the
+// n-contiguous op(B) = B tile it is row e / BN, column e % BN.  A source needs
+// 4-byte alignment only: with a leading dimension that is not a multiple of 4
+// the 16 bytes of a chunk start anywhere on a float boundary, and the loads
+// stay 16 bytes wide (4-byte loads would take four times the instructions).
+// Sources are 32-bit float offsets from the tile's first element, valid
+// because the host allows this path only when a tile's extent fits (rows x
+// leading dimension < 2^31).
 //
 // EDGE: the tile reaches past M or N.  Rows of A (and of B^T) past the matrix
 // load its last row instead, and for op(B) = B columns past N load its last
-// column (its last whole 4-column chunk with W = 4, which the caller allows
-// only when N % 4 == 0): those values only reach outputs that the masked
-// epilogue does not store, and every address stays inside the operands.
-template <class Gm, bool TRANS_B, bool DW>
+// whole 4-column chunk (the caller allows this only when N % 4 == 0): those
+// values only reach outputs that the masked epilogue does not store, and every
+// address stays inside the operands.
+template <class Gm, bool TRANS_B>
 struct DirectStage {
-    static constexpr int W = DW ? 1 : 4, BW = 64 * W;
+    static constexpr int W = 4, BW = 64 * W;
     static constexpr int A_N = Gm::KS * Gm::A_SZ / BW / Gm::NW;   // instructions per wavefront
     static constexpr int B_N = Gm::KS * Gm::B_SZ / BW / Gm::NW;
     static constexpr int A_BPS = Gm::A_SZ / BW, B_BPS = Gm::B_SZ / BW;  // blocks per slice tile
@@ -638,7 +636,7 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[Gm::FM][Gm::FN])
 
 // Register-staged k-loop.  FULL: the tile lies inside M x N (only the K tail
 // needs masks).
-template <class Gm, bool TRANS_B, bool VEC, bool FULL>
+template <class Gm, bool TRANS_B, bool FULL>
 __device__ __forceinline__ void gemm_tile_regs(const GemmArgs &a, float *smem, int m0, int n0)
 {
     constexpr int G = Gm::G;
@@ -649,7 +647,7 @@ __device__ __forceinline__ void gemm_tile_regs(const GemmArgs &a, float *smem, i
     if (pre)
         oc.template load<FULL>(a, m0, n0, ro);
 
-    RegStage<Gm, TRANS_B, VEC> st;
+    RegStage<Gm, TRANS_B> st;
     st.init(a, m0, n0);
     auto gload = [&](int kt) {
         if (FULL && (kt + 1) * Gm::KT <= a.K)
@@ -700,8 +698,9 @@ __device__ __forceinline__ void gemm_tile_regs(const GemmArgs &a, float *smem, i
     }
 }
 
-// Direct-staged k-loop for interior tiles with 16-byte aligned operands.
-template <class Gm, bool TRANS_B, bool EDGE, bool DW>
+// Direct-staged k-loop (interior tiles, and edge tiles whose clamped
+// addresses are exact).
+template <class Gm, bool TRANS_B, bool EDGE>
 __device__ __forceinline__ void gemm_tile_direct(const GemmArgs &a, float *smem, int m0, int n0)
 {
     constexpr int G = Gm::G;
@@ -719,7 +718,7 @@ __device__ __forceinline__ void gemm_tile_direct(const GemmArgs &a, float *smem,
     const int nf = a.K / Gm::KT;  // full stages
     Frags<Gm, TRANS_B> f[2];
 
-    DirectStage<Gm, TRANS_B, DW> ds;
+    DirectStage<Gm, TRANS_B> ds;
     ds.template init<EDGE>(a, m0, n0);
     if (nf > 0)
         ds.issue(0, buf0);
@@ -727,7 +726,7 @@ __device__ __forceinline__ void gemm_tile_direct(const GemmArgs &a, float *smem,
     // Partial last stage first (the order of the k sum is free): registers with
     // zero fill, through buffer 1, while stage 0 lands in buffer 0.
     if (nf * Gm::KT < a.K) {
-        RegStage<Gm, TRANS_B, !DW> st;
+        RegStage<Gm, TRANS_B> st;
         st.init(a, m0, n0);
         st.template load<true>(a, m0, n0, nf);
         st.store(buf1);
@@ -773,36 +772,30 @@ __device__ __forceinline__ void gemm_tile_direct(const GemmArgs &a, float *smem,
     }
 }
 
-// One output tile at (m0, n0): direct staging for interior tiles with aligned
-// operands (and edge tiles whose clamped addresses are exact), registers
-// otherwise.  GD: geometry of the direct path; GR: geometry of the register
-// path (same workgroup tile, wavefront layout and k-split, possibly a shorter
-// k-tile so the register staging fits next to the accumulators).
-template <class GD, class GR, bool TRANS_B, bool VEC>
+// One output tile at (m0, n0): direct staging for interior tiles (and edge
+// tiles whose clamped addresses are exact: op(B) = B^T, or op(B) = B with N a
+// multiple of 4, so that a 4-column chunk is wholly inside or outside),
+// registers otherwise.  GD: geometry of the direct path; GR: geometry of the
+// register path (same workgroup tile, wavefront layout and k-split, possibly a
+// shorter k-tile so the register staging fits next to the accumulators).
+template <class GD, class GR, bool TRANS_B>
 __device__ __forceinline__ void mfma_tile(const GemmArgs &a, float *smem, int m0, int n0)
 {
     const bool full = m0 + GD::BM <= a.M && n0 + GD::BN <= a.N;
-    // 16-byte direct loads for aligned operands, 4-byte ones otherwise (not on
-    // the 256 x 256 tile: its 32 per-lane source offsets would not fit beside
-    // the accumulators).  Edge tiles stage directly too whenever every clamped
-    // address is exact (with 16-byte loads op(B) = B needs whole 4-column chunks).
-    constexpr bool direct_ok = VEC || GD::BM * GD::BN <= 128 * 128;
-    if constexpr (direct_ok) {
-        if (a.flags & GEMM_FLAG_DIRECT) {
-            if (full) {
-                gemm_tile_direct<GD, TRANS_B, false, !VEC>(a, smem, m0, n0);
-                return;
-            }
-            if (!VEC || TRANS_B || (a.N & 3) == 0) {
-                gemm_tile_direct<GD, TRANS_B, true, !VEC>(a, smem, m0, n0);
-                return;
-            }
+    if (a.flags & GEMM_FLAG_DIRECT) {
+        if (full) {
+            gemm_tile_direct<GD, TRANS_B, false>(a, smem, m0, n0);
+            return;
+        }
+        if (TRANS_B || (a.N & 3) == 0) {
+            gemm_tile_direct<GD, TRANS_B, true>(a, smem, m0, n0);
+            return;
         }
     }
     if (full)
-        gemm_tile_regs<GR, TRANS_B, VEC, true>(a, smem, m0, n0);
+        gemm_tile_regs<GR, TRANS_B, true>(a, smem, m0, n0);
     else
-        gemm_tile_regs<GR, TRANS_B, VEC, false>(a, smem, m0, n0);
+        gemm_tile_regs<GR, TRANS_B, false>(a, smem, m0, n0);
 }
 
 template <class GD, class GR>
@@ -813,7 +806,7 @@ struct SharedGeo {
     static constexpr int SMEM = GD::SMEM > GR::SMEM ? GD::SMEM : GR::SMEM;
 };
 
-template <class GD, class GR, bool TRANS_B, bool VEC>
+template <class GD, class GR, bool TRANS_B>
 __global__ __launch_bounds__(GD::NT) __attribute__((amdgpu_waves_per_eu(GD::OCC)))
 void sgemm_mfma_kernel(GemmArgs a)
 {
@@ -829,7 +822,7 @@ void sgemm_mfma_kernel(GemmArgs a)
     const int nbm = (a.M + GD::BM - 1) / GD::BM, nbn = (a.N + GD::BN - 1) / GD::BN;
     int tile_m, tile_n;
     map_tile(blockIdx.x, nbm, nbn, tile_m, tile_n);
-    mfma_tile<GD, GR, TRANS_B, VEC>(a, smem, tile_m * GD::BM, tile_n * GD::BN);
+    mfma_tile<GD, GR, TRANS_B>(a, smem, tile_m * GD::BM, tile_n * GD::BN);
 }
 
 // A uniform value the compiler cannot see through (an empty asm that claims to
@@ -852,7 +845,7 @@ __device__ __forceinline__ int64_t opaque(int64_t v)
 // a whole tile is finished in place; any other piece writes its raw partial
 // product to the worker's slot and the fix-up kernel completes the tile.  No
 // workgroup ever waits for another.
-template <class GD, class GR, bool TRANS_B, bool VEC>
+template <class GD, class GR, bool TRANS_B>
 __global__ __launch_bounds__(GD::NT) __attribute__((amdgpu_waves_per_eu(GD::OCC)))
 void sgemm_mfma_sk_kernel(GemmArgs a, SkArgs sk)
 {
@@ -904,7 +897,7 @@ void sgemm_mfma_sk_kernel(GemmArgs a, SkArgs sk)
         }
         if (it != first)
             __syncthreads();  // the previous piece's last LDS reads are done
-        mfma_tile<GD, GR, TRANS_B, VEC>(b, smem, 0, 0);
+        mfma_tile<GD, GR, TRANS_B>(b, smem, 0, 0);
         it += ke - kb;
     }
 }
@@ -979,7 +972,7 @@ TileShape tile_shape(int kid)
 }
 
 template <int BM, int BN, int BKD, int BKR, int WGM, int WGN, int OCC, int KS>
-static void launch_cfg(const GemmArgs &a, bool transB, bool vec, hipStream_t stream, int splits)
+static void launch_cfg(const GemmArgs &a, bool transB, hipStream_t stream, int splits)
 {
     const int64_t blocks = ceil_div(a.M, BM) * ceil_div(a.N, BN);
     const dim3 grid((unsigned)blocks, (unsigned)splits), block(64 * WGM * WGN * KS);
@@ -987,38 +980,24 @@ static void launch_cfg(const GemmArgs &a, bool transB, bool vec, hipStream_t str
     typedef Geo<BM, BN, BKR, WGM, WGN, OCC, true, KS> GRT;
     typedef Geo<BM, BN, BKD, WGM, WGN, OCC, false, KS> GDN;
     typedef Geo<BM, BN, BKR, WGM, WGN, OCC, false, KS> GRN;
-    if (transB) {
-        if (vec)
-            sgemm_mfma_kernel<GDT, GRT, true, true><<<grid, block, 0, stream>>>(a);
-        else
-            sgemm_mfma_kernel<GDT, GRT, true, false><<<grid, block, 0, stream>>>(a);
-    } else {
-        if (vec)
-            sgemm_mfma_kernel<GDN, GRN, false, true><<<grid, block, 0, stream>>>(a);
-        else
-            sgemm_mfma_kernel<GDN, GRN, false, false><<<grid, block, 0, stream>>>(a);
-    }
+    if (transB)
+        sgemm_mfma_kernel<GDT, GRT, true><<<grid, block, 0, stream>>>(a);
+    else
+        sgemm_mfma_kernel<GDN, GRN, false><<<grid, block, 0, stream>>>(a);
 }
 
 template <int BM, int BN, int BKD, int BKR, int WGM, int WGN, int OCC, int KS>
-static void launch_sk_cfg(const GemmArgs &a, const SkArgs &sk, bool transB, bool vec, hipStream_t stream)
+static void launch_sk_cfg(const GemmArgs &a, const SkArgs &sk, bool transB, hipStream_t stream)
 {
     const dim3 grid((unsigned)(sk.dp + sk.workers)), block(64 * WGM * WGN * KS);
     typedef Geo<BM, BN, BKD, WGM, WGN, OCC, true, KS, true> GDT;
     typedef Geo<BM, BN, BKR, WGM, WGN, OCC, true, KS, true> GRT;
     typedef Geo<BM, BN, BKD, WGM, WGN, OCC, false, KS, true> GDN;
     typedef Geo<BM, BN, BKR, WGM, WGN, OCC, false, KS, true> GRN;
-    if (transB) {
-        if (vec)
-            sgemm_mfma_sk_kernel<GDT, GRT, true, true><<<grid, block, 0, stream>>>(a, sk);
-        else
-            sgemm_mfma_sk_kernel<GDT, GRT, true, false><<<grid, block, 0, stream>>>(a, sk);
-    } else {
-        if (vec)
-            sgemm_mfma_sk_kernel<GDN, GRN, false, true><<<grid, block, 0, stream>>>(a, sk);
-        else
-            sgemm_mfma_sk_kernel<GDN, GRN, false, false><<<grid, block, 0, stream>>>(a, sk);
-    }
+    if (transB)
+        sgemm_mfma_sk_kernel<GDT, GRT, true><<<grid, block, 0, stream>>>(a, sk);
+    else
+        sgemm_mfma_sk_kernel<GDN, GRN, false><<<grid, block, 0, stream>>>(a, sk);
     if (sk.sk_tiles > 0) {
         const dim3 fgrid((unsigned)sk.sk_tiles, BM / 16);
         const bool cvec = (reinterpret_cast<uintptr_t>(a.C) & 15) == 0 && (a.ldc & 3) == 0;
@@ -1038,23 +1017,23 @@ int mfma_stage_k(int kid)
     }
 }
 
-hipError_t launch_mfma_sk(const GemmArgs &a, const SkArgs &sk, int kid, bool transB, bool vec, hipStream_t stream)
+hipError_t launch_mfma_sk(const GemmArgs &a, const SkArgs &sk, int kid, bool transB, hipStream_t stream)
 {
     switch (kid) {
-    case KID_MFMA_L: launch_sk_cfg<256, 256, 32, 16, 4, 2, 2, 1>(a, sk, transB, vec, stream); break;
-    case KID_MFMA_M: launch_sk_cfg<128, 128, 32, 32, 2, 2, 2, 2>(a, sk, transB, vec, stream); break;
+    case KID_MFMA_L: launch_sk_cfg<256, 256, 32, 16, 4, 2, 2, 1>(a, sk, transB, stream); break;
+    case KID_MFMA_M: launch_sk_cfg<128, 128, 32, 32, 2, 2, 2, 2>(a, sk, transB, stream); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_mfma(const GemmArgs &a, int kid, bool transB, bool vec, hipStream_t stream, int splits)
+hipError_t launch_mfma(const GemmArgs &a, int kid, bool transB, hipStream_t stream, int splits)
 {
     switch (kid) {
-    case KID_MFMA_L: launch_cfg<256, 256, 32, 16, 4, 2, 2, 1>(a, transB, vec, stream, splits); break;
-    case KID_MFMA_M: launch_cfg<128, 128, 32, 32, 2, 2, 2, 2>(a, transB, vec, stream, splits); break;
-    case KID_MFMA_S: launch_cfg<64, 64, 32, 32, 2, 2, 4, 1>(a, transB, vec, stream, splits); break;
-    case KID_MFMA_S2: launch_cfg<64, 64, 32, 32, 2, 2, 2, 2>(a, transB, vec, stream, splits); break;
+    case KID_MFMA_L: launch_cfg<256, 256, 32, 16, 4, 2, 2, 1>(a, transB, stream, splits); break;
+    case KID_MFMA_M: launch_cfg<128, 128, 32, 32, 2, 2, 2, 2>(a, transB, stream, splits); break;
+    case KID_MFMA_S: launch_cfg<64, 64, 32, 32, 2, 2, 4, 1>(a, transB, stream, splits); break;
+    case KID_MFMA_S2: launch_cfg<64, 64, 32, 32, 2, 2, 2, 2>(a, transB, stream, splits); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -53,6 +53,10 @@ bool overlaps(const void *p, int64_t pb, const void *q, int64_t qb)
 
 bool aligned16(const void *p, int64_t ld) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0 && (ld & 3) == 0; }
 
+// A float pointer must hold a float boundary: the MFMA kernels read 16 bytes
+// at a time from any such address.
+bool float_aligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
+
 // MFMA tile from a wave-quantisation model.  Every tile has the 256 CUs as
 // workgroup slots (the 256 x 256 and 128 x 128 tiles hold a CU each; 64 x 64
 // workgroups share one up to 4 at a time and are dealt round-robin), so the
@@ -181,7 +185,7 @@ Plan make_plan(int algo, int64_t M, int64_t N, int64_t K, float alpha, const flo
         return fail(SGEMM_ERR_INVALID_VALUE);
     if (M == 0 || N == 0)
         return p;  // nothing to do
-    if (C == nullptr)
+    if (C == nullptr || !float_aligned(C))
         return fail(SGEMM_ERR_INVALID_VALUE);
     const bool product = alpha != 0.0f && K > 0;
     if (!product) {
@@ -194,7 +198,7 @@ Plan make_plan(int algo, int64_t M, int64_t N, int64_t K, float alpha, const flo
             return fail(SGEMM_ERR_INVALID_VALUE);
         return p;
     }
-    if (A == nullptr || B == nullptr)
+    if (A == nullptr || B == nullptr || !float_aligned(A) || !float_aligned(B))
         return fail(SGEMM_ERR_INVALID_VALUE);
     if (overlaps(C, c_bytes, A, a_bytes) || overlaps(C, c_bytes, B, b_bytes))
         return fail(SGEMM_ERR_ALIAS);
@@ -376,7 +380,7 @@ int run(int algo, int64_t M, int64_t N, int64_t K, float alpha, const float *A, 
     case KID_TILED_PAD: e = launch_tiled(a, p.transB, true, s); break;
     case KID_TILED_NOPAD: e = launch_tiled(a, p.transB, false, s); break;
     case KID_REGBLOCK: e = launch_regblock(a, p.transB, p.vec, s); break;
-    default: e = launch_mfma(a, p.kid, p.transB, p.vec, s); break;
+    default: e = launch_mfma(a, p.kid, p.transB, s); break;
     }
     return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
 }
@@ -485,7 +489,7 @@ int run_split(int64_t splits_req, int64_t M, int64_t N, int64_t K, float alpha, 
     a.c_split_stride = M * N;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    hipError_t e = launch_mfma(a, sp.kid, sp.base.transB, sp.base.vec, s, (int)sp.splits);
+    hipError_t e = launch_mfma(a, sp.kid, sp.base.transB, s, (int)sp.splits);
     if (e != hipSuccess)
         return SGEMM_ERR_LAUNCH;
     const bool rvec = (N % 4) == 0 && aligned16(W, N) && aligned16(C, ldc);
@@ -683,7 +687,7 @@ int launch_sk_plan(const SkPlan &sp, int64_t M, int64_t N, int64_t K, float alph
     sk.ws = static_cast<float *>(ws);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    const hipError_t e = launch_mfma_sk(a, sk, sp.tile_kid, sp.base.transB, sp.base.vec, s);
+    const hipError_t e = launch_mfma_sk(a, sk, sp.tile_kid, sp.base.transB, s);
     return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
 }
 

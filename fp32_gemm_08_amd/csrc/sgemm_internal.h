@@ -83,11 +83,13 @@ hipError_t launch_naive(const GemmArgs &a, bool transB, hipStream_t stream);
 hipError_t launch_naive_wg(const GemmArgs &a, bool transB, hipStream_t stream);
 hipError_t launch_tiled(const GemmArgs &a, bool transB, bool pad, hipStream_t stream);
 hipError_t launch_regblock(const GemmArgs &a, bool transB, bool vec, hipStream_t stream);
-hipError_t launch_mfma(const GemmArgs &a, int kid, bool transB, bool vec, hipStream_t stream, int splits = 1);
+// The MFMA kernels load operands 16 bytes at a time from any 4-byte aligned
+// address (the host requires float-aligned A and B).
+hipError_t launch_mfma(const GemmArgs &a, int kid, bool transB, hipStream_t stream, int splits = 1);
 // Stream-K launch of the 256 x 256 (KID_MFMA_L) or 128 x 128 (KID_MFMA_M)
 // tile, then the fix-up of its split tiles (nothing when sk.sk_tiles == 0).
 // `iters` must be ceil(K / mfma_stage_k(kid)).
-hipError_t launch_mfma_sk(const GemmArgs &a, const SkArgs &sk, int kid, bool transB, bool vec, hipStream_t stream);
+hipError_t launch_mfma_sk(const GemmArgs &a, const SkArgs &sk, int kid, bool transB, hipStream_t stream);
 int mfma_stage_k(int kid);
 // Mixed precision: operands rounded to fp16 (bf16 = false) or bf16 while staged.
 hipError_t launch_mfma_lp(const GemmArgs &a, bool large, bool bf16, bool transB, bool vec, hipStream_t stream);

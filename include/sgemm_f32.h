@@ -40,9 +40,10 @@
  * without a GPU:
  *   SGEMM_ERR_INVALID_VALUE   negative or too large (> 2^31 - 1025) dimension, a
  *                             leading dimension below its minimum, transB not 0/1, a
- *                             NULL pointer for an operand that would be read or
- *                             written, an unknown algorithm id, or a launch that
- *                             would need 2^32 or more work-items;
+ *                             NULL pointer, or one not on a 4-byte (float) boundary,
+ *                             for an operand that would be read or written, an
+ *                             unknown algorithm id, or a launch that would need
+ *                             2^32 or more work-items;
  *   SGEMM_ERR_ALIAS           C's byte range overlaps A's or B's (the kernels rely on
  *                             the no-alias premise of __restrict__, section 5.3 of the
  *                             first page); A and B may overlap each other;

@@ -75,6 +75,8 @@ def call(algo=0, M=64, N=64, K=64, alpha=1.0, A=PA, lda=None, B=PB, ldb=None, tr
     dict(A=0), dict(B=0), dict(C=0), dict(algo=10), dict(algo=-1),
     dict(M=(1 << 31) - 1024), dict(N=(1 << 31) - 1024), dict(K=(1 << 31) - 1024),
     dict(M=2, K=2, lda=1 << 61),
+    # pointers off a float boundary
+    dict(A=PA + 2), dict(B=PB + 1), dict(C=PC + 3), dict(C=PC + 2, K=0, beta=0.5), dict(A=PA + 6, algo=1),
 ])
 def test_invalid_arguments(kw):
     assert plan(**kw)[0] == INVALID

@@ -1,8 +1,8 @@
 """CPU emulation of the MFMA kernel's direct global->LDS staging (no GPU).
 
-Every wavefront lane of the MFMA kernel loads W floats (W = 4: 16-byte
-global_load_lds_dwordx4; W = 1: 4-byte global_load_lds_dword for unaligned
-operands) of one k-tile into LDS.  Its source offset follows the kernel's
+Every wavefront lane of the MFMA kernel loads W = 4 floats (one 16-byte
+global_load_lds_dwordx4, from any 4-byte aligned address: leading dimensions
+need not be multiples of 4) of one k-tile into LDS.  Its source offset follows the kernel's
 staging code: LDS float e of a k-contiguous tile row holds logical chunk
 (e % BK / 4) XOR swz(row) of that row; rows past M (and, for op(B) = B^T, past
 N) are clamped to the last valid row on edge tiles, and op(B) = B columns past
@@ -18,7 +18,8 @@ every wavefront and lane of each tile geometry the library launches and checks:
 
 Operands are filled with their own flat addresses, so content checks compare
 addresses.  The geometries are the kernel configurations in use: 64 x 64 with
-4 wavefronts, 64 x 64 and 128 x 128 with 8 wavefronts as two k-slices, BK 32.
+4 wavefronts, 64 x 64 and 128 x 128 with 8 wavefronts as two k-slices, and
+256 x 256 with 8 wavefronts, BK 32.
 """
 import numpy as np
 import pytest
@@ -28,12 +29,12 @@ def swz(r, cpr):
     return ((r >> 1) ^ (r >> 2)) & 3 if cpr == 4 else (r ^ (r >> 3)) & 7
 
 
-def stage_and_check(BM, BN, BK, NW, KS, trans_b, dword, edge, M, N, K, lda, ldb, m0, n0, kt, write_swz=swz):
+def stage_and_check(BM, BN, BK, NW, KS, trans_b, edge, M, N, K, lda, ldb, m0, n0, kt, write_swz=swz):
     cpr = BK // 4
     a_sz, b_sz = BM * BK, BK * BN
     slice_sz = a_sz + b_sz
     kt_len = KS * BK
-    W = 1 if dword else 4
+    W = 4
     bw = 64 * W
     a_n, b_n = KS * a_sz // bw // NW, KS * b_sz // bw // NW
     assert a_n * bw * NW == KS * a_sz and b_n * bw * NW == KS * b_sz
@@ -101,26 +102,26 @@ def stage_and_check(BM, BN, BK, NW, KS, trans_b, dword, edge, M, N, K, lda, ldb,
                     assert lds[p] == B[kk, n0 + n], ("B content", sl, n, k)
 
 
-GEOMETRIES = [(64, 64, 32, 4, 1), (64, 64, 32, 8, 2), (128, 128, 32, 8, 2)]
+GEOMETRIES = [(64, 64, 32, 4, 1), (64, 64, 32, 8, 2), (128, 128, 32, 8, 2), (256, 256, 32, 8, 1)]
 
 
 @pytest.mark.parametrize("geo", GEOMETRIES, ids=lambda g: f"{g[0]}x{g[1]}_w{g[3]}_ks{g[4]}")
 @pytest.mark.parametrize("trans_b", [False, True])
-@pytest.mark.parametrize("dword", [True, False], ids=["dword", "dwordx4"])
-def test_direct_staging(geo, trans_b, dword):
+@pytest.mark.parametrize("pad", [(4, 0), (1, 3), (3, 1)], ids=["aligned", "unaligned13", "unaligned31"])
+def test_direct_staging(geo, trans_b, pad):
     BM, BN, BK, NW, KS = geo
+    pa, pb = pad
     K = 4 * KS * BK
-    # an interior tile, leading dimensions unaligned (dword) or aligned (dwordx4)
+    # an interior tile; leading dimensions a multiple of 4 or not
     M = N = 3 * BM
-    stage_and_check(BM, BN, BK, NW, KS, trans_b, dword, False, M, N, K, K + (1 if dword else 4),
-                    (K if trans_b else N) + (3 if dword else 0), BM, BN, 1)
-    # an edge tile in M and N (16-byte loads of op(B) = B need N % 4 == 0)
-    M2, N2 = BM + 37, BN + (21 if dword or trans_b else 20)
-    stage_and_check(BM, BN, BK, NW, KS, trans_b, dword, True, M2, N2, K, K + (3 if dword else 0),
-                    (K if trans_b else N2) + (1 if dword else 0), BM, BN, 2)
+    stage_and_check(BM, BN, BK, NW, KS, trans_b, False, M, N, K, K + pa, (K if trans_b else N) + pb, BM, BN, 1)
+    # an edge tile in M and N (the edge path of op(B) = B needs N % 4 == 0)
+    M2, N2 = BM + 37, BN + (21 if trans_b else 20)
+    stage_and_check(BM, BN, BK, NW, KS, trans_b, True, M2, N2, K, K + pb, (K if trans_b else N2) + pa, BM, BN, 2)
     # an edge tile with a single valid row and column group
-    N3 = BN + (1 if dword or trans_b else 4)
-    stage_and_check(BM, BN, BK, NW, KS, trans_b, dword, True, BM + 1, N3, K, K, K if trans_b else N3, BM, BN, 0)
+    N3 = BN + (1 if trans_b else 4)
+    stage_and_check(BM, BN, BK, NW, KS, trans_b, True, BM + 1, N3, K, K + pa, (K if trans_b else N3) + pb, BM, BN,
+                    0)
 
 
 def test_emulation_catches_planted_mistakes():
@@ -128,7 +129,7 @@ def test_emulation_catches_planted_mistakes():
     # reader's fails on content, and an edge tile staged without the row clamp
     # fails on bounds
     with pytest.raises(AssertionError, match="content"):
-        stage_and_check(64, 64, 32, 4, 1, True, False, False, 192, 192, 128, 132, 132, 64, 64, 1,
+        stage_and_check(64, 64, 32, 4, 1, True, False, 192, 192, 128, 132, 132, 64, 64, 1,
                         write_swz=lambda r, cpr: 0)
     with pytest.raises(AssertionError, match="out of bounds"):
-        stage_and_check(64, 64, 32, 4, 1, True, False, False, 64 + 37, 64 + 21, 128, 128, 128, 64, 64, 2)
+        stage_and_check(64, 64, 32, 4, 1, True, False, 64 + 37, 64 + 21, 128, 128, 128, 64, 64, 2)
