@@ -84,8 +84,10 @@ double mfma_rate(int kid, int64_t M, int64_t N)
 // The FP32 MFMA kernels of the plain call.
 bool is_mfma_f32(int kid)
 {
-    return kid == KID_MFMA_L || kid == KID_MFMA_M || kid == KID_MFMA_S || kid == KID_MFMA_S2;
+    return kid == KID_MFMA_L || kid == KID_MFMA_M || kid == KID_MFMA_S || kid == KID_MFMA_S2 || kid == KID_MFMA_T;
 }
+
+constexpr int64_t kSmallGrid = 144;
 
 int choose_mfma(int64_t M, int64_t N, int64_t K)
 {
@@ -114,6 +116,15 @@ int choose_mfma(int64_t M, int64_t N, int64_t K)
         const int64_t tiles = ceil_div(M, 64) * ceil_div(N, 64);
         if ((tiles <= 256 || tiles > 512) && K >= 256 && tiles * 512 <= kMaxWorkItems)
             best = KID_MFMA_S2;
+        // With at most kSmallGrid tiles of 64 x 64 the grid leaves most CUs
+        // idle (or, above 128 tiles, gives a few of them a second round): the
+        // 32 x 32 tile with k split four ways inside the workgroup gives each
+        // CU one or two workgroups of a quarter of the work.  Measured on
+        // MI355X: 512^3 11.2 -> 5.6 us, 128^3 4.4 -> 4.1 us, 768^3 15.8 ->
+        // 15.2 us, 512 x 512 x 8192 138 -> 46 us; at 169 tiles (832^3) it is
+        // 13% slower.
+        if (tiles <= kSmallGrid)
+            best = KID_MFMA_T;
     }
     return best;
 }
@@ -139,6 +150,7 @@ void split_geometry(int64_t K, int64_t splits, int64_t &kc, int64_t &used)
 constexpr int64_t kSplitMinK = 128;
 constexpr int64_t kSplitLongK = 1024;
 constexpr int64_t kSplitMinTiles = 128;
+constexpr int64_t kPlainSmallWorkgroups = 4;  // 32 x 32 workgroups per 64 x 64 tile
 int64_t auto_splits(int64_t M, int64_t N, int64_t K)
 {
     const TileShape t = tile_shape(KID_MFMA_S);
@@ -151,12 +163,15 @@ int64_t auto_splits(int64_t M, int64_t N, int64_t K)
     int64_t s = 256 / tiles;
     s = s < K / kSplitMinK ? s : K / kSplitMinK;
     s = s < kMaxSplits ? s : kMaxSplits;
-    return s > 1 ? s : 1;
+    // Such grids run the plain call on the 32 x 32 tile: four workgroups per
+    // 64 x 64 tile, each with all of k.  Four splits or fewer add a reduction
+    // for no more workgroups (512^3: 5.6 us plain against 9.5 us in 4 splits).
+    return s > kPlainSmallWorkgroups ? s : 1;
 }
 
 int threads_per_block(int kid)
 {
-    return (kid == KID_MFMA_L || kid == KID_MFMA_M || kid == KID_MFMA_S2) ? 512 : 256;
+    return (kid == KID_MFMA_L || kid == KID_MFMA_M || kid == KID_MFMA_S2) ? 512 : 256;  // KID_MFMA_T: 256
 }
 
 Plan make_plan(int algo, int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
@@ -168,7 +183,7 @@ Plan make_plan(int algo, int64_t M, int64_t N, int64_t K, float alpha, const flo
         p.kid = KID_NONE;
         return p;
     };
-    if (algo < SGEMM_ALGO_AUTO || algo > SGEMM_ALGO_MFMA_64)
+    if (algo < SGEMM_ALGO_AUTO || algo > SGEMM_ALGO_MFMA_32)
         return fail(SGEMM_ERR_INVALID_VALUE);
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
         return fail(SGEMM_ERR_INVALID_VALUE);
@@ -214,6 +229,7 @@ Plan make_plan(int algo, int64_t M, int64_t N, int64_t K, float alpha, const flo
     case SGEMM_ALGO_MFMA_256: p.kid = KID_MFMA_L; break;
     case SGEMM_ALGO_MFMA_128: p.kid = KID_MFMA_M; break;
     case SGEMM_ALGO_MFMA_64: p.kid = KID_MFMA_S; break;
+    case SGEMM_ALGO_MFMA_32: p.kid = KID_MFMA_T; break;
     }
     const TileShape t = tile_shape(p.kid);
     p.tiles_m = ceil_div(M, t.bm);
@@ -295,6 +311,7 @@ const char *kernel_label(int kid)
     case KID_MFMA_M: return "mfma_128x128x32_w2x2_ks2";
     case KID_MFMA_S: return "mfma_64x64x32_w2x2";
     case KID_MFMA_S2: return "mfma_64x64x32_w2x2_ks2";
+    case KID_MFMA_T: return "mfma_32x32x32_w1x1_ks4";
     case KID_MFMA_L_SK: return "mfma_256x256x32_w4x2_streamk";
     case KID_MFMA_M_SK: return "mfma_128x128x32_w2x2_ks2_streamk";
     case KID_MFMA_LP_F16: return "mfma_lp_f16_256x256x32_w4x2";
@@ -728,6 +745,10 @@ WsChoice ws_auto(int64_t M, int64_t N, int64_t K, float alpha, const float *A, i
         c.method = 1;
         return c;
     }
+    // Grids that the plain call runs on the 32 x 32 tile are too small for the
+    // stream-K schedule to pay for its fix-up.
+    if (c.split.base.kid == KID_MFMA_T)
+        return c;
     c.sk = make_sk_plan(0, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc);
     if (c.sk.base.status == SGEMM_OK && c.sk.kid != KID_NONE && c.sk.sk.sk_tiles > 0 &&
         sk_time_us(c.sk, K) < 0.99 * plain_time_us(M, N, K))

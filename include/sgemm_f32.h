@@ -97,15 +97,18 @@ typedef enum {
  *                    the naive and 2-D block-tiled CUDA matmul, paragraph on the
  *                    naive implementation: one block per output element with an
  *                    in-block reduction).
- *   MFMA_256, MFMA_128, MFMA_64
+ *   MFMA_256, MFMA_128, MFMA_64, MFMA_32
  *                    the MFMA path with its workgroup tile fixed: 256 x 256 (8
- *                    wavefronts), 128 x 128 (8 wavefronts as two k-slices of 4) or
- *                    64 x 64 (4 wavefronts, up to 4 workgroups per CU).
+ *                    wavefronts), 128 x 128 (8 wavefronts as two k-slices of 4),
+ *                    64 x 64 (4 wavefronts, up to 4 workgroups per CU) or 32 x 32
+ *                    (4 wavefronts, each a k-slice of a quarter of k; 2 per CU).
  *   AUTO             MFMA with a tile chosen from the problem shape; where it picks
  *                    the 64 x 64 tile it runs it as 8 wavefronts (two k-slices of
  *                    4, kernel id 45) unless the grid is 257 to 512 tiles or K
  *                    is below 256, where the 4-wavefront kernel (id 42, as
- *                    MFMA_64) is faster.
+ *                    MFMA_64) is faster; and where that grid has at most 144
+ *                    tiles (too few to fill the 256 CUs) it takes the 32 x 32
+ *                    tile (kernel id 46, as MFMA_32).
  */
 typedef enum {
     SGEMM_ALGO_AUTO = 0,
@@ -117,7 +120,8 @@ typedef enum {
     SGEMM_ALGO_NAIVE_WG = 6,
     SGEMM_ALGO_MFMA_256 = 7,
     SGEMM_ALGO_MFMA_128 = 8,
-    SGEMM_ALGO_MFMA_64 = 9
+    SGEMM_ALGO_MFMA_64 = 9,
+    SGEMM_ALGO_MFMA_32 = 10
 } sgemm_algo;
 
 /*

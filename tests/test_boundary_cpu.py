@@ -19,7 +19,7 @@ HEADER = os.path.join(ROOT, "include", "sgemm_f32.h")
 OK, INVALID, ALIAS = 0, 1, 2
 KID_NONE, KID_SCALE, KID_NAIVE, KID_TILED, KID_TILED_NOPAD, KID_REG = 0, 1, 10, 20, 21, 30
 KID_NAIVE_WG = 11
-KID_L, KID_M, KID_S, KID_S2 = 40, 41, 42, 45
+KID_L, KID_M, KID_S, KID_S2, KID_T = 40, 41, 42, 45, 46
 
 # Fake, well-separated "device" addresses: planning only compares ranges.
 PA, PB, PC = 1 << 32, 1 << 40, 1 << 44
@@ -72,7 +72,7 @@ def call(algo=0, M=64, N=64, K=64, alpha=1.0, A=PA, lda=None, B=PB, ldb=None, tr
     dict(M=-1), dict(N=-1), dict(K=-1), dict(M=1 << 31), dict(K=1 << 31),
     dict(transB=2), dict(transB=-1),
     dict(lda=63), dict(ldb=63), dict(ldc=63), dict(transB=1, ldb=63),
-    dict(A=0), dict(B=0), dict(C=0), dict(algo=10), dict(algo=-1),
+    dict(A=0), dict(B=0), dict(C=0), dict(algo=11), dict(algo=-1),
     dict(M=(1 << 31) - 1024), dict(N=(1 << 31) - 1024), dict(K=(1 << 31) - 1024),
     dict(M=2, K=2, lda=1 << 61),
     # pointers off a float boundary
@@ -130,7 +130,7 @@ def test_product_free_cases_scale_c():
 
 
 @pytest.mark.parametrize("algo,kid", [(1, KID_NAIVE), (2, KID_TILED), (3, KID_REG), (5, KID_TILED_NOPAD),
-                                      (6, KID_NAIVE_WG), (7, KID_L), (8, KID_M), (9, KID_S)])
+                                      (6, KID_NAIVE_WG), (7, KID_L), (8, KID_M), (9, KID_S), (10, KID_T)])
 def test_explicit_algorithms(algo, kid):
     st, k, tm, tn, name = plan(algo=algo, M=1000, N=1017, K=999)
     assert (st, k) == (OK, kid)
@@ -144,6 +144,8 @@ def test_explicit_algorithms(algo, kid):
         assert (tm, tn) == (4, 4) and name.startswith("mfma_256x256")
     elif kid == KID_S:
         assert (tm, tn) == (16, 16) and name.startswith("mfma_64x64")
+    elif kid == KID_T:
+        assert (tm, tn) == (32, 32) and name.startswith("mfma_32x32x32_w1x1_ks4")
     else:
         assert (tm, tn) == (8, 8)
 
@@ -156,10 +158,16 @@ def test_explicit_algorithms(algo, kid):
     # the 64 x 64 tile: 8 wavefronts (k split in two) unless the grid is 257..512 tiles or K < 256
     ((1024, 1024, 1024), KID_S2, (16, 16)),
     ((1000, 1017, 999), KID_S2, (16, 16)),
-    ((512, 512, 512), KID_S2, (8, 8)),
-    ((128, 128, 128), KID_S, (2, 2)),          # K < 256: the 4-wavefront kernel
-    ((1, 1, 1), KID_S, (1, 1)),
-    ((128, 128, 256), KID_S2, (2, 2)),
+    ((832, 832, 832), KID_S2, (13, 13)),       # 169 tiles
+    ((768, 1024, 512), KID_S2, (12, 16)),      # 192 tiles
+    # at most 144 tiles of 64 x 64: the 32 x 32 tile, k split four ways
+    ((768, 768, 768), KID_T, (24, 24)),        # 144 tiles of 64 x 64
+    ((512, 512, 512), KID_T, (16, 16)),
+    ((128, 128, 128), KID_T, (4, 4)),
+    ((1, 1, 1), KID_T, (1, 1)),
+    ((128, 128, 256), KID_T, (4, 4)),
+    ((512, 512, 8192), KID_T, (16, 16)),
+    ((128, 4096, 1024), KID_T, (4, 128)),
     ((1280, 1280, 1280), KID_S, (20, 20)),     # 400 tiles
     ((512, 4096, 4096), KID_S, (8, 64)),       # 512 tiles
     ((576, 4096, 1024), KID_S2, (9, 64)),      # 576 tiles

@@ -9,7 +9,7 @@ import pytest
 import fp32_gemm_08_amd as lib
 
 OK, INVALID, ALIAS = 0, 1, 2
-KID_L, KID_M, KID_S, KID_S2 = 40, 41, 42, 45
+KID_L, KID_M, KID_S, KID_S2, KID_T = 40, 41, 42, 45, 46
 PA, PB, PC, PW = 1 << 32, 1 << 40, 1 << 44, 1 << 48
 
 
@@ -23,15 +23,17 @@ def built():
     ((4096, 4096, 4096), (1, KID_L, 0)),          # fills the chip: never split
     ((2048, 2048, 2048), (1, KID_M, 0)),
     ((1024, 1024, 1024), (1, KID_S2, 0)),         # 256 tiles of 64 x 64: the plain call's kernel
-    ((512, 512, 512), (4, KID_S, 4 * 512 * 512 * 4)),
-    ((768, 768, 768), (1, KID_S2, 0)),             # 144 tiles: over half the CUs busy already
+    ((512, 512, 512), (1, KID_T, 0)),            # 4 splits: no more workgroups than the plain 32 x 32 grid
+    ((700, 333, 1500), (1, KID_T, 0)),           # 3 splits
+    ((300, 333, 1500), (8, KID_S, 8 * 300 * 333 * 4)),
+    ((768, 768, 768), (1, KID_T, 0)),              # 144 tiles: over half the CUs busy already
     ((512, 512, 8192), (8, KID_S, 8 * 512 * 512 * 4)),       # two workgroups per CU, 1024 of k each
     ((256, 256, 8192), (16, KID_S, 16 * 256 * 256 * 4)),     # two per CU would leave only 256 of k
     ((256, 256, 32768), (32, KID_S, 32 * 256 * 256 * 4)),
     ((512, 256, 16384), (16, KID_S, 16 * 512 * 256 * 4)),
     ((384, 384, 8192), (7, KID_S, 7 * 384 * 384 * 4)),       # 36 tiles: 14 splits would get 585 of k
     ((64, 64, 65536), (64, KID_S, 64 * 64 * 64 * 4)),
-    ((128, 128, 128), (1, KID_S, 0)),             # k too short to split at 256 per split
+    ((128, 128, 128), (1, KID_T, 0)),             # k too short to split at 256 per split
 ])
 def test_auto_split_choice(shape, auto):
     st, used, kid, nbytes = lib.sgemm_f32_splitk_plan(0, *shape)
@@ -42,7 +44,7 @@ def test_explicit_split_geometry():
     # K = 100 in 8 splits: 32 per split (whole k-tiles) leaves 4 non-empty splits.
     assert lib.sgemm_f32_splitk_plan(8, 512, 512, 100)[:2] == (OK, 4)
     # K <= 32 cannot split.
-    assert lib.sgemm_f32_splitk_plan(4, 512, 512, 32)[1:] == (1, KID_S, 0)    # the plain call's kernel
+    assert lib.sgemm_f32_splitk_plan(4, 512, 512, 32)[1:] == (1, KID_T, 0)    # the plain call's kernel
     # an explicit count splits any shape, always with the 64 x 64 partial tile
     assert lib.sgemm_f32_splitk_plan(4, 1024, 1024, 1024)[1:] == (4, KID_S, 4 * 1024 * 1024 * 4)
     assert lib.sgemm_f32_splitk_plan(16, 4096, 4096, 4096)[1:] == (16, KID_S, 16 * 4096 * 4096 * 4)
@@ -76,7 +78,7 @@ def test_invalid_calls(kw):
 
 
 @pytest.mark.parametrize("kw", [dict(W=PA), dict(W=PC + 16), dict(W=PB - 2 * 512 * 512 * 4 + 16),
-                                dict(splits=None, W=PA + 16)])
+                                dict(splits=None, K=8192, W=PA + 16)])   # AUTO splits 512 x 512 x 8192
 def test_workspace_alias(kw):
     # the 2-split partials need 2 * 512 * 512 * 4 bytes from W on
     kw.setdefault("splits", 2)

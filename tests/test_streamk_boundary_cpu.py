@@ -88,7 +88,8 @@ def test_quick_returns():
     assert (st, dp, skt, wk, need) == (OK, 0, 0, 0, 0)
 
 
-@pytest.mark.parametrize("shape,method", [((4608, 4608, 4608), 2), ((3072, 3072, 3072), 2), ((512, 512, 512), 1),
+@pytest.mark.parametrize("shape,method", [((4608, 4608, 4608), 2), ((3072, 3072, 3072), 2), ((512, 512, 512), 0),
+                                          ((300, 333, 1500), 1),
                                           ((256, 256, 8192), 1), ((4096, 4096, 4096), 0), ((8192, 8192, 8192), 0),
                                           ((1024, 1024, 1024), 0)])
 def test_ws_plan_method(shape, method):

@@ -64,8 +64,8 @@ def check_pair(oracle_lib, case, splits, what):
 
 
 def test_two_calls_second_smaller(oracle_lib):
-    big = make_case(512, 512, 4096, trans_b=False, alpha=1.0, beta=1.0, dist="normal", seed=61)
-    check_pair(oracle_lib, big, 0, "512x512x4096 auto")
+    big = make_case(256, 256, 4096, trans_b=False, alpha=1.0, beta=1.0, dist="normal", seed=61)
+    check_pair(oracle_lib, big, 0, "256x256x4096 auto")
     small = make_case(200, 136, 1000, trans_b=True, alpha=1.5, beta=-0.5, dist="uniform", seed=62)
     check_pair(oracle_lib, small, 0, "200x136x1000 B^T auto")
 
