@@ -48,20 +48,68 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra=()) -> str:
+# Debug variants, built next to the library on request and loaded through
+# SGEMM_F32_LIBRARY (the product build is libsgemm_f32.so):
+#   poison    every LDS stage NaN-filled before it is staged (SGEMM_DEBUG_POISON_LDS)
+#   sanitize  host code under AddressSanitizer and UndefinedBehaviorSanitizer
+#             (device code as in the library), for the argument checks,
+#             planning and entry points of the C ABI on a machine without a
+#             GPU; load it with the sanitizer runtime preloaded
+#             (sanitizer_runtime())
+VARIANTS = {
+    "poison": ["-DSGEMM_DEBUG_POISON_LDS"],
+    "sanitize": ["-DSGEMM_DEBUG_SANITIZE", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+                 "-Xarch_host", "-shared-libsan"],
+}
+
+
+def variant_path(variant: str) -> str:
+    return os.path.join(PKG, f"libsgemm_f32_{variant}.so")
+
+
+def sanitizer_runtime() -> str:
+    """Path of the clang AddressSanitizer runtime the sanitize variant links."""
+    r = subprocess.run([hipcc(), "--print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("clang AddressSanitizer runtime not found")
+    return path
+
+
+def build(verbose: bool = False, extra=(), variant: str = "") -> str:
+    if variant and variant not in VARIANTS:
+        raise ValueError(f"unknown variant {variant!r}")
+    if variant:
+        global BUILD
+        saved, BUILD = BUILD, os.path.join(BUILD, variant)
+        try:
+            return _build(verbose, list(extra) + VARIANTS[variant], variant_path(variant), variant)
+        finally:
+            BUILD = saved
+    return _build(verbose, extra, LIB, "")
+
+
+def _build(verbose, extra, lib, variant) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    link_extra = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-shared-libsan"] if variant == "sanitize" else []
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + link_extra + ["-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True, extra=sys.argv[1:])
+    args = sys.argv[1:]
+    var = ""
+    if args and args[0].startswith("--variant="):
+        var = args.pop(0).split("=", 1)[1]
+    build(verbose=True, extra=args, variant=var)

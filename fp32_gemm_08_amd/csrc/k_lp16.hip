@@ -123,6 +123,7 @@ __global__ __launch_bounds__(Q::NT) void lp16_gemm_kernel(Lp16Args g)
     // Request the k-tile `src` into the buffer of stage `slot`.
     auto issue = [&](int src, int slot) {
         unsigned char *st = smem + (slot % Q::S) * Q::STAGE;
+        poison_lds(st, Q::STAGE);
 #pragma unroll
         for (int j = 0; j < Q::NA; ++j)
             q_load(pa[j] + (int64_t)src * g.slab_a, st + (w * Q::NA + j) * 1024);
@@ -295,6 +296,7 @@ __global__ __launch_bounds__(256) void lp16_round_transpose(const float *B, int6
     __shared__ T t[64][64 + 8];
     T *dst = static_cast<T *>(dst_);
     const int n0 = blockIdx.x * 64, k0 = blockIdx.y * 64;
+    poison_lds(t, (int)sizeof(t));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int e = threadIdx.x + 256 * i;

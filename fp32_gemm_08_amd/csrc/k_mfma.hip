@@ -170,7 +170,7 @@ struct Geo {
     static constexpr int RED = (KS - 1) * NWO * ACC * 64;  // floats for the k-slice reduction
     static constexpr int SMEM = (NS * STAGE > RED) ? NS * STAGE : RED;
     static_assert(WM % 32 == 0 && WN % 32 == 0, "tile shape");
-    static_assert(BK == 16 || BK == 32, "the chunk permutation covers 4 or 8 chunks per row");
+    static_assert(BK == 16 || BK == 32 || BK == 64, "the chunk permutation covers 4, 8 or 16 chunks per row");
     static_assert((KS * BM * CPR) % NT == 0 && (KS * BK * BN / 4) % NT == 0, "register staging split");
     static_assert(A_SZ % 256 == 0 && B_SZ % 256 == 0, "whole 1 KB blocks");
     static_assert((KS * A_BLK) % NW == 0 && (KS * B_BLK) % NW == 0, "direct staging split");
@@ -200,14 +200,17 @@ struct Role {
 // Physical 16-byte chunk of logical chunk c in row r of a k-contiguous tile.
 // Rows r..r+7 get 8 distinct permutations (CPR=8), and any 16 rows split into
 // pairs (r mod 2 or r mod 4) that differ too, so 8- and 16-lane read phases
-// both touch every bank once.
+// both touch every bank once.  With CPR=16 a row is a whole 256-byte bank row
+// and rows r..r+15 get 16 distinct chunks.
 template <int CPR>
 __device__ __forceinline__ int swz(int r)
 {
     if constexpr (CPR == 4)
         return ((r >> 1) ^ (r >> 2)) & 3;
-    else
+    else if constexpr (CPR == 8)
         return (r ^ (r >> 3)) & 7;
+    else
+        return (r ^ (r >> 4)) & 15;
 }
 
 // Float offset of logical chunk c of row r in a k-contiguous tile.
@@ -457,6 +460,7 @@ __device__ __forceinline__ bool reduce_slices(f32x16 (&acc)[Gm::FM][Gm::FN], flo
         return true;
     } else {
         __syncthreads();  // every wavefront is done with the stage buffers
+        poison_lds(smem, Gm::RED * 4);
         if (ro.slice > 0) {
             float *dst = smem + ((ro.slice - 1) * Gm::NWO + ro.wo) * Gm::ACC * 64 + ro.lane;
 #pragma unroll
@@ -666,6 +670,7 @@ __device__ __forceinline__ void gemm_tile_regs(const GemmArgs &a, float *smem, i
     const int nk = (a.K + Gm::KT - 1) / Gm::KT;
     Frags<Gm, TRANS_B> f[2];
     gload(0);
+    poison_lds(smem, Gm::STAGE * 4);
     st.store(smem);
     if (nk > 1)
         gload(1);
@@ -680,6 +685,7 @@ __device__ __forceinline__ void gemm_tile_regs(const GemmArgs &a, float *smem, i
         for (int g = 0; g < G; ++g) {
             group_step<Gm, TRANS_B>(acc, f[g & 1], [&] {
                 if (g == 0 && t + 1 < nk) {
+                    poison_lds(Sn, Gm::STAGE * 4);
                     st.store(Sn);   // stage t+1 into the free buffer
                     if (t + 2 < nk)
                         gload(t + 2);
@@ -724,8 +730,10 @@ __device__ __forceinline__ void gemm_tile_direct(const GemmArgs &a, float *smem,
 
     DirectStage<Gm, TRANS_B> ds;
     ds.template init<EDGE>(a, m0, n0);
-    if (nf > 0)
+    if (nf > 0) {
+        poison_lds(buf0, Gm::STAGE * 4);
         ds.issue(0, buf0);
+    }
 
     // Partial last stage first (the order of the k sum is free): registers with
     // zero fill, through buffer 1, while stage 0 lands in buffer 0.
@@ -733,6 +741,7 @@ __device__ __forceinline__ void gemm_tile_direct(const GemmArgs &a, float *smem,
         RegStage<Gm, TRANS_B> st;
         st.init(a, m0, n0);
         st.template load<true>(a, m0, n0, nf);
+        poison_lds(buf1, Gm::STAGE * 4);
         st.store(buf1);
         __syncthreads();
 #pragma unroll
@@ -751,6 +760,7 @@ __device__ __forceinline__ void gemm_tile_direct(const GemmArgs &a, float *smem,
             // All loads of stage t+1 go out first: measured against spreading them
             // over the MFMA steps, issuing them together at the top is faster.
             if (t + 1 < nf) {
+                poison_lds(Sn, Gm::STAGE * 4);
                 ds.issue(t + 1, Sn);
                 pin_order();
             }
@@ -831,14 +841,17 @@ __device__ __forceinline__ void gemm_tile_direct_ring(const GemmArgs &a, float *
     ds.template init<EDGE>(a, m0, n0);
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s)
-        if (s < nf)
+        if (s < nf) {
+            poison_lds(smem + s * Gm::STAGE, Gm::STAGE * 4);
             ds.issue(s, smem + s * Gm::STAGE);
+        }
 
     if (nf * Gm::KT < a.K) {
         float *tb = smem + (NS - 1) * Gm::STAGE;
         RegStage<Gm, TRANS_B> st;
         st.init(a, m0, n0);
         st.template load<true>(a, m0, n0, nf);
+        poison_lds(tb, Gm::STAGE * 4);
         st.store(tb);
         __syncthreads();
 #pragma unroll
@@ -858,6 +871,7 @@ __device__ __forceinline__ void gemm_tile_direct_ring(const GemmArgs &a, float *
             const int nxt = cur + 1 == NS ? 0 : cur + 1;
             if (t + NS - 1 < nf) {
                 const int fr = cur == 0 ? NS - 1 : cur - 1;  // the buffer stage t-1 used
+                poison_lds(smem + fr * Gm::STAGE, Gm::STAGE * 4);
                 ds.issue(t + NS - 1, smem + fr * Gm::STAGE);
                 pin_order();
             }

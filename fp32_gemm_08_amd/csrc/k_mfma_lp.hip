@@ -223,6 +223,7 @@ __global__ __launch_bounds__(Gm::NT) void sgemm_mfma_lp_kernel(GemmArgs g)
             st.template load<true>(g, m0, n0, k0);
     };
     load_tile(0);
+    poison_lds(smem, LP_STAGE * (int)sizeof(T));
     st.store(smem, smem + LBM * LP_PITCH);
     __syncthreads();
 
@@ -248,6 +249,7 @@ __global__ __launch_bounds__(Gm::NT) void sgemm_mfma_lp_kernel(GemmArgs g)
         }
         if (kt + 1 < nk) {
             T *nas = smem + ((kt + 1) & 1) * LP_STAGE;
+            poison_lds(nas, LP_STAGE * (int)sizeof(T));
             st.store(nas, nas + LBM * LP_PITCH);
         }
         __syncthreads();

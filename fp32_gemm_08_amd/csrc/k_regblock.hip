@@ -84,6 +84,8 @@ __global__ __launch_bounds__(256) void sgemm_regblock_kernel(GemmArgs a)
     const int nk = (a.K + BK - 1) / BK;
     f32x4 va, vb;
     gload(0, va, vb);
+    poison_lds(As[0], sizeof(As[0]));
+    poison_lds(Bs[0], sizeof(Bs[0]));
     sstore(0, va, vb);
     __syncthreads();
     for (int t = 0; t < nk; ++t) {
@@ -104,8 +106,11 @@ __global__ __launch_bounds__(256) void sgemm_regblock_kernel(GemmArgs a)
                 for (int j = 0; j < 8; ++j)
                     acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
         }
-        if (t + 1 < nk)
+        if (t + 1 < nk) {
+            poison_lds(As[cur ^ 1], sizeof(As[0]));
+            poison_lds(Bs[cur ^ 1], sizeof(Bs[0]));
             sstore(cur ^ 1, va, vb);
+        }
         __syncthreads();
     }
 

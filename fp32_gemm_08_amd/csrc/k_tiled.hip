@@ -96,6 +96,7 @@ __global__ __launch_bounds__(kLanes) void sgemm_tiled_kernel(GemmArgs g)
 
     PanelStager<TRANS_B, PAD> st;
     st.fetch(g, m0, n0, 0, tid);
+    poison_lds(&buf[0], sizeof(PanelBuf<PAD>));
     st.deposit(buf[0], tid);
     __syncthreads();
 
@@ -111,6 +112,7 @@ __global__ __launch_bounds__(kLanes) void sgemm_tiled_kernel(GemmArgs g)
         if (more) {
             // buf[(p + 1) & 1] was last read in panel p - 1, before the barrier
             // that ended it
+            poison_lds(&buf[(p + 1) & 1], sizeof(PanelBuf<PAD>));
             st.deposit(buf[(p + 1) & 1], tid);
             __syncthreads();
         }

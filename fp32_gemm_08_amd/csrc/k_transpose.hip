@@ -195,6 +195,7 @@ __global__ __launch_bounds__(256) void transpose_pipe_kernel(TransposeArgs a)
             m.template load<true>(a, r0, c0, w, lane);
     }
     for (; t < tiles; t += gridDim.x) {
+        poison_lds(tile, (int)sizeof(tile));
         m.to_lds(tile, w, lane);
         __syncthreads();
         const int cr0 = r0, cc0 = c0;
@@ -235,6 +236,7 @@ __global__ __launch_bounds__(TH) void transpose_tile_kernel(TransposeArgs a)
             m.template load<false>(a, r0, c0, w, lane);
         else
             m.template load<true>(a, r0, c0, w, lane);
+        poison_lds(tile, (int)sizeof(tile));
         m.to_lds(tile, w, lane);
         __syncthreads();
         if (full)

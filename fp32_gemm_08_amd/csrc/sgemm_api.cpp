@@ -1218,7 +1218,16 @@ const char *sgemm_f32_status_string(int status)
     }
 }
 
-const char *sgemm_f32_version(void) { return "sgemm_f32 0.1.0 (gfx950)"; }
+const char *sgemm_f32_version(void)
+{
+#if defined(SGEMM_DEBUG_POISON_LDS)
+    return "sgemm_f32 0.1.0 (gfx950, debug: LDS poisoned before staging)";
+#elif defined(SGEMM_DEBUG_SANITIZE)
+    return "sgemm_f32 0.1.0 (gfx950, debug: host code under ASan and UBSan)";
+#else
+    return "sgemm_f32 0.1.0 (gfx950)";
+#endif
+}
 
 int sgemm_f32_arch_status(const char *arch) { return sgemm::arch_status(arch); }
 

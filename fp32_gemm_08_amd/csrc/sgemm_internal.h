@@ -115,6 +115,32 @@ TileShape lp_tile_shape(bool large);
 hipError_t launch_splitk_reduce(const float *W, int splits, int64_t stride, int M, int N, float alpha, float beta,
                                 float *C, int64_t ldc, bool vec, hipStream_t stream);
 
+// Debug build (-DSGEMM_DEBUG_POISON_LDS): before a workgroup stages data
+// into an LDS region, the whole region is filled with a pattern that reads
+// as NaN in FP32, FP16 and BF16 (0x7fc07fc0 per 32-bit word), every
+// work-item a share, and the workgroup meets a barrier.  A read of a
+// location the staging never writes, a read that runs ahead of the copy
+// that fills it, or a staging write that lands while another wavefront
+// still reads the previous contents (the missing second barrier of
+// "CUDA矩阵乘法性能优化实战：从朴素内核到寄存器分块与Nsight剖析", section 3.2)
+// then puts a NaN into the result, where the parity checks see it.  In the
+// normal build the call is empty.  Call it from uniform control flow only.
+#ifdef SGEMM_DEBUG_POISON_LDS
+constexpr bool kPoisonLds = true;
+#else
+constexpr bool kPoisonLds = false;
+#endif
+
+__device__ __forceinline__ void poison_lds(void *p, int bytes)
+{
+    if constexpr (kPoisonLds) {
+        uint32_t *w = static_cast<uint32_t *>(p);
+        for (int i = (int)threadIdx.x; i < bytes / 4; i += (int)blockDim.x)
+            w[i] = 0x7fc07fc0u;
+        __syncthreads();
+    }
+}
+
 // Number of workgroup tiles along one dimension.
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

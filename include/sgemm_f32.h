@@ -466,7 +466,8 @@ int sgemm_f32_ws_plan(int64_t M, int64_t N, int64_t K, int transB, int *method, 
 /* Static, NUL-terminated text for a status code (unknown codes included). */
 const char *sgemm_f32_status_string(int status);
 
-/* Static, NUL-terminated library version string. */
+/* Static, NUL-terminated library version string; debug builds of the library
+ * (LDS poisoning, host sanitizers) say so in it. */
 const char *sgemm_f32_version(void);
 
 /*

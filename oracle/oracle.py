@@ -24,7 +24,11 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 ORACLE_SRC = os.path.join(_HERE, "oracle_gemm.c")
-ORACLE_SO = os.path.join(_HERE, "liboracle_gemm.so")
+# SGEMM_ORACLE_LIBRARY names another build of the same source (the
+# sanitizer build below); by default the gcc build next to this file is used.
+ORACLE_GCC_SO = os.path.join(_HERE, "liboracle_gemm.so")
+ORACLE_SO = os.environ.get("SGEMM_ORACLE_LIBRARY") or ORACLE_GCC_SO
+ORACLE_SANITIZE_SO = os.path.join(_HERE, "liboracle_gemm_sanitize.so")
 
 _lock = threading.Lock()
 _lib = None
@@ -32,13 +36,27 @@ _lib = None
 
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc (-O2, no fast math, no FP contraction)."""
-    if force or not os.path.exists(ORACLE_SO):
-        tmp = ORACLE_SO + ".tmp"
+    if force or not os.path.exists(ORACLE_GCC_SO):
+        tmp = ORACLE_GCC_SO + ".tmp"
         cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp",
                "-ffp-contract=off", "-fno-fast-math", ORACLE_SRC, "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
-        os.replace(tmp, ORACLE_SO)
-    return ORACLE_SO
+        os.replace(tmp, ORACLE_GCC_SO)
+    return ORACLE_GCC_SO
+
+
+def build_sanitized(clang: str = "/opt/rocm/llvm/bin/clang") -> str:
+    """The same source under AddressSanitizer and UndefinedBehaviorSanitizer,
+    built by clang (whose shared sanitizer runtime the sanitized GEMM library
+    uses too), with its OpenMP runtime found through an rpath."""
+    libdir = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(clang))), "lib")
+    tmp = ORACLE_SANITIZE_SO + ".tmp"
+    cmd = [clang, "-O1", "-g", "-std=c99", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer",
+           "-shared-libsan", ORACLE_SRC, "-o", tmp, "-lm", f"-Wl,-rpath,{libdir}"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, ORACLE_SANITIZE_SO)
+    return ORACLE_SANITIZE_SO
 
 
 def _load():
