@@ -32,12 +32,15 @@
 //     that share rows of A and columns of B run on the same L2.
 //
 // Two staging paths fill the same LDS layout:
-//   * direct (interior tiles, 16-byte aligned operands): global_load_lds_dwordx4
-//     writes each 1 KB LDS block straight from memory, no registers involved.
-//     Tile t+1 is issued at the start of iteration t into the free buffer and must
-//     land before the iteration's barrier.  A partial last k-tile (K % BK != 0) is
+//   * direct (interior tiles, and edge tiles whose clamped addresses stay
+//     exact): global_load_lds_dwordx4 writes each 1 KB LDS block straight from
+//     memory, no registers involved, 16 bytes per lane from any float-aligned
+//     address (leading dimensions need not be multiples of 4).  Tile t+1 is
+//     issued at the start of iteration t into the free buffer and must land
+//     before the iteration's barrier.  A partial last k-tile (K % BK != 0) is
 //     staged through registers with zero fill and multiplied first.
-//   * registers (edge tiles, unaligned operands): masked loads into registers,
+//   * registers (edge tiles of op(B) = B with N % 4 != 0, and leading
+//     dimensions too large for 32-bit offsets): masked loads into registers,
 //     one tile ahead: iteration t stores tile t+1 to the free buffer and issues
 //     the loads of tile t+2.
 // In both, each k-group's fragments are read while the previous group's MFMAs
@@ -140,12 +143,9 @@ __device__ __forceinline__ f32x4 load4(const float *p, bool ok, int first, int l
 // k-range of one output tile over KS groups of wavefronts ("k-slices"): an LDS
 // stage then holds KS consecutive BK-deep k-tiles, slice s multiplies the s-th
 // into its own accumulators, and the slices are added in LDS at the end.
-// NS: LDS stages of the direct path (2: double buffering; 3 or more: a ring
-// in which stage t+NS-1 is loaded while stage t is multiplied).
-template <int BM_, int BN_, int BK_, int WGM_, int WGN_, int OCC_, bool TRANS_B, int KS_ = 1, bool OPQ_ = false,
-          int NS_ = 2>
+template <int BM_, int BN_, int BK_, int WGM_, int WGN_, int OCC_, bool TRANS_B, int KS_ = 1, bool OPQ_ = false>
 struct Geo {
-    static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_, OCC = OCC_, KS = KS_, NS = NS_;
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_, OCC = OCC_, KS = KS_;
     static constexpr bool OPQ = OPQ_;                  // per-lane ids behind an asm (stream-K)
     static constexpr int NWO = WGM * WGN;              // wavefronts per k-slice (one output tile)
     static constexpr int NW = NWO * KS;                // wavefronts per workgroup
@@ -168,16 +168,15 @@ struct Geo {
     static constexpr int B_BLK_W = KS * B_BLK / NW;
     static constexpr int ACC = FM * FN * 16;           // accumulators per lane
     static constexpr int RED = (KS - 1) * NWO * ACC * 64;  // floats for the k-slice reduction
-    static constexpr int SMEM = (NS * STAGE > RED) ? NS * STAGE : RED;
+    static constexpr int SMEM = (2 * STAGE > RED) ? 2 * STAGE : RED;
     static_assert(WM % 32 == 0 && WN % 32 == 0, "tile shape");
-    static_assert(BK == 16 || BK == 32 || BK == 64, "the chunk permutation covers 4, 8 or 16 chunks per row");
+    static_assert(BK == 16 || BK == 32, "the chunk permutation covers 4 or 8 chunks per row");
     static_assert((KS * BM * CPR) % NT == 0 && (KS * BK * BN / 4) % NT == 0, "register staging split");
     static_assert(A_SZ % 256 == 0 && B_SZ % 256 == 0, "whole 1 KB blocks");
     static_assert((KS * A_BLK) % NW == 0 && (KS * B_BLK) % NW == 0, "direct staging split");
     static_assert(TRANS_B || 256 % BN == 0, "op(B)=B rows must tile a 1 KB block");
     static_assert(SMEM * 4 <= 160 * 1024, "LDS budget");
     static_assert(G % 2 == 0, "the fragment ping-pong needs an even number of k-groups");
-    static_assert(NS >= 2 && NS <= 4, "LDS stages");
 };
 
 // What one wavefront does: its k-slice and its place in the output tile.
@@ -200,17 +199,14 @@ struct Role {
 // Physical 16-byte chunk of logical chunk c in row r of a k-contiguous tile.
 // Rows r..r+7 get 8 distinct permutations (CPR=8), and any 16 rows split into
 // pairs (r mod 2 or r mod 4) that differ too, so 8- and 16-lane read phases
-// both touch every bank once.  With CPR=16 a row is a whole 256-byte bank row
-// and rows r..r+15 get 16 distinct chunks.
+// both touch every bank once.
 template <int CPR>
 __device__ __forceinline__ int swz(int r)
 {
     if constexpr (CPR == 4)
         return ((r >> 1) ^ (r >> 2)) & 3;
-    else if constexpr (CPR == 8)
-        return (r ^ (r >> 3)) & 7;
     else
-        return (r ^ (r >> 4)) & 15;
+        return (r ^ (r >> 3)) & 7;
 }
 
 // Float offset of logical chunk c of row r in a k-contiguous tile.
@@ -786,118 +782,6 @@ __device__ __forceinline__ void gemm_tile_direct(const GemmArgs &a, float *smem,
     }
 }
 
-// Waits until at most N of this wavefront's vector-memory loads are still in
-// flight (they complete in issue order, so every earlier one has landed), then
-// meets the workgroup barrier.  __syncthreads() would wait for all of them.
-template <int N>
-__device__ __forceinline__ void wait_loads_barrier()
-{
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-
-// Waits for this wavefront's loads of the stage about to be read, leaving the
-// loads of the `later` stages issued after it in flight (0 <= later <= NS - 2),
-// then the barrier: every wavefront's loads of that stage have landed.
-template <class Gm, int P>
-__device__ __forceinline__ void wait_stage(int later)
-{
-    if constexpr (Gm::NS >= 4) {
-        if (later >= 2) {
-            wait_loads_barrier<2 * P>();
-            return;
-        }
-    }
-    if (later >= 1)
-        wait_loads_barrier<P>();
-    else
-        wait_loads_barrier<0>();
-}
-
-// Direct-staged k-loop with an NS-stage ring of LDS buffers (NS >= 3): stage
-// t+NS-1 is issued at the top of iteration t into the buffer that stage t-1
-// used (every wavefront finished reading it before the barrier that ended
-// iteration t-1), so a load has NS-1 iterations of MFMAs to land instead of
-// one.  Otherwise as gemm_tile_direct: a partial last stage goes first,
-// through registers and the ring's last buffer, and one barrier per stage.
-template <class Gm, bool TRANS_B, bool EDGE>
-__device__ __forceinline__ void gemm_tile_direct_ring(const GemmArgs &a, float *smem, int m0, int n0)
-{
-    constexpr int G = Gm::G, NS = Gm::NS;
-    const Role<Gm> ro;
-    const int sl_off = ro.slice * Gm::SLICE;
-    OldC<Gm> oc;
-    const bool pre = OldC<Gm>::ON && a.beta != 0.0f && ro.slice == 0;
-    if (pre)
-        oc.template load<!EDGE>(a, m0, n0, ro);
-
-    f32x16 acc[Gm::FM][Gm::FN];
-    zero_acc<Gm>(acc);
-
-    const int nf = a.K / Gm::KT;  // full stages
-    Frags<Gm, TRANS_B> f[2];
-
-    DirectStage<Gm, TRANS_B> ds;
-    constexpr int P = DirectStage<Gm, TRANS_B>::A_N + DirectStage<Gm, TRANS_B>::B_N;  // loads per stage
-    ds.template init<EDGE>(a, m0, n0);
-#pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
-        if (s < nf) {
-            poison_lds(smem + s * Gm::STAGE, Gm::STAGE * 4);
-            ds.issue(s, smem + s * Gm::STAGE);
-        }
-
-    if (nf * Gm::KT < a.K) {
-        float *tb = smem + (NS - 1) * Gm::STAGE;
-        RegStage<Gm, TRANS_B> st;
-        st.init(a, m0, n0);
-        st.template load<true>(a, m0, n0, nf);
-        poison_lds(tb, Gm::STAGE * 4);
-        st.store(tb);
-        __syncthreads();
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            read_frags<Gm, TRANS_B>(f[0], tb + sl_off, tb + sl_off + Gm::A_SZ, g, ro.wm, ro.wn, ro.l32, ro.hi);
-            mfma_group<Gm, TRANS_B>(acc, f[0]);
-        }
-    }
-    if (nf > 0) {
-        // stage 0 has landed (and the tail's buffer is free again)
-        wait_stage<Gm, P>(min(nf, NS - 1) - 1);
-        read_frags<Gm, TRANS_B>(f[0], smem + sl_off, smem + sl_off + Gm::A_SZ, 0, ro.wm, ro.wn, ro.l32, ro.hi);
-        int cur = 0;  // buffer of stage t
-        for (int t = 0; t < nf; ++t) {
-            const float *As = smem + cur * Gm::STAGE + sl_off;
-            const float *Bs = As + Gm::A_SZ;
-            const int nxt = cur + 1 == NS ? 0 : cur + 1;
-            if (t + NS - 1 < nf) {
-                const int fr = cur == 0 ? NS - 1 : cur - 1;  // the buffer stage t-1 used
-                poison_lds(smem + fr * Gm::STAGE, Gm::STAGE * 4);
-                ds.issue(t + NS - 1, smem + fr * Gm::STAGE);
-                pin_order();
-            }
-            const float *Sn = smem + nxt * Gm::STAGE + sl_off;
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                group_step<Gm, TRANS_B>(acc, f[g & 1], [&] {
-                    if (g + 1 < G) {
-                        read_frags<Gm, TRANS_B>(f[(g + 1) & 1], As, Bs, g + 1, ro.wm, ro.wn, ro.l32, ro.hi);
-                    } else if (t + 1 < nf) {
-                        wait_stage<Gm, P>(min(nf - t - 2, NS - 2));
-                        read_frags<Gm, TRANS_B>(f[G & 1], Sn, Sn + Gm::A_SZ, 0, ro.wm, ro.wn, ro.l32, ro.hi);
-                    }
-                });
-            }
-            cur = nxt;
-        }
-    }
-    if (reduce_slices<Gm>(acc, smem, ro)) {
-        if (pre)
-            oc.template epilogue<!EDGE>(a, acc, m0, n0, ro);
-        else
-            epilogue<Gm, TRANS_B, !EDGE>(a, acc, m0, n0, ro);
-    }
-}
-
 // One output tile at (m0, n0): direct staging for interior tiles (and edge
 // tiles whose clamped addresses are exact: op(B) = B^T, or op(B) = B with N a
 // multiple of 4, so that a 4-column chunk is wholly inside or outside),
@@ -910,17 +794,10 @@ __device__ __forceinline__ void mfma_tile(const GemmArgs &a, float *smem, int m0
     const bool full = m0 + GD::BM <= a.M && n0 + GD::BN <= a.N;
     if (a.flags & GEMM_FLAG_DIRECT) {
         if (full || TRANS_B || (a.N & 3) == 0) {
-            if constexpr (GD::NS > 2) {
-                if (full)
-                    gemm_tile_direct_ring<GD, TRANS_B, false>(a, smem, m0, n0);
-                else
-                    gemm_tile_direct_ring<GD, TRANS_B, true>(a, smem, m0, n0);
-            } else {
-                if (full)
-                    gemm_tile_direct<GD, TRANS_B, false>(a, smem, m0, n0);
-                else
-                    gemm_tile_direct<GD, TRANS_B, true>(a, smem, m0, n0);
-            }
+            if (full)
+                gemm_tile_direct<GD, TRANS_B, false>(a, smem, m0, n0);
+            else
+                gemm_tile_direct<GD, TRANS_B, true>(a, smem, m0, n0);
             return;
         }
     }

@@ -27,11 +27,7 @@ import pytest
 
 
 def swz(r, cpr):
-    if cpr == 4:
-        return ((r >> 1) ^ (r >> 2)) & 3
-    if cpr == 8:
-        return (r ^ (r >> 3)) & 7
-    return (r ^ (r >> 4)) & 15
+    return ((r >> 1) ^ (r >> 2)) & 3 if cpr == 4 else (r ^ (r >> 3)) & 7
 
 
 def stage_and_check(BM, BN, BK, NW, KS, trans_b, edge, M, N, K, lda, ldb, m0, n0, kt, write_swz=swz):
