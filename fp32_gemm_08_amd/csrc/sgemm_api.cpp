@@ -9,6 +9,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <limits>
 #include <mutex>
@@ -339,6 +340,40 @@ int arch_status(const char *arch)
         return SGEMM_ERR_UNSUPPORTED_ARCH;
     const size_t n = std::strcspn(arch, ":");
     return (n == 6 && std::strncmp(arch, "gfx950", 6) == 0) ? SGEMM_OK : SGEMM_ERR_UNSUPPORTED_ARCH;
+}
+
+// SGEMM_F32_ALGO, read once per process, replaces the shape-based choice of
+// the public AUTO entry points (sgemm_f32, and sgemm_f32_algo / _plan with
+// SGEMM_ALGO_AUTO) by a fixed algorithm: a name of the sgemm_algo list in
+// lower case without the prefix ("naive", "lds_tiled", "mfma_64", ...) or its
+// number.  Unset or empty: no override.  Anything else: those calls return
+// SGEMM_ERR_INVALID_VALUE, so a mistyped override fails loudly.  The calls
+// with a workspace and the mixed-precision calls keep their own choices.
+constexpr int kNoOverride = -1, kBadOverride = -2;
+
+int parse_algo_override(const char *v)
+{
+    if (v == nullptr || *v == '\0')
+        return kNoOverride;
+    static const char *const names[] = {"auto", "naive", "lds_tiled", "regblock", "mfma", "lds_tiled_nopad",
+                                        "naive_wg", "mfma_256", "mfma_128", "mfma_64", "mfma_32"};
+    const int n = (int)(sizeof(names) / sizeof(names[0]));
+    for (int i = 0; i < n; ++i)
+        if (std::strcmp(v, names[i]) == 0)
+            return i == SGEMM_ALGO_AUTO ? kNoOverride : i;
+    char *end = nullptr;
+    const long x = std::strtol(v, &end, 10);
+    if (end != v && *end == '\0' && x >= 0 && x < n)
+        return x == SGEMM_ALGO_AUTO ? kNoOverride : (int)x;
+    return kBadOverride;
+}
+
+int auto_algo(int algo)
+{
+    if (algo != SGEMM_ALGO_AUTO)
+        return algo;
+    static const int over = parse_algo_override(std::getenv("SGEMM_F32_ALGO"));
+    return over == kNoOverride ? SGEMM_ALGO_AUTO : over;  // kBadOverride fails validation
 }
 
 // 0 = unknown, 1 = gfx950, 2 = other architecture.
@@ -969,20 +1004,22 @@ extern "C" {
 int sgemm_f32(int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda, const float *B,
               int64_t ldb, int transB, float beta, float *C, int64_t ldc, void *stream)
 {
-    return sgemm::run(SGEMM_ALGO_AUTO, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, stream);
+    return sgemm::run(sgemm::auto_algo(SGEMM_ALGO_AUTO), M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc,
+                      stream);
 }
 
 int sgemm_f32_algo(int algo, int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
                    const float *B, int64_t ldb, int transB, float beta, float *C, int64_t ldc, void *stream)
 {
-    return sgemm::run(algo, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, stream);
+    return sgemm::run(sgemm::auto_algo(algo), M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc, stream);
 }
 
 int sgemm_f32_plan(int algo, int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
                    const float *B, int64_t ldb, int transB, float beta, const float *C, int64_t ldc,
                    int *kernel_id, int64_t *tiles_m, int64_t *tiles_n, char *name, int name_len)
 {
-    const sgemm::Plan p = sgemm::make_plan(algo, M, N, K, alpha, A, lda, B, ldb, transB, beta, C, ldc);
+    const sgemm::Plan p = sgemm::make_plan(sgemm::auto_algo(algo), M, N, K, alpha, A, lda, B, ldb, transB, beta, C,
+                                           ldc);
     if (kernel_id)
         *kernel_id = p.kid;
     if (tiles_m)

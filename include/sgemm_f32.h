@@ -125,6 +125,17 @@ typedef enum {
 } sgemm_algo;
 
 /*
+ * Environment: SGEMM_F32_ALGO, read once per process, forces the algorithm of
+ * the AUTO entry points (sgemm_f32, and sgemm_f32_algo / sgemm_f32_plan with
+ * SGEMM_ALGO_AUTO): the lower-case name of an sgemm_algo value without its
+ * prefix ("naive", "lds_tiled", "regblock", "mfma", "lds_tiled_nopad",
+ * "naive_wg", "mfma_256", "mfma_128", "mfma_64", "mfma_32"; "auto" or an
+ * empty value: no override) or its number.  Any other value makes those calls
+ * return SGEMM_ERR_INVALID_VALUE.  The workspace, k-split, stream-K and
+ * mixed-precision calls are not affected.
+ */
+
+/*
  * C <- alpha*A*op(B) + beta*C with the AUTO algorithm.
  * Arguments as described above; `stream` is a hipStream_t (NULL: null stream).
  * Returns an sgemm_status.

@@ -230,3 +230,38 @@ def test_wave_per_output_has_no_grid_limit():
 def test_mfma_probe_rejects_bad_arguments(wg, trips, sink, clocks, status):
     # every case is refused on the host, before any HIP call
     assert lib.sgemm_f32_mfma_probe(wg, trips, sink, clocks, 0) == status
+
+
+_OVERRIDE_CHILD = r"""
+import json, sys
+sys.path.insert(0, sys.argv[1])
+import fp32_gemm_08_amd as lib
+PA, PB, PC = 1 << 32, 1 << 40, 1 << 44
+def plan(algo, M=1000, N=1017, K=999):
+    return lib.sgemm_f32_plan(algo, M, N, K, 1.0, PA, K, PB, N, 0, 0.0, PC, N)[:2]
+print(json.dumps([plan(0), plan(4), plan(1), lib.sgemm_f32_ws_plan(512, 512, 8192, 0)[:2], lib.sgemm_f32_lowp_plan(
+    2, 4096, 4096, 4096, 1.0, PA, 4096, PB, 4096, 0, 0.0, PC, 4096)[:2]]))
+"""
+
+
+@pytest.mark.parametrize("value,auto", [("", (OK, KID_S2)), ("auto", (OK, KID_S2)), ("regblock", (OK, KID_REG)),
+                                        ("mfma_256", (OK, KID_L)), ("9", (OK, KID_S)), ("mfma_32", (OK, KID_T)),
+                                        ("naive_wg", (OK, KID_NAIVE_WG)), ("fastest", (INVALID, KID_NONE)),
+                                        ("11", (INVALID, KID_NONE)), ("MFMA", (INVALID, KID_NONE))])
+def test_algo_environment_override(value, auto):
+    """SGEMM_F32_ALGO replaces AUTO's choice in sgemm_f32 / sgemm_f32_algo(AUTO) / the plan, fails loudly
+    when it names no algorithm, and leaves explicit algorithms and the workspace and mixed-precision
+    plans alone.  Host-only planning queries; each value in its own process (it is read once)."""
+    import subprocess
+    import sys
+    env = dict(os.environ, SGEMM_F32_ALGO=value)
+    r = subprocess.run([sys.executable, "-c", _OVERRIDE_CHILD, ROOT], env=env, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr[-2000:]
+    import json
+    got = [tuple(x) for x in json.loads(r.stdout.strip().splitlines()[-1])]
+    assert got[0] == auto
+    assert got[1] == (OK, KID_S2)                   # SGEMM_ALGO_MFMA is explicit: never overridden
+    assert got[2] == (OK, KID_NAIVE)
+    assert got[3] == (OK, 1)                        # sgemm_f32_ws still splits 512 x 512 x 8192
+    assert got[4] == (OK, 61)                       # the bf16 kernel of sgemm_f32_lowp
