@@ -365,10 +365,11 @@ int sgemm_f32_lowp_2pass_plan(int precision, int tile, int64_t M, int64_t N, int
  * use (`splits` = 0: what sgemm_f32_ws chooses -- no split while the 64 x 64
  * tile grid has at least 128 tiles; otherwise floor(512 / tiles) splits, two
  * workgroups per CU, when each gets at least 1024 of k, else the most splits
- * that keep one workgroup per CU with at least 128 of k each, at most 64;
- * otherwise the requested count,
- * clipped to the non-empty splits), the MFMA kernel id of the partial pass, and
- * the workspace bytes it needs.  *splits_used = 1 and *workspace_bytes = 0 when
+ * that keep one workgroup per CU with at least 128 of k each, at most 64; and
+ * no split when that comes to 4 or fewer, where the plain call's 32 x 32 tile
+ * already runs as many workgroups; otherwise the requested count, clipped to
+ * the non-empty splits), the MFMA kernel id of the partial pass, and the
+ * workspace bytes it needs.  *splits_used = 1 and *workspace_bytes = 0 when
  * the call runs unsplit (shapes that already fill the chip, K too short to
  * split, product-free cases).  Returns SGEMM_ERR_INVALID_VALUE for invalid
  * dimensions, transB or a split count outside 0..64.  Output pointers may be NULL.
