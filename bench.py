@@ -725,6 +725,9 @@ def main():
     ap.add_argument("--config", default="c4_4096",
                     help="workload name (GEMM: c1_128 ... c5_tall, k_* long-k, s_* stream-K; transpose: t_4096 ...)")
     ap.add_argument("--algo", default="auto")
+    ap.add_argument("--row-share", type=int, default=1, metavar="P",
+                    help="GEMM: run the first of P equal row shares of the workload (A and C rows, all of B): "
+                         "one GPU's part when the output is split by rows over P GPUs")
     ap.add_argument("--precision", choices=("fp32", "fp16", "bf16"), default="fp32",
                     help="GEMM: fp16/bf16 run sgemm_f32_lowp (operands rounded to that format, FP32 sums), "
                          "reported against the dense fp16/bf16 matrix-core peak")
@@ -788,15 +791,17 @@ def main():
         return
 
     import fp32_gemm_08_amd as lib
-    from fp32_gemm_08_amd.inputs import CONFIGS, make_config
+    from fp32_gemm_08_amd.inputs import make_config, make_row_share
 
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda", 0)
     log(f"bench: config={args.config} algo={args.algo} steps={args.steps} "
-        f"warmup={args.warmup if args.warmup is not None else 'auto'}")
-    case = make_config(args.config)
+        f"warmup={args.warmup if args.warmup is not None else 'auto'} row_share={args.row_share}")
+    share = args.row_share > 1
+    case = make_row_share(args.config, args.row_share, 0) if share else make_config(args.config)
+    label = f"{args.config}, row share 1 of {args.row_share}" if share else args.config
     M, N, K = case.M, case.N, case.K
     dA = torch.from_numpy(case.A).to(dev)
     dB = torch.from_numpy(case.B).to(dev)
@@ -903,8 +908,8 @@ def main():
     D_host = dC.cpu().numpy()
 
     out = {
-        "metric": (METRIC if args.config == "c4_4096" else f"FP32 GEMM TFLOP/s ({args.config}), 1 GPU")
-        if not lowp else f"mixed-precision GEMM TFLOP/s ({args.precision} operands, FP32 sums; {args.config}), 1 GPU",
+        "metric": (METRIC if args.config == "c4_4096" and not share else f"FP32 GEMM TFLOP/s ({label}), 1 GPU")
+        if not lowp else f"mixed-precision GEMM TFLOP/s ({args.precision} operands, FP32 sums; {label}), 1 GPU",
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -920,8 +925,10 @@ def main():
         "config": {
             "workload": f"sgemm {M}x{N}x{K} row-major, D=alpha*A*{'B^T' if case.trans_b else 'B'}+beta*C, "
                         f"alpha={case.alpha:g}, beta={case.beta:g}, {case.meta['dist']} inputs, "
-                        f"seed {case.meta['seed']}",
-            "name": args.config, "M": M, "N": N, "K": K, "trans_b": case.trans_b,
+                        f"seed {case.meta['seed']}"
+                        + (f"; rows 0..{M - 1} of the {args.config} workload (one of {args.row_share} row shares, "
+                           f"all of B)" if share else ""),
+            "name": label, "M": M, "N": N, "K": K, "trans_b": case.trans_b,
             "lda": case.lda, "ldb": case.ldb, "ldc": case.ldc,
             "algo": args.algo, "kernel": kname, "workgroups": tm * tn,
             "k_splits": splits, "workspace_bytes": ws_bytes,
@@ -952,7 +959,7 @@ def main():
         "device": device_record(torch, dev, clock),
         "cpu_baseline": None,
     }
-    traffic = read_traffic() if (args.config == "c4_4096" and kid == 40) else None
+    traffic = read_traffic() if (args.config == "c4_4096" and not share and kid == 40) else None
     out["roofline"]["traffic"] = traffic
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on a sample of rows for ~{args.cpu_seconds:.0f} s")

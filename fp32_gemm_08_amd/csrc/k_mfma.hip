@@ -76,12 +76,9 @@ template <> __device__ __forceinline__ void vset<1>(float &v, int, float x) { v 
 template <> __device__ __forceinline__ void vset<2>(f32x2 &v, int i, float x) { v[i] = x; }
 template <> __device__ __forceinline__ void vset<4>(f32x4 &v, int i, float x) { v[i] = x; }
 
-// Wavefront index within the workgroup, as a wave-uniform (scalar) value: the
-// LDS block addresses derived from it then stay in scalar registers, and M0 for
-// the direct loads is set without a per-load vector-to-scalar move (measured ~1%).
-// threadIdx.x; OPQ: behind an empty asm, so that each tile's set-up derives
-// its per-lane offsets afresh.  The stream-K kernel runs the tile code in a
-// loop and would otherwise hoist them out of it and hold them (spilled)
+// threadIdx.x; with OPQ, behind an empty asm, so that each tile's set-up
+// derives its per-lane offsets afresh.  The stream-K kernel runs the tile code
+// in a loop and would otherwise hoist them out of it and hold them (spilled)
 // across the loop; the plain kernels keep the direct read (measured 0.6%
 // faster at 4096^3).
 template <bool OPQ>
@@ -93,6 +90,9 @@ __device__ __forceinline__ int work_item()
     return t;
 }
 
+// Wavefront index within the workgroup, as a wave-uniform (scalar) value: the
+// LDS block addresses derived from it then stay in scalar registers, and M0 for
+// the direct loads is set without a per-load vector-to-scalar move (measured ~1%).
 template <bool OPQ>
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(work_item<OPQ>() >> 6); }
 

@@ -129,6 +129,21 @@ def make_config(name: str, **overrides) -> Case:
     return c
 
 
+def make_row_share(name: str, parts: int, index: int = 0) -> Case:
+    """Rows [index*M/parts, (index+1)*M/parts) of workload `name` (A and C
+    rows; all of B): what one of `parts` GPUs computes when the output is split
+    by rows and B is replicated.  Output tiles are independent ("CUDA矩阵乘法
+    性能优化实战", section 1.1), so no share needs another's rows."""
+    base = make_config(name)
+    if parts < 1 or base.M % parts != 0 or not 0 <= index < parts:
+        raise ValueError(f"{name}: {base.M} rows do not split into {parts} equal shares (index {index})")
+    r0, r1 = index * base.M // parts, (index + 1) * base.M // parts
+    C = None if base.C is None else base.C[r0:r1].copy()
+    meta = dict(base.meta, row_share=(parts, index))
+    return Case(r1 - r0, base.N, base.K, base.trans_b, base.alpha, base.beta, base.A[r0:r1].copy(), base.B, C,
+                base.ldc, meta)
+
+
 def flops(M, N, K) -> float:
     """2*M*N*K, the FLOP convention every throughput figure uses."""
     return 2.0 * M * N * K

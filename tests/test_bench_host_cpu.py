@@ -1,4 +1,5 @@
-"""Host-side behaviour of bench.py that needs no GPU: the one-GPU guard."""
+"""Host-side behaviour of bench.py that needs no GPU: the one-GPU guard, the
+warm-up rule and the row shares it can time."""
 import os
 import subprocess
 import sys
@@ -47,3 +48,25 @@ def test_warm_up_runs_the_count_and_the_minimum_time():
     calls.clear()
     n = bench.warm_up(_FakeTorch(), lambda i: calls.append(i), 300)
     assert n == len(calls) >= 300
+
+
+def test_row_share_is_the_matching_rows_of_the_workload():
+    import numpy as np
+    import pytest
+
+    from fp32_gemm_08_amd.inputs import make_config, make_row_share
+
+    for name, parts in (("c5_512", 4), ("c3_ragged_bt", 8)):
+        whole = make_config(name)
+        for index in (0, parts - 1):
+            s = make_row_share(name, parts, index)
+            r0 = index * whole.M // parts
+            assert s.M == whole.M // parts and (s.N, s.K, s.trans_b) == (whole.N, whole.K, whole.trans_b)
+            assert np.array_equal(s.A, whole.A[r0:r0 + s.M]) and np.array_equal(s.B, whole.B)
+            assert (s.C is None) == (whole.C is None)
+            if s.C is not None:
+                assert np.array_equal(s.C, whole.C[r0:r0 + s.M])
+    with pytest.raises(ValueError):
+        make_row_share("c3_ragged_bt", 3)       # 1000 rows do not split in 3
+    with pytest.raises(ValueError):
+        make_row_share("c5_512", 4, 4)

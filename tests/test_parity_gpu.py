@@ -381,6 +381,36 @@ def test_deterministic_reruns_large(name):
             assert torch.equal(first.view(torch.int32), C.view(torch.int32)), f"call {i} differs"
 
 
+_whole_256 = {}
+
+
+@pytest.mark.parametrize("name,parts,index", [("c4_4096", 8, 0), ("c4_4096", 8, 5), ("c4_4096", 8, 7),
+                                              ("c5_tall", 8, 3)])
+def test_row_share_of_a_workload(oracle_lib, name, parts, index):
+    """One GPU's part of the row split (A and C rows, all of B): AUTO meets the
+    oracle on those rows of the whole workload, and the 256 x 256 kernel gives
+    bit for bit the rows the whole product gives (the same tiles, each with
+    the same k order), so the split needs no exchange and changes no bit."""
+    from fp32_gemm_08_amd.inputs import make_row_share
+
+    whole = cached_config(name)
+    share = make_row_share(name, parts, index)
+    r0 = index * share.M
+    st, Dg = run_case(share, "auto")
+    assert st == 0, lib.sgemm_f32_status_string(st)
+    D, S = cached_oracle(oracle_lib, name)
+    assert_parity(Dg[:, :share.N], D[r0:r0 + share.M], S[r0:r0 + share.M], share.K,
+                  f"{name} rows {r0}..{r0 + share.M - 1} (share {index} of {parts})")
+    if name not in _whole_256:
+        st, Dw = run_case(whole, "mfma_256", guard=False)
+        assert st == 0
+        _whole_256[name] = Dw
+    st, Ds = run_case(share, "mfma_256", guard=False)
+    assert st == 0
+    assert np.array_equal(Ds[:, :share.N].view(np.uint32),
+                          _whole_256[name][r0:r0 + share.M, :share.N].view(np.uint32))
+
+
 def test_transposed_storage_agrees(oracle_lib):
     """op(B) = B^T on a materialised B^T agrees with op(B) = B (both within the bound)."""
     case0 = make_case(300, 280, 260, dist="normal", seed=8)
