@@ -36,8 +36,9 @@
 //     exact): global_load_lds_dwordx4 writes each 1 KB LDS block straight from
 //     memory, no registers involved, 16 bytes per lane from any float-aligned
 //     address (leading dimensions need not be multiples of 4).  Tile t+1 is
-//     issued at the start of iteration t into the free buffer and must land
-//     before the iteration's barrier.  A partial last k-tile (K % BK != 0) is
+//     issued during iteration t into the free buffer (at its start, or by half
+//     of the wavefronts of the 8-wavefront tiles one k-group later) and must
+//     land before the iteration's barrier.  A partial last k-tile (K % BK != 0) is
 //     staged through registers with zero fill and multiplied first.
 //   * registers (edge tiles of op(B) = B with N % 4 != 0, and leading
 //     dimensions too large for 32-bit offsets): masked loads into registers,
@@ -704,6 +705,23 @@ __device__ __forceinline__ void gemm_tile_regs(const GemmArgs &a, float *smem, i
     }
 }
 
+// Where the wavefronts of an 8-wavefront workgroup issue the next stage's
+// direct loads.  Issued by all eight at the top of the stage, they queue 64
+// wavefront instructions at the CU's address unit at once, and each wavefront
+// waits behind its own before its next MFMA.  So half the wavefronts (those
+// with wave & MASK set) issue theirs after the first MFMA step of k-group
+// GROUP instead, while the others multiply; the loads still land long before
+// the stage's closing barrier.  The masks are the fastest measured on MI355X
+// per tile, among splits by wave bit 0, 1 or 2 at k-group 1 or 2 (4096^3
+// 144.4 -> 146.5 TFLOP/s, 8192^3 145.5 -> 147.6; 128 x 128 tile at 6144^3
+// 138.3 -> 140.3; 64 x 64 tile at 1024^3 105.8 -> 109.4); MASK 0: no split.
+template <class Gm>
+struct IssueSplit {
+    static constexpr int MASK = Gm::NW != 8 ? 0 : Gm::BM == 64 ? 4 : 1;
+    static constexpr int GROUP = 1;
+    static_assert(MASK == 0 || GROUP < Gm::G - 1, "the late loads must come before the closing barrier's group");
+};
+
 // Direct-staged k-loop (interior tiles, and edge tiles whose clamped
 // addresses are exact).
 template <class Gm, bool TRANS_B, bool EDGE>
@@ -726,6 +744,8 @@ __device__ __forceinline__ void gemm_tile_direct(const GemmArgs &a, float *smem,
 
     DirectStage<Gm, TRANS_B> ds;
     ds.template init<EDGE>(a, m0, n0);
+    typedef IssueSplit<Gm> IS;
+    const bool late = IS::MASK != 0 && (wave_id<Gm::OPQ>() & IS::MASK) != 0;  // wave-uniform
     if (nf > 0) {
         poison_lds(buf0, Gm::STAGE * 4);
         ds.issue(0, buf0);
@@ -753,16 +773,20 @@ __device__ __forceinline__ void gemm_tile_direct(const GemmArgs &a, float *smem,
             const float *As = ((t & 1) ? buf1 : buf0) + sl_off;
             const float *Bs = As + Gm::A_SZ;
             float *Sn = (t & 1) ? buf0 : buf1;
-            // All loads of stage t+1 go out first: measured against spreading them
-            // over the MFMA steps, issuing them together at the top is faster.
+            // A wavefront's loads of stage t+1 go out together (measured against
+            // spreading them over its MFMA steps, that is faster): at the top of
+            // the stage, or for the late half at k-group IssueSplit::GROUP.
             if (t + 1 < nf) {
                 poison_lds(Sn, Gm::STAGE * 4);
-                ds.issue(t + 1, Sn);
+                if (!late)
+                    ds.issue(t + 1, Sn);
                 pin_order();
             }
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 group_step<Gm, TRANS_B>(acc, f[g & 1], [&] {
+                    if (late && g == IS::GROUP && t + 1 < nf)
+                        ds.issue(t + 1, Sn);
                     if (g + 1 < G) {
                         read_frags<Gm, TRANS_B>(f[(g + 1) & 1], As, Bs, g + 1, ro.wm, ro.wn, ro.l32, ro.hi);
                     } else if (t + 1 < nf) {
