@@ -168,7 +168,13 @@ struct Geo {
     static constexpr int A_BLK_W = KS * A_BLK / NW;    // direct path: blocks per wavefront
     static constexpr int B_BLK_W = KS * B_BLK / NW;
     static constexpr int ACC = FM * FN * 16;           // accumulators per lane
-    static constexpr int RED = (KS - 1) * NWO * ACC * 64;  // floats for the k-slice reduction
+    static constexpr int UNITS = 2 * FM;               // output units per wavefront tile (8 accumulator rows)
+    // k-slices that finish units: spread over up to four slices (measured on
+    // MI355X: the 32 x 32 tile's four slices, 512^3 with beta = 1 47.5 -> 49.6
+    // TFLOP/s); with two slices, slice 0 finishing the whole tile measured
+    // faster (2048^3: 134.2 against 121.8 for the spread finish)
+    static constexpr int FIN = KS >= 4 ? (KS < UNITS ? KS : UNITS) : 1;
+    static constexpr int RED = KS == 1 ? 0 : (FIN == 1 ? KS - 1 : KS) * NWO * ACC * 64;  // floats for the k-slice sums
     static constexpr int SMEM = (2 * STAGE > RED) ? 2 * STAGE : RED;
     static_assert(WM % 32 == 0 && WN % 32 == 0, "tile shape");
     static_assert(BK == 16 || BK == 32, "the chunk permutation covers 4 or 8 chunks per row");
@@ -447,9 +453,10 @@ struct DirectStage {
     }
 };
 
-// KS > 1: k-slices 1..KS-1 leave their accumulators in LDS and slice 0 adds them
-// in slice order (a fixed order, so results are reproducible).  Called by every
-// wavefront; returns true for the wavefronts that write the output.
+// One finishing slice (FIN == 1) and KS > 1: k-slices 1..KS-1 leave their
+// accumulators in LDS and slice 0 adds them in slice order (a fixed order, so
+// results are reproducible).  Called by every wavefront; returns true for the
+// wavefronts that write the output.
 template <class Gm>
 __device__ __forceinline__ bool reduce_slices(f32x16 (&acc)[Gm::FM][Gm::FN], float *smem, const Role<Gm> &ro)
 {
@@ -586,15 +593,20 @@ struct OldC {
     static constexpr bool ON = Gm::FM * Gm::FN == 1;
     float v[ON ? 16 : 1];
 
+    // One finishing slice: all 16 values of the block; more: the 8 of the unit
+    // this wavefront's k-slice finishes (unit = slice, half h = slice; see Finish).
     template <bool FULL>
     __device__ __forceinline__ void load(const GemmArgs &a, int m0, int n0, const Role<Gm> &ro)
     {
         if constexpr (ON) {
             const int col = n0 + ro.wn * Gm::WN + ro.l32;
+            constexpr int NV = Gm::FIN == 1 ? 16 : 8;
+            const int r0 = Gm::FIN == 1 ? 0 : 8 * ro.slice;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
+            for (int i = 0; i < NV; ++i) {
+                const int r = r0 + i;
                 const int row = m0 + ro.wm * Gm::WM + 8 * (r / 4) + 4 * ro.hi + (r % 4);
-                v[r] = (FULL || (row < a.M && col < a.N)) ? a.C[(int64_t)row * a.ldc + col] : 0.0f;
+                v[i] = (FULL || (row < a.M && col < a.N)) ? a.C[(int64_t)row * a.ldc + col] : 0.0f;
             }
         }
     }
@@ -614,6 +626,168 @@ struct OldC {
         }
     }
 };
+
+// FIN > 1: the output of a wavefront tile is finished in units of 8
+// accumulator rows (unit u = 2*fm + h: registers 8h .. 8h+7 of each of the FN
+// blocks in block row fm), unit u by k-slice u % FIN, so that adding the
+// slices' partial sums and storing the result are spread over up to FIN
+// slices instead of falling to one.  Every slice leaves all its partial sums
+// in LDS; a finishing slice reads back the KS partials of each of its units
+// and adds them in slice order, as (p0 + p1) + p2 ..., so the result does not
+// depend on which slice finishes a unit and repeats bit for bit.  The units
+// and rows are picked with addresses, never with register indices, so the
+// accumulators stay in fixed registers.
+template <class Gm>
+struct Finish {
+    static constexpr int PER = Gm::UNITS / Gm::FIN;  // units per finishing slice
+    f32x4 v[PER][Gm::FN][2];                        // unit k: registers 8h+4q .. 8h+4q+3 of block fn in v[k][fn][q]
+};
+
+// Returns true for the wavefronts that finish units.
+template <class Gm>
+__device__ __forceinline__ bool reduce_units(const f32x16 (&acc)[Gm::FM][Gm::FN], float *smem, const Role<Gm> &ro,
+                                             Finish<Gm> &out)
+{
+    // Region of (slice, wavefront): the lane's ACC accumulators as ACC/4
+    // float4s, float4 j of lane L at j*64 + L (128-bit LDS accesses).
+    constexpr int Q = Gm::ACC / 4;
+    f32x4 *red = reinterpret_cast<f32x4 *>(smem);
+    __syncthreads();  // every wavefront is done with the stage buffers
+    poison_lds(smem, Gm::RED * 4);
+    f32x4 *mine = red + (ro.slice * Gm::NWO + ro.wo) * Q * 64 + ro.lane;
+#pragma unroll
+    for (int fm = 0; fm < Gm::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < Gm::FN; ++fn)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x16 &x = acc[fm][fn];
+                mine[((fm * Gm::FN + fn) * 4 + q) * 64] = f32x4{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
+            }
+    __syncthreads();
+    if (ro.slice >= Gm::FIN)
+        return false;
+    const f32x4 *part = red + ro.wo * Q * 64 + ro.lane;
+#pragma unroll
+    for (int k = 0; k < Finish<Gm>::PER; ++k) {
+        const int u = k * Gm::FIN + ro.slice, fm = u >> 1, h = u & 1;
+#pragma unroll
+        for (int fn = 0; fn < Gm::FN; ++fn)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int at = ((fm * Gm::FN + fn) * 4 + 2 * h + q) * 64;
+                f32x4 v = part[at];
+#pragma unroll
+                for (int sl = 1; sl < Gm::KS; ++sl)
+                    v += part[sl * Gm::NWO * Q * 64 + at];
+                out.v[k][fn][q] = v;
+            }
+    }
+    return true;
+}
+
+// The finished units to C.  MODE 0: beta == 0, C not read; 1: the 8 rows' old
+// values of a unit are loaded before the first of them is stored (as in
+// epilogue_rows); 2: old values loaded before the k-loop (OldC).
+template <class Gm, bool TRANS_B, bool FULL, int MODE>
+__device__ __forceinline__ void store_units(const GemmArgs &a, const Finish<Gm> &fin, const OldC<Gm> &oc, int m0,
+                                            int n0, const Role<Gm> &ro)
+{
+    typedef typename vec_of<Gm::IL>::type bvec;
+    constexpr int IL = Gm::IL;
+    const int l32 = ro.l32, hi = ro.hi;
+    const uintptr_t cbase = reinterpret_cast<uintptr_t>(a.C);
+    const bool cvec = IL > 1 && (cbase % (4 * IL)) == 0 && (a.ldc % IL) == 0;
+#pragma unroll
+    for (int k = 0; k < Finish<Gm>::PER; ++k) {
+        const int u = k * Gm::FIN + ro.slice, fm = u >> 1, h = u & 1;
+        const int row0 = m0 + ro.wm * Gm::WM + 32 * fm + 16 * h + 4 * hi;  // rows row0 + 8*(i/4) + i%4
+        float old[8][Gm::FN];
+        if constexpr (MODE == 1) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int row = row0 + 8 * (i / 4) + (i % 4);
+                if (!FULL && row >= a.M)
+                    continue;
+                const float *crow = a.C + (int64_t)row * a.ldc;
+#pragma unroll
+                for (int gr = 0; gr < Gm::NG; ++gr) {
+                    const int col = n0 + ro.wn * Gm::WN + gr * 32 * IL + IL * l32;
+                    if (IL > 1 && cvec && (FULL || col + IL <= a.N)) {
+                        const bvec o = *reinterpret_cast<const bvec *>(crow + col);
+#pragma unroll
+                        for (int b = 0; b < IL; ++b)
+                            old[i][gr * IL + b] = vget<IL>(o, b);
+                    } else {
+#pragma unroll
+                        for (int b = 0; b < IL; ++b)
+                            old[i][gr * IL + b] = (FULL || col + b < a.N) ? crow[col + b] : 0.0f;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = row0 + 8 * (i / 4) + (i % 4);
+            if (!FULL && row >= a.M)
+                continue;
+            float *crow = a.C + (int64_t)row * a.ldc;
+#pragma unroll
+            for (int gr = 0; gr < Gm::NG; ++gr) {
+                const int col = n0 + ro.wn * Gm::WN + gr * 32 * IL + IL * l32;
+                float v[IL];
+#pragma unroll
+                for (int b = 0; b < IL; ++b) {
+                    const float x = fin.v[k][gr * IL + b][i / 4][i % 4];
+                    if constexpr (MODE == 0)
+                        v[b] = a.alpha * x;
+                    else if constexpr (MODE == 1)
+                        v[b] = fmaf(a.alpha, x, a.beta * old[i][gr * IL + b]);
+                    else
+                        v[b] = fmaf(a.alpha, x, a.beta * oc.v[i]);
+                }
+                if (IL > 1 && cvec && (FULL || col + IL <= a.N)) {
+                    bvec o;
+#pragma unroll
+                    for (int b = 0; b < IL; ++b)
+                        vset<IL>(o, b, v[b]);
+                    *reinterpret_cast<bvec *>(crow + col) = o;
+                } else {
+#pragma unroll
+                    for (int b = 0; b < IL; ++b)
+                        if (FULL || col + b < a.N)
+                            crow[col + b] = v[b];
+                }
+            }
+        }
+    }
+}
+
+// After the k-loop: add the k-slices (KS > 1) and write the tile's outputs.
+// `pre`: this wavefront loaded its old C before the k-loop (OldC).
+template <class Gm, bool TRANS_B, bool FULL>
+__device__ __forceinline__ void finish_tile(const GemmArgs &a, f32x16 (&acc)[Gm::FM][Gm::FN], float *smem, int m0,
+                                            int n0, const Role<Gm> &ro, bool pre, const OldC<Gm> &oc)
+{
+    if constexpr (Gm::FIN == 1) {
+        if (reduce_slices<Gm>(acc, smem, ro)) {
+            if (pre)
+                oc.template epilogue<FULL>(a, acc, m0, n0, ro);
+            else
+                epilogue<Gm, TRANS_B, FULL>(a, acc, m0, n0, ro);
+        }
+    } else {
+        Finish<Gm> fin;
+        if (!reduce_units<Gm>(acc, smem, ro, fin))
+            return;
+        if (pre)
+            store_units<Gm, TRANS_B, FULL, 2>(a, fin, oc, m0, n0, ro);
+        else if (a.beta != 0.0f)
+            store_units<Gm, TRANS_B, FULL, 1>(a, fin, oc, m0, n0, ro);
+        else
+            store_units<Gm, TRANS_B, FULL, 0>(a, fin, oc, m0, n0, ro);
+    }
+}
 
 // One k-group of one stage: the first MFMA step runs on fragments read a whole
 // group earlier, before any new LDS traffic (so the wait in front of it never
@@ -648,7 +822,7 @@ __device__ __forceinline__ void gemm_tile_regs(const GemmArgs &a, float *smem, i
     const Role<Gm> ro;
     const int sl_off = ro.slice * Gm::SLICE;
     OldC<Gm> oc;
-    const bool pre = OldC<Gm>::ON && a.beta != 0.0f && ro.slice == 0;
+    const bool pre = OldC<Gm>::ON && a.beta != 0.0f && ro.slice < Gm::FIN;
     if (pre)
         oc.template load<FULL>(a, m0, n0, ro);
 
@@ -697,12 +871,7 @@ __device__ __forceinline__ void gemm_tile_regs(const GemmArgs &a, float *smem, i
             });
         }
     }
-    if (reduce_slices<Gm>(acc, smem, ro)) {
-        if (pre)
-            oc.template epilogue<FULL>(a, acc, m0, n0, ro);
-        else
-            epilogue<Gm, TRANS_B, FULL>(a, acc, m0, n0, ro);
-    }
+    finish_tile<Gm, TRANS_B, FULL>(a, acc, smem, m0, n0, ro, pre, oc);
 }
 
 // Where the wavefronts of an 8-wavefront workgroup issue the next stage's
@@ -732,7 +901,7 @@ __device__ __forceinline__ void gemm_tile_direct(const GemmArgs &a, float *smem,
     const int sl_off = ro.slice * Gm::SLICE;
     float *buf0 = smem, *buf1 = smem + Gm::STAGE;
     OldC<Gm> oc;
-    const bool pre = OldC<Gm>::ON && a.beta != 0.0f && ro.slice == 0;
+    const bool pre = OldC<Gm>::ON && a.beta != 0.0f && ro.slice < Gm::FIN;
     if (pre)
         oc.template load<!EDGE>(a, m0, n0, ro);
 
@@ -798,12 +967,7 @@ __device__ __forceinline__ void gemm_tile_direct(const GemmArgs &a, float *smem,
             }
         }
     }
-    if (reduce_slices<Gm>(acc, smem, ro)) {
-        if (pre)
-            oc.template epilogue<!EDGE>(a, acc, m0, n0, ro);
-        else
-            epilogue<Gm, TRANS_B, !EDGE>(a, acc, m0, n0, ro);
-    }
+    finish_tile<Gm, TRANS_B, !EDGE>(a, acc, smem, m0, n0, ro, pre, oc);
 }
 
 // One output tile at (m0, n0): direct staging for interior tiles (and edge
