@@ -881,12 +881,14 @@ __device__ __forceinline__ void gemm_tile_regs(const GemmArgs &a, float *smem, i
 // with wave & MASK set) issue theirs after the first MFMA step of k-group
 // GROUP instead, while the others multiply; the loads still land long before
 // the stage's closing barrier.  The masks are the fastest measured on MI355X
-// per tile, among splits by wave bit 0, 1 or 2 at k-group 1 or 2 (4096^3
+// per kernel, among splits by wave bit 0, 1 or 2 at k-group 1 or 2 (4096^3
 // 144.4 -> 146.5 TFLOP/s, 8192^3 145.5 -> 147.6; 128 x 128 tile at 6144^3
-// 138.3 -> 140.3; 64 x 64 tile at 1024^3 105.8 -> 109.4); MASK 0: no split.
+// 138.3 -> 140.3; 64 x 64 tile at 1024^3 105.8 -> 109.4; the stream-K
+// 128 x 128 kernel at 2048^3 131.1 -> 133.1 with bit 2, where bit 0 gave
+// 120.9); MASK 0: no split.
 template <class Gm>
 struct IssueSplit {
-    static constexpr int MASK = Gm::NW != 8 ? 0 : Gm::BM == 64 ? 4 : 1;
+    static constexpr int MASK = Gm::NW != 8 ? 0 : (Gm::BM == 64 || (Gm::OPQ && Gm::KS == 2)) ? 4 : 1;
     static constexpr int GROUP = 1;
     static_assert(MASK == 0 || GROUP < Gm::G - 1, "the late loads must come before the closing barrier's group");
 };
