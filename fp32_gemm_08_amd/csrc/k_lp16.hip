@@ -181,6 +181,15 @@ __global__ __launch_bounds__(Q::NT) void lp16_gemm_kernel(Lp16Args g)
     // all earlier LDS reads and waits only for the newer ones.
     const int nk = g.Kp / QK;
     constexpr int NF = Q::FM * Q::FN;
+    // With 8 wavefronts, those with wave bit 1 set request their share of a
+    // stage after the step's last MFMAs instead of right after the barrier,
+    // so the CU's address unit does not take all 8 wavefronts' loads at once
+    // (measured on MI355X, bf16 two-pass step: 4096^3 867.5 -> 878.8 TFLOP/s,
+    // 8192^3 1034 -> 1039).  The request still comes before the next wait, so
+    // the count of loads in flight there is unchanged.  The LDS-poisoning
+    // build poisons a stage with a barrier inside `issue`, which every
+    // wavefront must reach at the same point: it keeps one issue point.
+    const bool late = !kPoisonLds && Q::NT == 512 && (w & 2) != 0;
 #pragma unroll
     for (int st = 0; st < Q::S - 1; ++st)
         issue(min(st, nk - 1), st);
@@ -194,10 +203,14 @@ __global__ __launch_bounds__(Q::NT) void lp16_gemm_kernel(Lp16Args g)
         __builtin_amdgcn_sched_barrier(0);
         mma_step(fa0, fb0, 1, NF);
         q_wait_barrier<(Q::S - 3) * Q::LOADS>();  // stage kt+1 has landed
-        issue(min(kt + Q::S - 1, nk - 1), kt + Q::S - 1);
+        if (!late)
+            issue(min(kt + Q::S - 1, nk - 1), kt + Q::S - 1);
         read_frags(kt + 1, 0, fa0, fb0);
         __builtin_amdgcn_sched_barrier(0);
         mma_step(fa1, fb1, 0, NF);
+        __builtin_amdgcn_sched_barrier(0);
+        if (late)
+            issue(min(kt + Q::S - 1, nk - 1), kt + Q::S - 1);
     }
 
     // Epilogue: D = alpha * acc + beta * C, masked to M x N (C not read when
