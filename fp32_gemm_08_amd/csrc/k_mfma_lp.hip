@@ -227,13 +227,21 @@ __global__ __launch_bounds__(Gm::NT) void sgemm_mfma_lp_kernel(GemmArgs g)
     st.store(smem, smem + LBM * LP_PITCH);
     __syncthreads();
 
+    // With 8 wavefronts, those with wave bit 2 set issue the next k-tile's
+    // loads after the first 16-k step's MFMAs instead of at the top, so the
+    // CU's address unit does not take all 8 wavefronts' loads at once
+    // (measured on MI355X, bf16: 4096^3 790 -> 832 TFLOP/s, 8192^3 694 -> 707;
+    // bits 0 and 1 were faster at 4096^3 but slower at 8192^3 and 6144^3).
+    const bool late = Gm::NT == 512 && (w & 4) != 0;
     for (int kt = 0; kt < nk; ++kt) {
         T *as = smem + (kt & 1) * LP_STAGE;
         T *bs = as + LBM * LP_PITCH;
-        if (kt + 1 < nk)
+        if (!late && kt + 1 < nk)
             load_tile(kt + 1);
 #pragma unroll
         for (int ks = 0; ks < LBK / 16; ++ks) {
+            if (ks == 1 && late && kt + 1 < nk)
+                load_tile(kt + 1);
             V8 af[LFM], bf[LFN];
 #pragma unroll
             for (int fm = 0; fm < LFM; ++fm)
