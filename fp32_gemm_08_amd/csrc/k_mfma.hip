@@ -885,7 +885,9 @@ __device__ __forceinline__ void gemm_tile_regs(const GemmArgs &a, float *smem, i
 // 144.4 -> 146.5 TFLOP/s, 8192^3 145.5 -> 147.6; 128 x 128 tile at 6144^3
 // 138.3 -> 140.3; 64 x 64 tile at 1024^3 105.8 -> 109.4; the stream-K
 // 128 x 128 kernel at 2048^3 131.1 -> 133.1 with bit 2, where bit 0 gave
-// 120.9); MASK 0: no split.
+// 120.9); MASK 0: no split, as for the 4-wavefront tiles, where splitting
+// by bit 0 or 1 measured up to 10% slower (k-split partial pass, 512 x 512
+// x 8192 on the 32 x 32 tile).
 template <class Gm>
 struct IssueSplit {
     static constexpr int MASK = Gm::NW != 8 ? 0 : (Gm::BM == 64 || (Gm::OPQ && Gm::KS == 2)) ? 4 : 1;
