@@ -780,12 +780,12 @@ __device__ __forceinline__ void finish_tile(const GemmArgs &a, f32x16 (&acc)[Gm:
         Finish<Gm> fin;
         if (!reduce_units<Gm>(acc, smem, ro, fin))
             return;
-        if (pre)
-            store_units<Gm, TRANS_B, FULL, 2>(a, fin, oc, m0, n0, ro);
-        else if (a.beta != 0.0f)
-            store_units<Gm, TRANS_B, FULL, 1>(a, fin, oc, m0, n0, ro);
-        else
+        if (a.beta == 0.0f)
             store_units<Gm, TRANS_B, FULL, 0>(a, fin, oc, m0, n0, ro);
+        else if constexpr (OldC<Gm>::ON)
+            store_units<Gm, TRANS_B, FULL, 2>(a, fin, oc, m0, n0, ro);  // a finishing slice loaded its old C
+        else
+            store_units<Gm, TRANS_B, FULL, 1>(a, fin, oc, m0, n0, ro);
     }
 }
 
