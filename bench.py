@@ -893,7 +893,7 @@ def main():
     value = K_steps * flop / wall / 1e12
     kern_avg = span / K_steps
     achieved = flop / kern_avg / 1e12
-    mfma = kid in (40, 41, 42, 43, 44, 45, 60, 61, 62, 63, 64, 65, 66, 67)
+    mfma = kid in (40, 41, 42, 43, 44, 45, 46, 47, 60, 61, 62, 63, 64, 65, 66, 67)  # every matrix-core kernel id
     peak = HALF_MFMA_PEAK_TFLOPS if lowp else FP32_MFMA_PEAK_TFLOPS if mfma else FP32_VALU_PEAK_TFLOPS
     log(f"{'step (both kernels)' if ws is not None else 'kernel'} {kname}: avg {kern_avg * 1e3:.4f} ms "
         f"over {K_steps} calls "

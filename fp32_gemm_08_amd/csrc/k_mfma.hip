@@ -1164,6 +1164,7 @@ TileShape tile_shape(int kid)
     case KID_MFMA_S:
     case KID_MFMA_S2: return {64, 64};
     case KID_MFMA_T: return {32, 32};
+    case KID_MFMA_R: return {128, 64};
     case KID_REGBLOCK: return {128, 128};
     case KID_TILED_PAD:
     case KID_TILED_NOPAD: return {16, 16};
@@ -1237,6 +1238,7 @@ hipError_t launch_mfma(const GemmArgs &a, int kid, bool transB, hipStream_t stre
     case KID_MFMA_S: launch_cfg<64, 64, 32, 32, 2, 2, 4, 1>(a, transB, stream, splits); break;
     case KID_MFMA_S2: launch_cfg<64, 64, 32, 32, 2, 2, 2, 2>(a, transB, stream, splits); break;
     case KID_MFMA_T: launch_cfg<32, 32, 32, 32, 1, 1, 2, 4>(a, transB, stream, splits); break;
+    case KID_MFMA_R: launch_cfg<128, 64, 32, 32, 4, 1, 2, 2>(a, transB, stream, splits); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -85,7 +85,8 @@ double mfma_rate(int kid, int64_t M, int64_t N)
 // The FP32 MFMA kernels of the plain call.
 bool is_mfma_f32(int kid)
 {
-    return kid == KID_MFMA_L || kid == KID_MFMA_M || kid == KID_MFMA_S || kid == KID_MFMA_S2 || kid == KID_MFMA_T;
+    return kid == KID_MFMA_L || kid == KID_MFMA_M || kid == KID_MFMA_S || kid == KID_MFMA_S2 || kid == KID_MFMA_T ||
+           kid == KID_MFMA_R;
 }
 
 constexpr int64_t kSmallGrid = 144;
@@ -117,6 +118,16 @@ int choose_mfma(int64_t M, int64_t N, int64_t K)
         const int64_t tiles = ceil_div(M, 64) * ceil_div(N, 64);
         if ((tiles <= 256 || tiles > 512) && K >= 256 && tiles * 512 <= kMaxWorkItems)
             best = KID_MFMA_S2;
+        // Grids of 257 to 512 such tiles: the 128 x 64 tile (8 wavefronts, k
+        // split two ways) gives one workgroup per CU with a quarter fewer
+        // operand bytes per FLOP than two 64 x 64 workgroups, where it stays
+        // within 256 tiles and pads at most 1/16 more rows.  Measured on MI355X:
+        // 512 x 4096 x 4096 130.0 -> 133.6 TFLOP/s, 1024 x 2048 x 2048 126.2 ->
+        // 129.0, 768 x 2048 x 4096 98.4 -> 101.0, 1280^3 96.6 -> 97.0.
+        const int64_t rows_r = ceil_div(M, 128) * 128, rows_s = ceil_div(M, 64) * 64;
+        if (tiles > 256 && tiles <= 512 && K >= 256 && ceil_div(M, 128) * ceil_div(N, 64) <= 256 &&
+            rows_r * 16 <= rows_s * 17)
+            best = KID_MFMA_R;
         // With at most kSmallGrid tiles of 64 x 64 the grid leaves most CUs
         // idle (or, above 128 tiles, gives a few of them a second round): the
         // 32 x 32 tile with k split four ways inside the workgroup gives each
@@ -172,7 +183,8 @@ int64_t auto_splits(int64_t M, int64_t N, int64_t K)
 
 int threads_per_block(int kid)
 {
-    return (kid == KID_MFMA_L || kid == KID_MFMA_M || kid == KID_MFMA_S2) ? 512 : 256;  // KID_MFMA_T: 256
+    return (kid == KID_MFMA_L || kid == KID_MFMA_M || kid == KID_MFMA_S2 || kid == KID_MFMA_R) ? 512
+                                                                                              : 256;  // KID_MFMA_T: 256
 }
 
 Plan make_plan(int algo, int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
@@ -184,7 +196,7 @@ Plan make_plan(int algo, int64_t M, int64_t N, int64_t K, float alpha, const flo
         p.kid = KID_NONE;
         return p;
     };
-    if (algo < SGEMM_ALGO_AUTO || algo > SGEMM_ALGO_MFMA_32)
+    if (algo < SGEMM_ALGO_AUTO || algo > SGEMM_ALGO_MFMA_128X64)
         return fail(SGEMM_ERR_INVALID_VALUE);
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
         return fail(SGEMM_ERR_INVALID_VALUE);
@@ -231,6 +243,7 @@ Plan make_plan(int algo, int64_t M, int64_t N, int64_t K, float alpha, const flo
     case SGEMM_ALGO_MFMA_128: p.kid = KID_MFMA_M; break;
     case SGEMM_ALGO_MFMA_64: p.kid = KID_MFMA_S; break;
     case SGEMM_ALGO_MFMA_32: p.kid = KID_MFMA_T; break;
+    case SGEMM_ALGO_MFMA_128X64: p.kid = KID_MFMA_R; break;
     }
     const TileShape t = tile_shape(p.kid);
     p.tiles_m = ceil_div(M, t.bm);
@@ -312,6 +325,7 @@ const char *kernel_label(int kid)
     case KID_MFMA_M: return "mfma_128x128x32_w2x2_ks2";
     case KID_MFMA_S: return "mfma_64x64x32_w2x2";
     case KID_MFMA_S2: return "mfma_64x64x32_w2x2_ks2";
+    case KID_MFMA_R: return "mfma_128x64x32_w4x1_ks2";
     case KID_MFMA_T: return "mfma_32x32x32_w1x1_ks4";
     case KID_MFMA_L_SK: return "mfma_256x256x32_w4x2_streamk";
     case KID_MFMA_M_SK: return "mfma_128x128x32_w2x2_ks2_streamk";
@@ -355,8 +369,8 @@ int parse_algo_override(const char *v)
 {
     if (v == nullptr || *v == '\0')
         return kNoOverride;
-    static const char *const names[] = {"auto", "naive", "lds_tiled", "regblock", "mfma", "lds_tiled_nopad",
-                                        "naive_wg", "mfma_256", "mfma_128", "mfma_64", "mfma_32"};
+    static const char *const names[] = {"auto",     "naive",    "lds_tiled", "regblock", "mfma",   "lds_tiled_nopad",
+                                        "naive_wg", "mfma_256", "mfma_128",  "mfma_64",  "mfma_32", "mfma_128x64"};
     const int n = (int)(sizeof(names) / sizeof(names[0]));
     for (int i = 0; i < n; ++i)
         if (std::strcmp(v, names[i]) == 0)
@@ -651,7 +665,9 @@ SkPlan sk_schedule(const Plan &base, int kid, int64_t M, int64_t N, int64_t K)
 // the two stream-K tiles came within 1.5% of the fastest every time.
 double plain_time_us(int64_t M, int64_t N, int64_t K)
 {
-    const int kid = choose_mfma(M, N, K);
+    int kid = choose_mfma(M, N, K);
+    if (kid == KID_MFMA_R)
+        kid = KID_MFMA_S;  // modelled as the 64 x 64 grid it replaces (it runs ~2% faster)
     return 2.0 * (double)M * (double)N * (double)K / (mfma_rate(kid, M, N) * 1e6);
 }
 

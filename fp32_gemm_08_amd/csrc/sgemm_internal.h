@@ -62,6 +62,7 @@ enum KernelId : int {
     KID_MFMA_M_SK = 44,     // KID_MFMA_M under a stream-K schedule (+ fix-up kernel)
     KID_MFMA_S2 = 45,       // 64 x 64, 8 wavefronts: 2 x 2 over the tile x 2 over k
     KID_MFMA_T = 46,        // 32 x 32, 4 wavefronts: one per k-slice, k split 4 ways
+    KID_MFMA_R = 47,        // 128 x 64, 8 wavefronts: 4 x 1 over the tile x 2 over k
     KID_MFMA_LP_F16 = 60,   // mixed precision, operands rounded to fp16, 256 x 256
     KID_MFMA_LP_BF16 = 61,  // the same with bf16
     KID_MFMA_LP_F16_S = 62, // mixed precision, fp16, 64 x 64 (few output tiles)

@@ -29,7 +29,7 @@ SGEMM_ERR_SCRATCH_LIMIT = 6
 SCRATCH_BYTES = 16 << 20
 
 ALGO = {"auto": 0, "naive": 1, "lds_tiled": 2, "regblock": 3, "mfma": 4, "lds_tiled_nopad": 5, "naive_wg": 6,
-        "mfma_256": 7, "mfma_128": 8, "mfma_64": 9, "mfma_32": 10}
+        "mfma_256": 7, "mfma_128": 8, "mfma_64": 9, "mfma_32": 10, "mfma_128x64": 11}
 TRANSPOSE_ALGO = {"auto": 0, "naive": 1, "lds": 2, "lds_nopad": 3, "narrow": 4}
 
 # Symbols declared in include/sgemm_f32.h.

@@ -97,18 +97,22 @@ typedef enum {
  *                    the naive and 2-D block-tiled CUDA matmul, paragraph on the
  *                    naive implementation: one block per output element with an
  *                    in-block reduction).
- *   MFMA_256, MFMA_128, MFMA_64, MFMA_32
+ *   MFMA_256, MFMA_128, MFMA_64, MFMA_32, MFMA_128X64
  *                    the MFMA path with its workgroup tile fixed: 256 x 256 (8
  *                    wavefronts), 128 x 128 (8 wavefronts as two k-slices of 4),
- *                    64 x 64 (4 wavefronts, up to 4 workgroups per CU) or 32 x 32
- *                    (4 wavefronts, each a k-slice of a quarter of k; 2 per CU).
+ *                    64 x 64 (4 wavefronts, up to 4 workgroups per CU), 32 x 32
+ *                    (4 wavefronts, each a k-slice of a quarter of k; 2 per CU)
+ *                    or 128 x 64 (8 wavefronts as two k-slices of 4).
  *   AUTO             MFMA with a tile chosen from the problem shape; where it picks
  *                    the 64 x 64 tile it runs it as 8 wavefronts (two k-slices of
- *                    4, kernel id 45) unless the grid is 257 to 512 tiles or K
- *                    is below 256, where the 4-wavefront kernel (id 42, as
- *                    MFMA_64) is faster; and where that grid has at most 144
- *                    tiles (too few to fill the 256 CUs) it takes the 32 x 32
- *                    tile (kernel id 46, as MFMA_32).
+ *                    4, kernel id 45), except: on grids of 257 to 512 such tiles
+ *                    with K of at least 256 it takes the 128 x 64 tile (kernel id
+ *                    47, as MFMA_128X64: one workgroup per CU) when that tile
+ *                    gives at most 256 workgroups and pads at most 1/16 more
+ *                    rows, else the 4-wavefront kernel (id 42, as MFMA_64), which
+ *                    also runs those grids when K is below 256; and where the
+ *                    64 x 64 grid has at most 144 tiles (too few to fill the 256
+ *                    CUs) it takes the 32 x 32 tile (kernel id 46, as MFMA_32).
  */
 typedef enum {
     SGEMM_ALGO_AUTO = 0,
@@ -121,7 +125,8 @@ typedef enum {
     SGEMM_ALGO_MFMA_256 = 7,
     SGEMM_ALGO_MFMA_128 = 8,
     SGEMM_ALGO_MFMA_64 = 9,
-    SGEMM_ALGO_MFMA_32 = 10
+    SGEMM_ALGO_MFMA_32 = 10,
+    SGEMM_ALGO_MFMA_128X64 = 11
 } sgemm_algo;
 
 /*
@@ -129,7 +134,8 @@ typedef enum {
  * the AUTO entry points (sgemm_f32, and sgemm_f32_algo / sgemm_f32_plan with
  * SGEMM_ALGO_AUTO): the lower-case name of an sgemm_algo value without its
  * prefix ("naive", "lds_tiled", "regblock", "mfma", "lds_tiled_nopad",
- * "naive_wg", "mfma_256", "mfma_128", "mfma_64", "mfma_32"; "auto" or an
+ * "naive_wg", "mfma_256", "mfma_128", "mfma_64", "mfma_32", "mfma_128x64";
+ * "auto" or an
  * empty value: no override) or its number.  Any other value makes those calls
  * return SGEMM_ERR_INVALID_VALUE.  The workspace, k-split, stream-K and
  * mixed-precision calls are not affected.

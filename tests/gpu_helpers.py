@@ -8,7 +8,7 @@ import fp32_gemm_08_amd as lib
 
 CANARY = np.float32(-7777.25)
 GUARD_ROWS = 2
-ALGOS = ["naive", "naive_wg", "lds_tiled", "lds_tiled_nopad", "regblock", "mfma", "mfma_32", "auto"]
+ALGOS = ["naive", "naive_wg", "lds_tiled", "lds_tiled_nopad", "regblock", "mfma", "mfma_32", "mfma_128x64", "auto"]
 
 
 def say(*msg):

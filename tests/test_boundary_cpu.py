@@ -19,7 +19,7 @@ HEADER = os.path.join(ROOT, "include", "sgemm_f32.h")
 OK, INVALID, ALIAS = 0, 1, 2
 KID_NONE, KID_SCALE, KID_NAIVE, KID_TILED, KID_TILED_NOPAD, KID_REG = 0, 1, 10, 20, 21, 30
 KID_NAIVE_WG = 11
-KID_L, KID_M, KID_S, KID_S2, KID_T = 40, 41, 42, 45, 46
+KID_L, KID_M, KID_S, KID_S2, KID_T, KID_R = 40, 41, 42, 45, 46, 47
 
 # Fake, well-separated "device" addresses: planning only compares ranges.
 PA, PB, PC = 1 << 32, 1 << 40, 1 << 44
@@ -72,7 +72,7 @@ def call(algo=0, M=64, N=64, K=64, alpha=1.0, A=PA, lda=None, B=PB, ldb=None, tr
     dict(M=-1), dict(N=-1), dict(K=-1), dict(M=1 << 31), dict(K=1 << 31),
     dict(transB=2), dict(transB=-1),
     dict(lda=63), dict(ldb=63), dict(ldc=63), dict(transB=1, ldb=63),
-    dict(A=0), dict(B=0), dict(C=0), dict(algo=11), dict(algo=-1),
+    dict(A=0), dict(B=0), dict(C=0), dict(algo=12), dict(algo=-1),
     dict(M=(1 << 31) - 1024), dict(N=(1 << 31) - 1024), dict(K=(1 << 31) - 1024),
     dict(M=2, K=2, lda=1 << 61),
     # pointers off a float boundary
@@ -130,7 +130,8 @@ def test_product_free_cases_scale_c():
 
 
 @pytest.mark.parametrize("algo,kid", [(1, KID_NAIVE), (2, KID_TILED), (3, KID_REG), (5, KID_TILED_NOPAD),
-                                      (6, KID_NAIVE_WG), (7, KID_L), (8, KID_M), (9, KID_S), (10, KID_T)])
+                                      (6, KID_NAIVE_WG), (7, KID_L), (8, KID_M), (9, KID_S), (10, KID_T),
+                                      (11, KID_R)])
 def test_explicit_algorithms(algo, kid):
     st, k, tm, tn, name = plan(algo=algo, M=1000, N=1017, K=999)
     assert (st, k) == (OK, kid)
@@ -146,6 +147,8 @@ def test_explicit_algorithms(algo, kid):
         assert (tm, tn) == (16, 16) and name.startswith("mfma_64x64")
     elif kid == KID_T:
         assert (tm, tn) == (32, 32) and name.startswith("mfma_32x32x32_w1x1_ks4")
+    elif kid == KID_R:
+        assert (tm, tn) == (8, 16) and name.startswith("mfma_128x64x32_w4x1_ks2")
     else:
         assert (tm, tn) == (8, 8)
 
@@ -155,7 +158,8 @@ def test_explicit_algorithms(algo, kid):
     ((8192, 8192, 8192), KID_L, (32, 32)),
     ((16384, 4096, 1024), KID_L, (64, 16)),
     ((2048, 2048, 2048), KID_M, (16, 16)),
-    # the 64 x 64 tile: 8 wavefronts (k split in two) unless the grid is 257..512 tiles or K < 256
+    # the 64 x 64 tile: 8 wavefronts (k split in two); grids of 257..512 tiles: the 128 x 64 tile when it
+    # gives at most 256 workgroups and pads at most 1/16 more rows, else (and with K < 256) 4 wavefronts
     ((1024, 1024, 1024), KID_S2, (16, 16)),
     ((1000, 1017, 999), KID_S2, (16, 16)),
     ((832, 832, 832), KID_S2, (13, 13)),       # 169 tiles
@@ -168,8 +172,12 @@ def test_explicit_algorithms(algo, kid):
     ((128, 128, 256), KID_T, (4, 4)),
     ((512, 512, 8192), KID_T, (16, 16)),
     ((128, 4096, 1024), KID_T, (4, 128)),
-    ((1280, 1280, 1280), KID_S, (20, 20)),     # 400 tiles
-    ((512, 4096, 4096), KID_S, (8, 64)),       # 512 tiles
+    ((1280, 1280, 1280), KID_R, (10, 20)),     # 400 tiles of 64 x 64
+    ((512, 4096, 4096), KID_R, (4, 64)),       # 512 tiles
+    ((1088, 1024, 1024), KID_R, (9, 16)),      # 17 x 16 tiles; 9 x 128 rows pad 1/17 more
+    ((576, 2048, 1024), KID_S, (9, 32)),       # 288 tiles; 5 x 128 rows would pad 1/9 more
+    ((1280, 1280, 128), KID_S, (20, 20)),      # K below 256
+    ((2176, 512, 1024), KID_R, (17, 8)),       # 272 tiles of 64 x 64
     ((576, 4096, 1024), KID_S2, (9, 64)),      # 576 tiles
     ((3584, 3584, 3584), KID_S2, (56, 56)),
     ((4608, 4608, 4608), KID_S2, (72, 72)),
@@ -247,7 +255,8 @@ print(json.dumps([plan(0), plan(4), plan(1), lib.sgemm_f32_ws_plan(512, 512, 819
 @pytest.mark.parametrize("value,auto", [("", (OK, KID_S2)), ("auto", (OK, KID_S2)), ("regblock", (OK, KID_REG)),
                                         ("mfma_256", (OK, KID_L)), ("9", (OK, KID_S)), ("mfma_32", (OK, KID_T)),
                                         ("naive_wg", (OK, KID_NAIVE_WG)), ("fastest", (INVALID, KID_NONE)),
-                                        ("11", (INVALID, KID_NONE)), ("MFMA", (INVALID, KID_NONE))])
+                                        ("mfma_128x64", (OK, KID_R)), ("11", (OK, KID_R)),
+                                        ("12", (INVALID, KID_NONE)), ("MFMA", (INVALID, KID_NONE))])
 def test_algo_environment_override(value, auto):
     """SGEMM_F32_ALGO replaces AUTO's choice in sgemm_f32 / sgemm_f32_algo(AUTO) / the plan, fails loudly
     when it names no algorithm, and leaves explicit algorithms and the workspace and mixed-precision

@@ -72,7 +72,7 @@ def test_config_full(oracle_lib, name, algo):
 
 # The product paths (AUTO picks among the MFMA tiles) and the register-blocked
 # stage: every output element.
-FULL_ALGOS = ["auto", "mfma", "mfma_256", "mfma_128", "mfma_64", "regblock"]
+FULL_ALGOS = ["auto", "mfma", "mfma_256", "mfma_128", "mfma_64", "mfma_128x64", "regblock"]
 SAMPLED_ALGOS = [a for a in ALGOS if a not in FULL_ALGOS]
 
 
@@ -168,8 +168,8 @@ def _sweep_cases(n, seed):
     return out
 
 
-@pytest.mark.parametrize("algo", ["mfma", "mfma_256", "mfma_128", "mfma_64", "mfma_32", "regblock", "lds_tiled",
-                                  "naive", "naive_wg"])
+@pytest.mark.parametrize("algo", ["mfma", "mfma_256", "mfma_128", "mfma_64", "mfma_32", "mfma_128x64", "regblock",
+                                  "lds_tiled", "naive", "naive_wg"])
 def test_random_ragged_sweep(oracle_lib, algo):
     """Seeded sweep of ragged shapes in [1, 700]^3, both op(B), random alpha/beta."""
     for (M, N, K, t, alpha, beta, seed) in _sweep_cases(24 if algo.startswith("mfma") else 8, 42):
@@ -180,8 +180,8 @@ def test_random_ragged_sweep(oracle_lib, algo):
         assert_parity(Dg[:, :N], D, S, K, f"sweep {M}x{N}x{K} t{t}/{algo}")
 
 
-@pytest.mark.parametrize("algo", ["mfma", "mfma_256", "mfma_128", "mfma_64", "mfma_32", "regblock", "lds_tiled",
-                                  "naive", "naive_wg"])
+@pytest.mark.parametrize("algo", ["mfma", "mfma_256", "mfma_128", "mfma_64", "mfma_32", "mfma_128x64", "regblock",
+                                  "lds_tiled", "naive", "naive_wg"])
 def test_degenerate_shapes(oracle_lib, algo):
     for (M, N, K, t) in [(1, 1, 1, 0), (1, 1, 1, 1), (1, 513, 1, 0), (513, 1, 2, 1), (31, 33, 1, 0),
                          (64, 64, 8, 1), (65, 65, 9, 0), (7, 5, 4099, 1)]:
@@ -231,14 +231,15 @@ def test_mid_tile_integers_bit_exact(oracle_lib):
 # (op(B) = B with N % 4 != 0); K tails on some.
 # Kernel 45, the 64 x 64 tile as 8 wavefronts (two k-slices), runs where AUTO
 # picks the 64 x 64 tile on a grid of at most 256 (or over 512) tiles.
-TILE_ALGO = {40: "mfma_256", 41: "mfma_128", 42: "mfma_64", 45: "auto", 46: "mfma_32"}
+TILE_ALGO = {40: "mfma_256", 41: "mfma_128", 42: "mfma_64", 45: "auto", 46: "mfma_32", 47: "mfma_128x64"}
 EDGE_SHAPES = [(1000, 1000, 1024, 0, 42), (1000, 1000, 1024, 1, 42), (1000, 1004, 999, 0, 42),
                (1003, 1001, 1000, 1, 42), (1001, 1003, 1000, 0, 42), (2000, 2052, 1000, 0, 41),
                (2001, 1999, 777, 1, 41), (3999, 4000, 512, 0, 40), (4000, 3998, 520, 1, 40),
                (4001, 4003, 300, 0, 40), (1000, 1000, 1024, 0, 45), (1000, 1000, 1024, 1, 45),
                (1000, 1004, 999, 0, 45), (1003, 1001, 1000, 1, 45), (1001, 1003, 1000, 0, 45),
                (2237, 2243, 509, 1, 45), (500, 300, 1000, 0, 46), (333, 556, 777, 1, 46), (1001, 1003, 999, 0, 46),
-               (97, 4100, 300, 1, 46)]
+               (97, 4100, 300, 1, 46), (1000, 1000, 1024, 0, 47), (1003, 1001, 1000, 1, 47),
+               (1001, 1003, 1000, 0, 47), (1290, 1270, 509, 0, 47), (1290, 1270, 509, 1, 47)]
 
 
 @pytest.mark.parametrize("shape", EDGE_SHAPES, ids=lambda s: "x".join(str(v) for v in s[:4]))
@@ -263,7 +264,8 @@ def test_edge_tiles_aligned(oracle_lib, shape):
 # number of 32-wide k-tiles (K = 288: 9 tiles) or end in a k tail (K = 257).
 @pytest.mark.parametrize("shape", [(832, 832, 255, 0, 42), (832, 832, 256, 0, 45), (832, 832, 257, 1, 45),
                                    (832, 836, 288, 0, 45), (1000, 1000, 1024, 1, 45), (768, 768, 1000, 1, 46),
-                                   (1000, 500, 300, 0, 46)],
+                                   (1000, 500, 300, 0, 46), (1280, 1280, 1280, 0, 47), (1280, 1283, 257, 1, 47),
+                                   (1280, 1280, 255, 0, 42), (576, 2048, 1024, 1, 42)],
                          ids=lambda s: "x".join(str(v) for v in s[:4]))
 def test_auto_64_kernel_switch(oracle_lib, shape):
     M, N, K, t, want = shape
@@ -284,7 +286,8 @@ def test_auto_64_kernel_switch(oracle_lib, shape):
 UNALIGNED_SHAPES = [(1000, 1017, 999, 1, 0, 42), (1001, 1003, 1000, 0, 0, 42), (1000, 1000, 1024, 0, 1, 42),
                     (2001, 1999, 777, 1, 0, 41), (2048, 2050, 1001, 0, 1, 41), (3999, 4001, 501, 0, 0, 40),
                     (1000, 1017, 999, 1, 0, 45), (1001, 1003, 1000, 0, 0, 45), (1000, 1000, 1024, 0, 1, 45),
-                    (1000, 1017, 999, 1, 0, 46), (1001, 1003, 1000, 0, 1, 46)]
+                    (1000, 1017, 999, 1, 0, 46), (1001, 1003, 1000, 0, 1, 46), (1000, 1017, 999, 1, 0, 47),
+                    (1001, 1003, 1000, 0, 1, 47)]
 
 
 @pytest.mark.parametrize("shape", UNALIGNED_SHAPES, ids=lambda s: "x".join(str(v) for v in s[:5]))
@@ -302,7 +305,7 @@ def test_unaligned_operands(oracle_lib, shape):
     assert_parity(Dg[rows, :N], D, S, K, f"unaligned {M}x{N}x{K} t{t} a_off={a_off}")
 
 
-@pytest.mark.parametrize("algo", ["mfma_256", "mfma_128", "mfma_64", "mfma_32", "auto"])
+@pytest.mark.parametrize("algo", ["mfma_256", "mfma_128", "mfma_64", "mfma_32", "mfma_128x64", "auto"])
 @pytest.mark.parametrize("t", [0, 1])
 def test_unaligned_integers_bit_exact(oracle_lib, t, algo):
     case = make_case(1003, 1001, 999, trans_b=t, alpha=1.0, beta=1.0, dist="int2", seed=23)
@@ -312,7 +315,7 @@ def test_unaligned_integers_bit_exact(oracle_lib, t, algo):
     assert np.array_equal(Dg[:, :1001], D.astype(np.float32))
 
 
-@pytest.mark.parametrize("algo", ["mfma_256", "mfma_128", "mfma_64", "mfma_32", "auto"])
+@pytest.mark.parametrize("algo", ["mfma_256", "mfma_128", "mfma_64", "mfma_32", "mfma_128x64", "auto"])
 @pytest.mark.parametrize("t", [0, 1])
 def test_edge_tiles_integers_bit_exact(oracle_lib, t, algo):
     case = make_case(1003, 1004, 1000, trans_b=t, alpha=1.0, beta=1.0, dist="int2", seed=19)
@@ -346,7 +349,8 @@ def test_empty_shapes_touch_nothing():
         assert np.all(Dg[:, :N] == 1.0)
 
 
-@pytest.mark.parametrize("algo", ["auto", "mfma_256", "mfma_128", "mfma_64", "mfma_32", "regblock", "lds_tiled"])
+@pytest.mark.parametrize("algo", ["auto", "mfma_256", "mfma_128", "mfma_64", "mfma_32", "mfma_128x64", "regblock",
+                                  "lds_tiled"])
 def test_deterministic_reruns(algo):
     """Ten reruns give the same bits: the summation order is fixed per kernel."""
     case = make_case(1000, 1017, 999, trans_b=True, alpha=1.5, beta=-0.5, dist="uniform", seed=2)

@@ -18,9 +18,9 @@ every wavefront and lane of each tile geometry the library launches and checks:
 
 Operands are filled with their own flat addresses, so content checks compare
 addresses.  The geometries are the kernel configurations in use: 64 x 64 with
-4 wavefronts, 64 x 64 and 128 x 128 with 8 wavefronts as two k-slices,
-256 x 256 with 8 wavefronts, and 32 x 32 with 4 wavefronts as four k-slices,
-BK 32.
+4 wavefronts, 64 x 64, 128 x 128 and 128 x 64 with 8 wavefronts as two
+k-slices, 256 x 256 with 8 wavefronts, and 32 x 32 with 4 wavefronts as four
+k-slices, BK 32.
 """
 import numpy as np
 import pytest
@@ -103,7 +103,8 @@ def stage_and_check(BM, BN, BK, NW, KS, trans_b, edge, M, N, K, lda, ldb, m0, n0
                     assert lds[p] == B[kk, n0 + n], ("B content", sl, n, k)
 
 
-GEOMETRIES = [(64, 64, 32, 4, 1), (64, 64, 32, 8, 2), (128, 128, 32, 8, 2), (256, 256, 32, 8, 1), (32, 32, 32, 4, 4)]
+GEOMETRIES = [(64, 64, 32, 4, 1), (64, 64, 32, 8, 2), (128, 128, 32, 8, 2), (256, 256, 32, 8, 1), (32, 32, 32, 4, 4),
+              (128, 64, 32, 8, 2)]
 
 
 @pytest.mark.parametrize("geo", GEOMETRIES, ids=lambda g: f"{g[0]}x{g[1]}_w{g[3]}_ks{g[4]}")
@@ -114,7 +115,7 @@ def test_direct_staging(geo, trans_b, pad):
     pa, pb = pad
     K = 4 * KS * BK
     # an interior tile; leading dimensions a multiple of 4 or not
-    M = N = 3 * BM
+    M, N = 3 * BM, 3 * BN
     stage_and_check(BM, BN, BK, NW, KS, trans_b, False, M, N, K, K + pa, (K if trans_b else N) + pb, BM, BN, 1)
     # an edge tile in M and N (the edge path of op(B) = B needs N % 4 == 0)
     M2, N2 = BM + 37, BN + (21 if trans_b else 20)
