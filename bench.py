@@ -478,6 +478,119 @@ def bench_mfma_ceiling(args):
     print(json.dumps(out), flush=True)
 
 
+LP_PROBE_FLOP_PER_TRIP = 4 * 8 * 32768.0   # per workgroup: 4 wavefronts x 8 MFMAs x 32768 FLOP
+
+
+def bench_mfma_ceiling_lp(args):
+    """The 16-bit matrix-core rate the device sustains with register operands
+    only, random and all-zero, against the published 2500 TFLOP/s: how far the
+    clock falls under a full 16-bit matrix-core load sets the ceiling the
+    mixed-precision GEMM is compared with."""
+    import torch
+
+    import fp32_gemm_08_amd as lib
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream(dev)
+    prec = lib.PRECISION[args.precision]
+    workgroups, trips = 512, 8000       # 2 workgroups per CU: 2 wavefronts on every SIMD; ~3-4 ms a launch
+    sink = torch.empty(workgroups * 256, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(workgroups * 2, dtype=torch.int64, device=dev)
+    flop = workgroups * trips * LP_PROBE_FLOP_PER_TRIP
+
+    def measure(zero):
+        def launch():
+            st = lib.sgemm_f32_mfma_probe_lp(prec, zero, workgroups, trips, sink.data_ptr(), clocks.data_ptr(),
+                                             stream.cuda_stream)
+            if st != 0:
+                raise RuntimeError(lib.sgemm_f32_status_string(st))
+
+        t_end = time.perf_counter() + 0.5      # let the clock settle under this load
+        while time.perf_counter() < t_end:
+            for _ in range(10):
+                launch()
+            torch.cuda.synchronize()
+        steps = max(args.steps // 5, 5)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        avg = e0.elapsed_time(e1) * 1e-3 / steps
+        c = clocks.cpu().view(workgroups, 2).double()
+        mhz = 100.0 * c[:, 0] / c[:, 1]
+        return steps, avg, {"mean": round(mhz.mean().item(), 1), "min": round(mhz.min().item(), 1),
+                            "max": round(mhz.max().item(), 1)}
+
+    steps, avg, clk = measure(0)
+    _, avg0, clk0 = measure(1)
+    out = {
+        "metric": f"{args.precision.upper()} matrix-core sustained TFLOP/s (register-only MFMA probe), 1 GPU",
+        "value": round(flop / avg / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+        "higher_is_better": True, "kernel_avg_ms": round(avg * 1e3, 4),
+        "peak": HALF_MFMA_PEAK_TFLOPS, "frac": round(flop / avg / 1e12 / HALF_MFMA_PEAK_TFLOPS, 4),
+        "config": {"workload": f"{workgroups} workgroups x 4 wavefronts x {trips * 8} "
+                               f"v_mfma_f32_32x32x16_{args.precision}, random register operands in [-1, 1)",
+                   "flop_per_launch": flop},
+        "shader_clock_mhz": clk,
+        "zero_operands": {"value": round(flop / avg0 / 1e12, 2), "kernel_avg_ms": round(avg0 * 1e3, 4),
+                          "frac": round(flop / avg0 / 1e12 / HALF_MFMA_PEAK_TFLOPS, 4), "shader_clock_mhz": clk0},
+        "device": device_record(torch, dev),
+    }
+    print(json.dumps(out), flush=True)
+
+
+# Load-probe layouts: (name, region bytes, workgroups sharing a region).
+LOAD_PROBE_MODES = (("L2-resident: 256 KiB per XCD, read by its 32 workgroups", 256 << 10, 32),
+                    ("panels: 4 MiB read by 4 workgroups of one XCD (256 MiB in all)", 4 << 20, 4),
+                    ("private: 4 MiB per workgroup (1 GiB in all, from HBM)", 4 << 20, 1))
+
+
+def load_ceiling():
+    """Bytes per shader cycle one CU stages into LDS with direct loads and
+    nothing else running (one workgroup per CU, 4 MiB each), by wavefronts,
+    loads in flight per wavefront and where the data come from: the feed
+    ceiling of the MFMA kernels' staging."""
+    import torch
+
+    import fp32_gemm_08_amd as lib
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream(dev)
+    workgroups = 256
+    src_bytes = 1 << 30
+    src = torch.zeros(src_bytes // 4, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(workgroups * 2, dtype=torch.int64, device=dev)
+    print("| source | wavefronts | loads in flight per wavefront | KiB in flight per CU | B per CU-cycle | "
+          "chip TB/s (events) | shader clock MHz |")
+    print("|---|---|---|---|---|---|---|")
+    for name, region, share in LOAD_PROBE_MODES:
+        for waves in (4, 8):
+            for depth in (1, 2, 4, 8):
+                loads = (4 << 20) // (waves * 1024)
+
+                def launch():
+                    st = lib.sgemm_f32_load_probe(waves, depth, workgroups, src.data_ptr(), src_bytes, region, share,
+                                                  loads, clocks.data_ptr(), stream.cuda_stream)
+                    if st != 0:
+                        raise RuntimeError(lib.sgemm_f32_status_string(st))
+
+                for _ in range(3):
+                    launch()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(5):
+                    launch()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                t = e0.elapsed_time(e1) * 1e-3 / 5
+                c = clocks.cpu().view(workgroups, 2).double()
+                per_wg = loads * waves * 1024.0
+                bpc = per_wg / c[:, 0].mean().item()
+                mhz = (100.0 * c[:, 0] / c[:, 1]).mean().item()
+                print(f"| {name} | {waves} | {depth} | {waves * depth} | {bpc:.1f} | "
+                      f"{workgroups * per_wg / t / 1e12:.2f} | {mhz:.0f} |", flush=True)
+
+
 def device_record(torch, dev, clock=None):
     """What the run ran on: device, compute units, memory, HIP/ROCm versions and
     the shader clock read right after the timed steps."""
@@ -746,9 +859,12 @@ def main():
                     help="time the FP64 oracle on every GEMM workload (CPU only, reported, no JSON line)")
     ap.add_argument("--cu-scaling", action="store_true",
                     help="time the 256x256 MFMA kernel with 16..256 busy CUs, one tile each (table)")
+    ap.add_argument("--load-ceiling", action="store_true",
+                    help="table of the direct global->LDS load rate per CU (the library's load probe)")
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="time the library's register-only MFMA probe: the FP32 matrix-core rate the device "
-                         "sustains and its shader clock (one JSON line)")
+                         "sustains and its shader clock (one JSON line); with --precision fp16|bf16 the 16-bit "
+                         "matrix cores, with random and with all-zero operands")
     ap.add_argument("--tile-sweep", action="store_true",
                     help="time each fixed MFMA tile, AUTO and the workspace schedules over a spread of shapes (no JSON line)")
     args = ap.parse_args()
@@ -767,6 +883,12 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.mfma_ceiling and args.precision != "fp32":
+        bench_mfma_ceiling_lp(args)
+        return
+    if args.load_ceiling:
+        load_ceiling()
         return
     if args.mfma_ceiling:
         bench_mfma_ceiling(args)

@@ -11,7 +11,8 @@ from .sgemm import (ALGO, EXPORTS, LIB_PATH, PRECISION, SCRATCH_BYTES, SGEMM_ERR
                     TRANSPOSE_ALGO, SgemmError, gemm, load,
                     sgemm_f32, sgemm_f32_algo, sgemm_f32_arch_status, sgemm_f32_device_status, sgemm_f32_lowp, sgemm_f32_lowp_2pass, sgemm_f32_lowp_2pass_plan,
                     sgemm_f32_lowp_plan, sgemm_f32_lowp_ws,
-                    sgemm_f32_lowp_ws_plan, sgemm_f32_mfma_probe, sgemm_f32_plan,
+                    sgemm_f32_load_probe, sgemm_f32_lowp_ws_plan, sgemm_f32_mfma_probe, sgemm_f32_mfma_probe_lp,
+                    sgemm_f32_plan,
                     sgemm_f32_splitk, sgemm_f32_splitk_noalloc, sgemm_f32_splitk_plan, sgemm_f32_status_string, sgemm_f32_streamk,
                     sgemm_f32_streamk_plan, sgemm_f32_ws, sgemm_f32_ws_plan,
                     sgemm_f32_transpose, sgemm_f32_transpose_algo, sgemm_f32_transpose_plan,

@@ -1302,4 +1302,47 @@ int sgemm_f32_mfma_probe(int64_t workgroups, int64_t trips, float *sink, unsigne
     return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
 }
 
+int sgemm_f32_mfma_probe_lp(int precision, int zero_operands, int64_t workgroups, int64_t trips, float *sink,
+                            unsigned long long *clocks, void *stream)
+{
+    if ((precision != SGEMM_PREC_FP16 && precision != SGEMM_PREC_BF16) || (zero_operands != 0 && zero_operands != 1))
+        return SGEMM_ERR_INVALID_VALUE;
+    if (workgroups < 1 || workgroups > (int64_t{1} << 20) || trips < 1 || trips > (int64_t{1} << 24) ||
+        sink == nullptr || clocks == nullptr)
+        return SGEMM_ERR_INVALID_VALUE;
+    if (sgemm::overlaps(sink, workgroups * 256 * (int64_t)sizeof(float), clocks,
+                        workgroups * 2 * (int64_t)sizeof(unsigned long long)))
+        return SGEMM_ERR_ALIAS;
+    const int dev_status = sgemm::check_device();
+    if (dev_status != SGEMM_OK)
+        return dev_status;
+    const hipError_t e = sgemm::launch_mfma_lp_probe(precision == SGEMM_PREC_BF16, zero_operands == 1, (int)workgroups,
+                                                     (int)trips, sink, clocks, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
+}
+
+int sgemm_f32_load_probe(int waves, int depth, int64_t workgroups, const void *src, int64_t src_bytes,
+                         int64_t region_bytes, int64_t share, int64_t loads, unsigned long long *clocks, void *stream)
+{
+    if ((waves != 4 && waves != 8) || (depth != 1 && depth != 2 && depth != 4 && depth != 8))
+        return SGEMM_ERR_INVALID_VALUE;
+    if (workgroups < 1 || workgroups > (int64_t{1} << 16) || share < 1 || share > (int64_t{1} << 16) || loads < 1 ||
+        loads > (int64_t{1} << 24) || region_bytes < 1024 || region_bytes % 1024 != 0 ||
+        region_bytes > (int64_t{1} << 31) || src == nullptr || clocks == nullptr ||
+        (reinterpret_cast<uintptr_t>(src) & 15) != 0)
+        return SGEMM_ERR_INVALID_VALUE;
+    // The last region read: 8 * (((workgroups - 1) / 8) / share) + 7 at most.
+    const int64_t regions = 8 * (((workgroups - 1) / 8) / share) + 8;
+    if (src_bytes < 0 || regions > src_bytes / region_bytes)
+        return SGEMM_ERR_INVALID_VALUE;
+    if (sgemm::overlaps(src, regions * region_bytes, clocks, workgroups * 2 * (int64_t)sizeof(unsigned long long)))
+        return SGEMM_ERR_ALIAS;
+    const int dev_status = sgemm::check_device();
+    if (dev_status != SGEMM_OK)
+        return dev_status;
+    const hipError_t e = sgemm::launch_load_probe(waves, depth, (int)workgroups, src, region_bytes, (int)share,
+                                                  (int)loads, clocks, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
+}
+
 }  // extern "C"

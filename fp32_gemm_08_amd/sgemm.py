@@ -39,7 +39,7 @@ EXPORTS = ("sgemm_f32", "sgemm_f32_algo", "sgemm_f32_arch_status", "sgemm_f32_de
            "sgemm_f32_lowp_plan", "sgemm_f32_lowp_ws",
            "sgemm_f32_lowp_ws_plan", "sgemm_f32_plan",
            "sgemm_f32_splitk", "sgemm_f32_splitk_noalloc", "sgemm_f32_splitk_plan",
-           "sgemm_f32_mfma_probe", "sgemm_f32_status_string", "sgemm_f32_streamk", "sgemm_f32_streamk_plan", "sgemm_f32_transpose",
+           "sgemm_f32_load_probe", "sgemm_f32_mfma_probe", "sgemm_f32_mfma_probe_lp", "sgemm_f32_status_string", "sgemm_f32_streamk", "sgemm_f32_streamk_plan", "sgemm_f32_transpose",
            "sgemm_f32_transpose_algo", "sgemm_f32_transpose_plan", "sgemm_f32_version", "sgemm_f32_ws",
            "sgemm_f32_ws_plan")
 
@@ -121,6 +121,10 @@ def load():
         lib.sgemm_f32_version.argtypes = []
         lib.sgemm_f32_mfma_probe.restype = ci
         lib.sgemm_f32_mfma_probe.argtypes = [i64, i64, vp, vp, vp]
+        lib.sgemm_f32_mfma_probe_lp.restype = ci
+        lib.sgemm_f32_mfma_probe_lp.argtypes = [ci, ci, i64, i64, vp, vp, vp]
+        lib.sgemm_f32_load_probe.restype = ci
+        lib.sgemm_f32_load_probe.argtypes = [ci, ci, i64, vp, i64, i64, i64, i64, vp, vp]
         lib.sgemm_f32_arch_status.restype = ci
         lib.sgemm_f32_arch_status.argtypes = [ctypes.c_char_p]
         lib.sgemm_f32_device_status.restype = ci
@@ -302,6 +306,21 @@ def sgemm_f32_mfma_probe(workgroups, trips, sink, clocks, stream=0) -> int:
     MFMAs (4096 FLOP each) on register operands; clocks receives (shader
     cycles, 100 MHz ticks) per workgroup.  Returns the status code."""
     return load().sgemm_f32_mfma_probe(workgroups, trips, sink, clocks, stream)
+
+
+def sgemm_f32_mfma_probe_lp(precision, zero_operands, workgroups, trips, sink, clocks, stream=0) -> int:
+    """Measurement aid: as sgemm_f32_mfma_probe with 16-bit MFMAs (32768 FLOP
+    each; precision 1 = fp16, 2 = bf16) on random or all-zero operands."""
+    return load().sgemm_f32_mfma_probe_lp(precision, zero_operands, workgroups, trips, sink, clocks, stream)
+
+
+def sgemm_f32_load_probe(waves, depth, workgroups, src, src_bytes, region_bytes, share, loads, clocks,
+                         stream=0) -> int:
+    """Measurement aid: each workgroup's `waves` wavefronts stream `loads` 1 KB
+    direct global->LDS loads from its region of src, `depth` in flight;
+    clocks receives (shader cycles, 100 MHz ticks) per workgroup."""
+    return load().sgemm_f32_load_probe(waves, depth, workgroups, src, src_bytes, region_bytes, share, loads,
+                                       clocks, stream)
 
 
 def _check(status):

@@ -534,6 +534,55 @@ int sgemm_f32_device_status(void);
 int sgemm_f32_mfma_probe(int64_t workgroups, int64_t trips, float *sink, unsigned long long *clocks,
                          void *stream);
 
+/*
+ * Measurement aid, not part of the GEMM: the same chain on the 16-bit matrix
+ * cores behind the mixed-precision calls ("GPU矩阵乘法优化：共享内存Tiling技术实战",
+ * section 7.1: half-precision operands on the matrix cores).  Each wavefront
+ * issues trips * 8 v_mfma_f32_32x32x16_{f16,bf16} (32768 FLOP each; precision
+ * SGEMM_PREC_FP16 or SGEMM_PREC_BF16) over four accumulators, on eight operand
+ * pairs of random values in [-1, 1) rounded to 16 bits, or all zeros when
+ * zero_operands = 1 (how much the operands toggle decides the power the matrix
+ * cores draw, and with it the clock the part holds).  One call performs
+ * workgroups * 4 * trips * 8 * 32768 FLOP.  sink, clocks, the limits, the
+ * errors and the asynchrony are sgemm_f32_mfma_probe's; precision or
+ * zero_operands out of range: SGEMM_ERR_INVALID_VALUE.
+ */
+int sgemm_f32_mfma_probe_lp(int precision, int zero_operands, int64_t workgroups, int64_t trips, float *sink,
+                            unsigned long long *clocks, void *stream);
+
+/*
+ * Measurement aid, not part of the GEMM: the rate at which one CU stages
+ * global memory into LDS with the direct loads the MFMA kernels use
+ * (global_load_lds_dwordx4: 16 bytes per lane, 1 KB per wavefront instruction,
+ * no registers), with nothing else running.  The tiled kernels' pages put a
+ * kernel's time in its loads and their latency ("GPU矩阵乘法优化：共享内存Tiling
+ * 技术实战", section 3.2, double buffering hides the load latency); this gives
+ * that stream's own ceiling.  `workgroups` workgroups of `waves` wavefronts
+ * (4 or 8); each workgroup claims 100 KB of LDS, so one runs per CU.
+ * Workgroup w reads the region g = w % 8 + 8 * ((w / 8) / share) of
+ * `region_bytes` bytes at src + g * region_bytes (workgroups are dealt to the
+ * eight XCDs in turn, so `share` workgroups of one XCD read each region, as
+ * the tiles of a GEMM share operand panels); its wavefront v issues `loads`
+ * loads, the j-th taking the region's 1 KB chunk (j * waves + v) modulo
+ * region_bytes / 1024, and keeps at most `depth` (1, 2, 4 or 8) in flight.  The
+ * data land in LDS and are dropped.  Wavefront 0 writes the elapsed shader
+ * cycles (all of the workgroup's loads landed) to clocks[2w] and the 100 MHz
+ * ticks to clocks[2w+1]: one workgroup moves loads * waves * 1024 bytes.
+ *
+ * src: DEVICE buffer of src_bytes bytes, 16-byte aligned, owned by the caller
+ * and only read; it must hold every region read,
+ * (8 * (((workgroups - 1) / 8) / share) + 8) * region_bytes bytes.  clocks:
+ * DEVICE buffer of workgroups * 2 uint64, not overlapping those regions
+ * (SGEMM_ERR_ALIAS).  workgroups in 1..2^16, share in 1..2^16, loads in
+ * 1..2^24, region_bytes a multiple of 1024 in 1024..2^31, else
+ * SGEMM_ERR_INVALID_VALUE (checked before any HIP call).  Enqueued on
+ * `stream`; SGEMM_ERR_NO_DEVICE / SGEMM_ERR_UNSUPPORTED_ARCH /
+ * SGEMM_ERR_LAUNCH as sgemm_f32.
+ */
+int sgemm_f32_load_probe(int waves, int depth, int64_t workgroups, const void *src, int64_t src_bytes,
+                         int64_t region_bytes, int64_t share, int64_t loads, unsigned long long *clocks,
+                         void *stream);
+
 #ifdef __cplusplus
 }
 #endif

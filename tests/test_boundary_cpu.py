@@ -240,6 +240,50 @@ def test_mfma_probe_rejects_bad_arguments(wg, trips, sink, clocks, status):
     assert lib.sgemm_f32_mfma_probe(wg, trips, sink, clocks, 0) == status
 
 
+@pytest.mark.parametrize("prec,zero,wg,trips,sink,clocks,status", [
+    (0, 0, 4, 10, PA, PB, INVALID), (3, 0, 4, 10, PA, PB, INVALID), (2, 2, 4, 10, PA, PB, INVALID),
+    (2, -1, 4, 10, PA, PB, INVALID), (1, 0, 0, 10, PA, PB, INVALID), (2, 1, (1 << 20) + 1, 10, PA, PB, INVALID),
+    (2, 0, 4, 0, PA, PB, INVALID), (1, 1, 4, (1 << 24) + 1, PA, PB, INVALID),
+    (2, 0, 4, 10, 0, PB, INVALID), (2, 0, 4, 10, PA, 0, INVALID),
+    (2, 0, 4, 10, PA, PA + 4 * 256 * 4 - 8, ALIAS),
+])
+def test_mfma_probe_lp_rejects_bad_arguments(prec, zero, wg, trips, sink, clocks, status):
+    assert lib.sgemm_f32_mfma_probe_lp(prec, zero, wg, trips, sink, clocks, 0) == status
+
+
+MiB = 1 << 20
+
+
+@pytest.mark.parametrize("waves,depth,wg,src,src_bytes,region,share,loads,clocks,status", [
+    (2, 4, 256, PA, 1 << 30, 4 * MiB, 1, 512, PB, INVALID),       # 4 or 8 wavefronts
+    (8, 3, 256, PA, 1 << 30, 4 * MiB, 1, 512, PB, INVALID),       # 1, 2, 4 or 8 in flight
+    (8, 16, 256, PA, 1 << 30, 4 * MiB, 1, 512, PB, INVALID),
+    (8, 4, 0, PA, 1 << 30, 4 * MiB, 1, 512, PB, INVALID),
+    (8, 4, (1 << 16) + 1, PA, 1 << 40, 1024, 1, 512, PB, INVALID),
+    (8, 4, 256, PA, 1 << 30, 4 * MiB, 0, 512, PB, INVALID),
+    (8, 4, 256, PA, 1 << 30, 4 * MiB, 1, 0, PB, INVALID),
+    (8, 4, 256, PA, 1 << 30, 4 * MiB, 1, (1 << 24) + 1, PB, INVALID),
+    (8, 4, 256, PA, 1 << 30, 1000, 1, 512, PB, INVALID),          # whole 1 KB chunks
+    (8, 4, 256, PA, 1 << 40, 1 << 32, 1, 512, PB, INVALID),       # region above 2^31
+    (8, 4, 256, PA + 4, 1 << 30, 4 * MiB, 1, 512, PB, INVALID),   # 16-byte aligned source
+    (8, 4, 256, 0, 1 << 30, 4 * MiB, 1, 512, PB, INVALID),
+    (8, 4, 256, PA, 1 << 30, 4 * MiB, 1, 512, 0, INVALID),
+    (8, 4, 256, PA, (1 << 30) - 1, 4 * MiB, 1, 512, PB, INVALID),  # 256 regions of 4 MiB do not fit
+    (8, 4, 256, PA, 256 * MiB, 4 * MiB, 4, 512, PB, OK),          # 64 regions: fits (host check only)
+    (8, 4, 256, PA, 256 * MiB - 1, 4 * MiB, 4, 512, PB, INVALID),
+    (8, 4, 9, PA, 16 * 1024, 1024, 1, 1, PB, OK),                 # workgroups 8 and 0 share region 8's row
+    (8, 4, 9, PA, 15 * 1024, 1024, 1, 1, PB, INVALID),
+    (8, 4, 256, PA, 1 << 30, 4 * MiB, 1, 512, PA + (1 << 29), ALIAS),   # clocks inside the regions read
+])
+def test_load_probe_rejects_bad_arguments(waves, depth, wg, src, src_bytes, region, share, loads, clocks, status):
+    st = lib.sgemm_f32_load_probe(waves, depth, wg, src, src_bytes, region, share, loads, clocks, 0)
+    if status == OK:
+        # the arguments pass every host check; what follows is the device check
+        assert st not in (INVALID, ALIAS)
+    else:
+        assert st == status
+
+
 _OVERRIDE_CHILD = r"""
 import json, sys
 sys.path.insert(0, sys.argv[1])

@@ -65,6 +65,9 @@ for name, algo in lib.TRANSPOSE_ALGO.items():
     calls["transpose_" + name] = lib.sgemm_f32_transpose_algo(algo, 300, 200, PA, 200, PB, 300, 0)
 calls["transpose"] = lib.sgemm_f32_transpose(300, 200, PA, 200, PB, 300, 0)
 calls["probe"] = lib.sgemm_f32_mfma_probe(4, 4, PA, PB, 0)
+for p in (1, 2):
+    calls[f"probe_lp_{p}"] = lib.sgemm_f32_mfma_probe_lp(p, 0, 4, 4, PA, PB, 0)
+calls["load_probe"] = lib.sgemm_f32_load_probe(8, 4, 256, PA, 1 << 30, 4 << 20, 1, 512, PB, 0)
 bad = {k: v for k, v in calls.items() if v != 3}
 print("BAD", bad if bad else "", len(calls))
 """
