@@ -181,15 +181,18 @@ __global__ __launch_bounds__(Q::NT) void lp16_gemm_kernel(Lp16Args g)
     // all earlier LDS reads and waits only for the newer ones.
     const int nk = g.Kp / QK;
     constexpr int NF = Q::FM * Q::FN;
-    // With 8 wavefronts, those with wave bit 1 set request their share of a
+    // With 16 wavefronts, those with wave bit 3 set request their share of a
     // stage after the step's last MFMAs instead of right after the barrier,
-    // so the CU's address unit does not take all 8 wavefronts' loads at once
-    // (measured on MI355X, bf16 two-pass step: 4096^3 867.5 -> 878.8 TFLOP/s,
-    // 8192^3 1034 -> 1039).  The request still comes before the next wait, so
-    // the count of loads in flight there is unchanged.  The LDS-poisoning
-    // build poisons a stage with a barrier inside `issue`, which every
-    // wavefront must reach at the same point: it keeps one issue point.
-    const bool late = !kPoisonLds && Q::NT == 512 && (w & 2) != 0;
+    // so the CU's address unit does not take all the wavefronts' loads at
+    // once (measured on MI355X, GEMM pass alone on the 16-wavefront layout:
+    // 4096^3 123.1-124.1 -> 120.8-121.4 us against bits 0 or 2 or none; with
+    // 8 wavefronts of 64 x 128, bit 1 had taken the two-pass step from 867.5
+    // to 878.8 TFLOP/s).  The request
+    // still comes before the next wait, so the count of loads in flight there
+    // is unchanged.  The LDS-poisoning build poisons a stage with a barrier
+    // inside `issue`, which every wavefront must reach at the same point: it
+    // keeps one issue point.
+    const bool late = !kPoisonLds && Q::NT == 1024 && (w & 8) != 0;
 #pragma unroll
     for (int st = 0; st < Q::S - 1; ++st)
         issue(min(st, nk - 1), st);
@@ -351,7 +354,17 @@ __global__ __launch_bounds__(256) void lp16_round_transpose(const float *B, int6
 
 }  // namespace
 
-typedef QGeo<256, 256, 4, 2, 4> QL;  // 8 wavefronts of 64 x 128, 4 stages (128 KB)
+// The 256 x 256 tile runs 16 wavefronts of 64 x 64 (four on each SIMD, 108
+// VGPRs each), where 8 wavefronts of 64 x 128 (two per SIMD, 191 VGPRs) read
+// a quarter fewer fragment bytes per FLOP from the LDS: the LDS has the
+// bandwidth to spare (a CU reads over 300 bytes per cycle from it), and the
+// second pair of wavefronts on each SIMD covers the fragment-read and barrier
+// waits that held the matrix cores at half their rate.  Measured on MI355X
+// (GEMM pass alone, bf16, same bits): 4096^3 120.1 -> 116.4 us, 6144^3 465.9 ->
+// 453.5, 16384 x 4096 x 1024 166.9 -> 154.0, 4096 x 4096 x 1024 44.5 -> 38.9,
+// 8192^3 level (884-905 us both).  On the 128 x 128 tile 8 wavefronts of
+// 64 x 32 gained at K <= 2048 and lost 3-6% at K = 4096-8192, so it keeps 4.
+typedef QGeo<256, 256, 4, 4, 4> QL;  // 16 wavefronts of 64 x 64, 4 stages (128 KB)
 typedef QGeo<128, 128, 2, 2, 4> QS;  // 4 wavefronts of 64 x 64, 4 stages (64 KB)
 
 template <class Q>

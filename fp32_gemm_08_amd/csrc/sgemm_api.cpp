@@ -333,8 +333,8 @@ const char *kernel_label(int kid)
     case KID_MFMA_LP_BF16: return "mfma_lp_bf16_256x256x32_w4x2";
     case KID_MFMA_LP_F16_S: return "mfma_lp_f16_64x64x32_w2x1";
     case KID_MFMA_LP_BF16_S: return "mfma_lp_bf16_64x64x32_w2x1";
-    case KID_LP16_F16: return "lp16_f16_256x256x32_w4x2_s4 (+ rounding pass)";
-    case KID_LP16_BF16: return "lp16_bf16_256x256x32_w4x2_s4 (+ rounding pass)";
+    case KID_LP16_F16: return "lp16_f16_256x256x32_w4x4_s4 (+ rounding pass)";
+    case KID_LP16_BF16: return "lp16_bf16_256x256x32_w4x4_s4 (+ rounding pass)";
     case KID_LP16_F16_S: return "lp16_f16_128x128x32_w2x2_s4 (+ rounding pass)";
     case KID_LP16_BF16_S: return "lp16_bf16_128x128x32_w2x2_s4 (+ rounding pass)";
     case KID_TRANSPOSE_NAIVE: return "transpose_naive_64x16";
