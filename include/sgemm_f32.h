@@ -19,7 +19,9 @@
  *   C      M x N,  element (i,j) at C[i*ldc + j],  ldc >= max(1, N)
  *
  * Ownership: A, B and C are DEVICE pointers owned by the caller.  The library
- * never allocates, frees, copies or synchronises, and uses no workspace.
+ * never allocates, frees, copies or synchronises.  The plain calls use no memory
+ * beyond their operands; the workspace calls below take a caller-owned
+ * workspace, and sgemm_f32_splitk_noalloc a static array of the library.
  *
  * Asynchrony: a call validates its arguments on the host, enqueues its kernel on
  * `stream` (a hipStream_t; NULL means the null stream) and returns.  Faults inside
@@ -53,8 +55,10 @@
  *                             case of section 6.2 of the first page);
  *   SGEMM_ERR_LAUNCH          the launch was rejected (hipGetLastError after it).
  *
- * Thread safety: calls are reentrant; the only shared state is a per-device
- * architecture cache filled once.
+ * Thread safety: calls are reentrant; the only shared host state is a
+ * per-device architecture cache filled once and, for sgemm_f32_splitk_noalloc,
+ * a mutex-guarded per-device table of its scratch address (that call's device
+ * scratch itself is shared by all its calls on a GPU; see there).
  */
 #ifndef SGEMM_F32_H
 #define SGEMM_F32_H
