@@ -284,6 +284,22 @@ def test_load_probe_rejects_bad_arguments(waves, depth, wg, src, src_bytes, regi
         assert st == status
 
 
+@pytest.mark.parametrize("wg,share", [(1, 1), (7, 1), (8, 1), (9, 1), (256, 1), (256, 4), (256, 32), (257, 3),
+                                      (1000, 7), (65536, 1), (65536, 65536), (300, 300)])
+def test_load_probe_regions_cover_every_read(wg, share):
+    """Replay of the load probe's addressing: workgroup b reads region b % 8 + 8 * ((b / 8) / share),
+    chunks 0 .. region/1024 - 1 of it.  The host check asks for (8 * (((wg - 1) / 8) / share) + 8)
+    regions; every region a workgroup reads must lie inside them, that size must pass and one byte
+    less must be refused."""
+    region = 1024
+    last = max(b % 8 + 8 * ((b // 8) // share) for b in range(wg))
+    regions = 8 * (((wg - 1) // 8) // share) + 8
+    assert last < regions                     # every region read lies inside what the host asks for
+    ok = lib.sgemm_f32_load_probe(8, 4, wg, PA, regions * region, region, share, 1, PB, 0)
+    assert ok not in (INVALID, ALIAS)         # exactly that much passes the host checks
+    assert lib.sgemm_f32_load_probe(8, 4, wg, PA, regions * region - 1, region, share, 1, PB, 0) == INVALID
+
+
 _OVERRIDE_CHILD = r"""
 import json, sys
 sys.path.insert(0, sys.argv[1])
