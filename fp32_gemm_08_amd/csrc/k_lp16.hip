@@ -362,10 +362,19 @@ __global__ __launch_bounds__(256) void lp16_round_transpose(const float *B, int6
 // waits that held the matrix cores at half their rate.  Measured on MI355X
 // (GEMM pass alone, bf16, same bits): 4096^3 120.1 -> 116.4 us, 6144^3 465.9 ->
 // 453.5, 16384 x 4096 x 1024 166.9 -> 154.0, 4096 x 4096 x 1024 44.5 -> 38.9,
-// 8192^3 level (884-905 us both).  On the 128 x 128 tile 8 wavefronts of
-// 64 x 32 gained at K <= 2048 and lost 3-6% at K = 4096-8192, so it keeps 4.
-typedef QGeo<256, 256, 4, 4, 4> QL;  // 16 wavefronts of 64 x 64, 4 stages (128 KB)
-typedef QGeo<128, 128, 2, 2, 4> QS;  // 4 wavefronts of 64 x 64, 4 stages (64 KB)
+// 8192^3 level (884-905 us both).
+//
+// The 128 x 128 tile runs 8 wavefronts of 64 x 32 (two per SIMD; 2 workgroups
+// per CU) up to K = 3072 and 4 wavefronts of 64 x 64 above: measured on
+// MI355X (GEMM pass alone, bf16, same bits), 8 wavefronts took 2048 x 2048 x K
+// from 15.9 to 12.7 us at K = 512, 20.2 -> 17.3 at 1024, 24.1 -> 21.9 at 1536,
+// 28.2 -> 26.5 at 2048, 37.2 -> 35.3 at 3072, 1024^3 18.3 -> 15.2; level at
+// K = 2560 and 4096; slower at 1024 x 1024 x 4096 (39.1 -> 40.3) and
+// 2048 x 2048 x 8192 (73.9 -> 78.7).
+typedef QGeo<256, 256, 4, 4, 4> QL;   // 16 wavefronts of 64 x 64, 4 stages (128 KB)
+typedef QGeo<128, 128, 2, 4, 4> QS8;  // 8 wavefronts of 64 x 32, 4 stages (64 KB): K <= kQs8MaxK
+typedef QGeo<128, 128, 2, 2, 4> QS;   // 4 wavefronts of 64 x 64, 4 stages (64 KB): longer K
+constexpr int64_t kQs8MaxK = 3072;    // padded K
 
 template <class Q>
 static void launch_q(const Lp16Args &g, bool bf16, hipStream_t s)
@@ -452,6 +461,8 @@ hipError_t launch_lp16(const GemmArgs &a, bool large, bool bf16, bool transB, vo
     g.tiles_n = (int)(Np / t.bn);
     if (large)
         launch_q<QL>(g, bf16, s);
+    else if (Kp <= kQs8MaxK)
+        launch_q<QS8>(g, bf16, s);
     else
         launch_q<QS>(g, bf16, s);
     return hipGetLastError();

@@ -335,8 +335,8 @@ const char *kernel_label(int kid)
     case KID_MFMA_LP_BF16_S: return "mfma_lp_bf16_64x64x32_w2x1";
     case KID_LP16_F16: return "lp16_f16_256x256x32_w4x4_s4 (+ rounding pass)";
     case KID_LP16_BF16: return "lp16_bf16_256x256x32_w4x4_s4 (+ rounding pass)";
-    case KID_LP16_F16_S: return "lp16_f16_128x128x32_w2x2_s4 (+ rounding pass)";
-    case KID_LP16_BF16_S: return "lp16_bf16_128x128x32_w2x2_s4 (+ rounding pass)";
+    case KID_LP16_F16_S: return "lp16_f16_128x128x32_w2x4_s4 up to K = 3072, else w2x2 (+ rounding pass)";
+    case KID_LP16_BF16_S: return "lp16_bf16_128x128x32_w2x4_s4 up to K = 3072, else w2x2 (+ rounding pass)";
     case KID_TRANSPOSE_NAIVE: return "transpose_naive_64x16";
     case KID_TRANSPOSE_LDS_PAD: return "transpose_lds_128x128_pad1";
     case KID_TRANSPOSE_LDS_NOPAD: return "transpose_lds_128x128_pad0";

@@ -125,7 +125,10 @@ def test_configs_sampled(prec, name):
 @pytest.mark.parametrize("prec", PRECS)
 @pytest.mark.parametrize("shape", [(257, 255, 33, False, dict(lda=35)), (300, 270, 131, True, dict(ldb=140)),
                                    (513, 1, 700, False, {}), (1, 700, 513, True, {}), (256, 256, 32, False, {}),
-                                   (1000, 1017, 999, False, {}), (2049, 2051, 517, True, {}), (64, 64, 1, False, {})])
+                                   (1000, 1017, 999, False, {}), (2049, 2051, 517, True, {}), (64, 64, 1, False, {}),
+                                   # the 128 x 128 tile's two layouts, on both sides of K = 3072
+                                   (257, 255, 3072, False, dict(lda=3075)), (96, 200, 3073, True, {}),
+                                   (130, 260, 4100, True, dict(ldb=4103))])
 def test_edges_and_unaligned(prec, shape, tile):
     M, N, K, tb, extra = shape
     case = make_case(M, N, K, trans_b=tb, alpha=-0.75, beta=0.5, seed=M + N + K, **extra)

@@ -143,8 +143,8 @@ def test_transposing_rounding_matches_row_rounding_of_bt(K, N, Np):
     assert np.array_equal(round_transpose(K, N, Np, Kp), round_rows(N, K, Np, Kp))
 
 
-@pytest.mark.parametrize("geo", [(256, 256, 4, 4), (256, 256, 4, 2), (128, 128, 2, 2)],
-                         ids=["256x256_w4x4", "256x256_w4x2", "128x128_w2x2"])
+@pytest.mark.parametrize("geo", [(256, 256, 4, 4), (256, 256, 4, 2), (128, 128, 2, 4), (128, 128, 2, 2)],
+                         ids=["256x256_w4x4", "256x256_w4x2", "128x128_w2x4", "128x128_w2x2"])
 def test_gemm_staging_and_fragments(geo):
     BM, BN, WGM, WGN = geo
     M, N, K = BM + 17, BN + 3, 70            # edge rows and columns, a k tail
