@@ -260,11 +260,22 @@ __global__ __launch_bounds__(Q::NT) void lp16_gemm_kernel(Lp16Args g)
     }
 }
 
+// Four FP32 operand values, 16-byte aligned; NT: a streaming (non-temporal)
+// load, which does not keep the line in the caches for a later reuse.
+template <bool NT>
+__device__ __forceinline__ lp_f32x4 lp16_load4(const float *p)
+{
+    if constexpr (NT)
+        return __builtin_nontemporal_load(reinterpret_cast<const lp_f32x4 *>(p));
+    else
+        return *reinterpret_cast<const lp_f32x4 *>(p);
+}
+
 // Rounding pass, k-contiguous source (A, or op(B) = B^T stored N x K): item i
 // rounds the 8 values at k = 32*slab + 8*c of row r, i = (slab*Rp + r)*4 + c,
 // so consecutive items write consecutive 16-byte chunks of the slab layout;
 // zero past R rows and K columns.
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, bool NTL>
 __global__ __launch_bounds__(256) void lp16_round_rows(const float *src, int64_t ld, int R, int K, void *dst_,
                                                        int Rp, int Kp)
 {
@@ -280,8 +291,8 @@ __global__ __launch_bounds__(256) void lp16_round_rows(const float *src, int64_t
         float x[8];
         const float *p = src + (int64_t)r * ld + k;
         if (VEC && r < R && k + 8 <= K) {
-            const lp_f32x4 x0 = *reinterpret_cast<const lp_f32x4 *>(p);
-            const lp_f32x4 x1 = *reinterpret_cast<const lp_f32x4 *>(p + 4);
+            const lp_f32x4 x0 = lp16_load4<NTL>(p);
+            const lp_f32x4 x1 = lp16_load4<NTL>(p + 4);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 x[q] = x0[q];
@@ -303,7 +314,7 @@ __global__ __launch_bounds__(256) void lp16_round_rows(const float *src, int64_t
 // Rounding pass for op(B) = B (stored K x N): element (n, k) of the slab layout
 // <- r(B[k][n]) through a 64 x 64 LDS tile (rows read along n, written along
 // k), zero past K and N.
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, bool NTL>
 __global__ __launch_bounds__(256) void lp16_round_transpose(const float *B, int64_t ldb, int K, int N, void *dst_,
                                                             int Np, int Kp)
 {
@@ -321,7 +332,7 @@ __global__ __launch_bounds__(256) void lp16_round_transpose(const float *B, int6
         const float *p = B + (int64_t)k * ldb + n;
         float x[4];
         if (VEC && k < K && n + 4 <= N) {
-            const lp_f32x4 v = *reinterpret_cast<const lp_f32x4 *>(p);
+            const lp_f32x4 v = lp16_load4<NTL>(p);
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 x[q] = v[q];
@@ -388,23 +399,52 @@ static void launch_q(const Lp16Args &g, bool bf16, hipStream_t s)
 
 static int64_t up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
-// R x K k-contiguous FP32 rows -> Rp x Kp 16-bit rows.
-static void round_rows(const float *src, int64_t ld, int R, int K, void *dst, int64_t Rp, int64_t Kp, bool bf16,
-                       bool vec, hipStream_t s)
+// The rounding passes read the FP32 operands with streaming loads when A,
+// op(B) and C together exceed kStreamBytes, a working set that the 256 MB
+// Infinity Cache does not keep from one call to the next: the loads then pass
+// by the caches instead of evicting the 16-bit operands that the GEMM pass
+// reads right after.  Below it, ordinary loads keep the operands in the cache
+// for a repeated call.  Measured on MI355X (bf16, full two-pass step, same
+// bits): 16384 x 4096 x 1024 188.7 -> 176.6 us, 8192^3 1071 -> 1050, 6144^3
+// 541 -> 535; with streaming loads at 4096^3 (192 MB) 152.1 -> 157.4 us.
+constexpr int64_t kStreamBytes = int64_t{200} << 20;
+
+template <bool BF16>
+static void round_rows_t(const float *src, int64_t ld, int R, int K, void *dst, int64_t Rp, int64_t Kp, bool vec,
+                         bool nt, hipStream_t s)
 {
     const int64_t chunks = Rp * (Kp / 8);
     const unsigned grid = (unsigned)std::min<int64_t>((chunks + 255) / 256, 8192);
-    if (bf16) {
-        if (vec)
-            lp16_round_rows<true, true><<<grid, 256, 0, s>>>(src, ld, R, K, dst, (int)Rp, (int)Kp);
-        else
-            lp16_round_rows<true, false><<<grid, 256, 0, s>>>(src, ld, R, K, dst, (int)Rp, (int)Kp);
-    } else {
-        if (vec)
-            lp16_round_rows<false, true><<<grid, 256, 0, s>>>(src, ld, R, K, dst, (int)Rp, (int)Kp);
-        else
-            lp16_round_rows<false, false><<<grid, 256, 0, s>>>(src, ld, R, K, dst, (int)Rp, (int)Kp);
-    }
+    if (!vec)
+        lp16_round_rows<BF16, false, false><<<grid, 256, 0, s>>>(src, ld, R, K, dst, (int)Rp, (int)Kp);
+    else if (nt)
+        lp16_round_rows<BF16, true, true><<<grid, 256, 0, s>>>(src, ld, R, K, dst, (int)Rp, (int)Kp);
+    else
+        lp16_round_rows<BF16, true, false><<<grid, 256, 0, s>>>(src, ld, R, K, dst, (int)Rp, (int)Kp);
+}
+
+// R x K k-contiguous FP32 rows -> Rp x Kp 16-bit rows.
+static void round_rows(const float *src, int64_t ld, int R, int K, void *dst, int64_t Rp, int64_t Kp, bool bf16,
+                       bool vec, bool nt, hipStream_t s)
+{
+    if (bf16)
+        round_rows_t<true>(src, ld, R, K, dst, Rp, Kp, vec, nt, s);
+    else
+        round_rows_t<false>(src, ld, R, K, dst, Rp, Kp, vec, nt, s);
+}
+
+// K x N FP32 op(B) = B -> Np x Kp 16-bit rows of B^T.
+template <bool BF16>
+static void round_transpose_t(const float *B, int64_t ldb, int K, int N, void *dst, int64_t Np, int64_t Kp, bool vec,
+                              bool nt, hipStream_t s)
+{
+    const dim3 grid((unsigned)(Np / 64), (unsigned)((Kp + 63) / 64));
+    if (!vec)
+        lp16_round_transpose<BF16, false, false><<<grid, 256, 0, s>>>(B, ldb, K, N, dst, (int)Np, (int)Kp);
+    else if (nt)
+        lp16_round_transpose<BF16, true, true><<<grid, 256, 0, s>>>(B, ldb, K, N, dst, (int)Np, (int)Kp);
+    else
+        lp16_round_transpose<BF16, true, false><<<grid, 256, 0, s>>>(B, ldb, K, N, dst, (int)Np, (int)Kp);
 }
 
 TileShape lp16_tile_shape(bool large) { return large ? TileShape{QL::BM, QL::BN} : TileShape{QS::BM, QS::BN}; }
@@ -428,23 +468,15 @@ hipError_t launch_lp16(const GemmArgs &a, bool large, bool bf16, bool transB, vo
 
     const bool avec = (reinterpret_cast<uintptr_t>(a.A) & 15) == 0 && (a.lda & 3) == 0;
     const bool bvec = (reinterpret_cast<uintptr_t>(a.B) & 15) == 0 && (a.ldb & 3) == 0;
-    round_rows(a.A, a.lda, a.M, a.K, A16, Mp, Kp, bf16, avec, s);
-    if (transB) {
-        round_rows(a.B, a.ldb, a.N, a.K, B16, Np, Kp, bf16, bvec, s);
-    } else {
-        const dim3 grid((unsigned)(Np / 64), (unsigned)((Kp + 63) / 64));
-        if (bf16) {
-            if (bvec)
-                lp16_round_transpose<true, true><<<grid, 256, 0, s>>>(a.B, a.ldb, a.K, a.N, B16, (int)Np, (int)Kp);
-            else
-                lp16_round_transpose<true, false><<<grid, 256, 0, s>>>(a.B, a.ldb, a.K, a.N, B16, (int)Np, (int)Kp);
-        } else {
-            if (bvec)
-                lp16_round_transpose<false, true><<<grid, 256, 0, s>>>(a.B, a.ldb, a.K, a.N, B16, (int)Np, (int)Kp);
-            else
-                lp16_round_transpose<false, false><<<grid, 256, 0, s>>>(a.B, a.ldb, a.K, a.N, B16, (int)Np, (int)Kp);
-        }
-    }
+    const int64_t M = a.M, N = a.N, K = a.K;
+    const bool nt = 4 * (M * K + K * N + M * N) > kStreamBytes;
+    round_rows(a.A, a.lda, a.M, a.K, A16, Mp, Kp, bf16, avec, nt, s);
+    if (transB)
+        round_rows(a.B, a.ldb, a.N, a.K, B16, Np, Kp, bf16, bvec, nt, s);
+    else if (bf16)
+        round_transpose_t<true>(a.B, a.ldb, a.K, a.N, B16, Np, Kp, bvec, nt, s);
+    else
+        round_transpose_t<false>(a.B, a.ldb, a.K, a.N, B16, Np, Kp, bvec, nt, s);
     Lp16Args g;
     g.A16 = A16;
     g.B16 = B16;
