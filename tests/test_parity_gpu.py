@@ -180,6 +180,34 @@ def test_random_ragged_sweep(oracle_lib, algo):
         assert_parity(Dg[:, :N], D, S, K, f"sweep {M}x{N}x{K} t{t}/{algo}")
 
 
+def _hundreds_cases(n, seed):
+    """n seeded shapes, each side log-uniform in [1, 600], with random op(B), alpha, beta and 0-3 floats of
+    padding on every leading dimension."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        M, N, K = (int(round(np.exp(rng.uniform(0.0, np.log(600.0))))) for _ in range(3))
+        t = int(rng.integers(0, 2))
+        alpha = float(rng.choice([1.0, -0.5, 1.5]))
+        beta = float(rng.choice([0.0, 1.0, -0.5]))
+        pa, pb, pc = (int(p) for p in rng.integers(0, 4, 3))
+        out.append((M, N, K, t, alpha, beta, pa, pb, pc, 5000 + i))
+    return out
+
+
+def test_hundreds_of_random_shapes_auto(oracle_lib):
+    """The CUDA-SGEMM page's correctness habit (section 7): check a kernel against a CPU reference over
+    hundreds of random shapes.  200 seeded shapes through the AUTO path, every element against the
+    oracle, canaries around C."""
+    for (M, N, K, t, alpha, beta, pa, pb, pc, seed) in _hundreds_cases(200, 77):
+        case = make_case(M, N, K, trans_b=t, alpha=alpha, beta=beta, dist="uniform", seed=seed,
+                         lda=K + pa, ldb=(K if t else N) + pb, ldc=N + pc)
+        st, Dg = run_case(case, "auto")
+        assert st == 0
+        D, S = oracle_rows(oracle_lib, case)
+        assert_parity(Dg[:, :N], D, S, K, f"random {M}x{N}x{K} t{t} pads {pa},{pb},{pc}")
+
+
 @pytest.mark.parametrize("algo", ["mfma", "mfma_256", "mfma_128", "mfma_64", "mfma_32", "mfma_128x64", "regblock",
                                   "lds_tiled", "naive", "naive_wg"])
 def test_degenerate_shapes(oracle_lib, algo):
