@@ -113,6 +113,24 @@ def test_edges_and_unaligned(prec, shape):
     assert_lowp_parity(case, prec, D, what=f"{M}x{N}x{K}")
 
 
+def test_random_shapes_both_formats():
+    """100 seeded shapes (each side log-uniform in [1, 600], random op(B), alpha, beta and leading-dimension
+    padding), fp16 and bf16 in turn, against both bounds of the mixed-precision contract."""
+    rng = np.random.default_rng(91)
+    for i in range(100):
+        M, N, K = (int(round(np.exp(rng.uniform(0.0, np.log(600.0))))) for _ in range(3))
+        t = bool(rng.integers(0, 2))
+        alpha = float(rng.choice([1.0, -0.5, 1.5]))
+        beta = float(rng.choice([0.0, 1.0, -0.5]))
+        pa, pb, pc = (int(p) for p in rng.integers(0, 4, 3))
+        prec = PRECS[i % 2]
+        case = make_case(M, N, K, trans_b=t, alpha=alpha, beta=beta, seed=7000 + i, lda=K + pa,
+                         ldb=(K if t else N) + pb, ldc=N + pc)
+        st, D = run_lowp(case, prec)
+        assert st == 0
+        assert_lowp_parity(case, prec, D, what=f"random {M}x{N}x{K} t{int(t)}")
+
+
 @pytest.mark.parametrize("prec", PRECS)
 def test_misaligned_base(prec):
     case = make_case(400, 384, 260, seed=43)
