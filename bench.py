@@ -392,6 +392,50 @@ def probe_clock(lib, torch, dev, stream, workgroups=512, trips=2000, launches=3)
                       "the timed steps (each workgroup's wavefront 0)"}
 
 
+def sustained_ceiling(lib, torch, dev, stream, precision="fp32"):
+    """The matrix-core rate the device sustains with register operands only
+    (the library's probe: FP32 chains, or 16-bit chains on random operands),
+    measured after the timed steps: ~0.3 s of launches to let the clock settle
+    under that load, then launches between two events.  The published peak
+    assumes the full clock; under a 16-bit matrix-core load the part holds a
+    lower one, so this is the rate a kernel of the same type can reach."""
+    workgroups = 512
+    sink = torch.empty(workgroups * 256, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(workgroups * 2, dtype=torch.int64, device=dev)
+    if precision == "fp32":
+        trips, flop = 10000, workgroups * 10000 * MFMA_PROBE_FLOP_PER_TRIP
+
+        def launch():
+            return lib.sgemm_f32_mfma_probe(workgroups, trips, sink.data_ptr(), clocks.data_ptr(), stream.cuda_stream)
+    else:
+        prec = lib.PRECISION[precision]
+        trips, flop = 16000, workgroups * 16000 * LP_PROBE_FLOP_PER_TRIP
+
+        def launch():
+            return lib.sgemm_f32_mfma_probe_lp(prec, 0, workgroups, trips, sink.data_ptr(), clocks.data_ptr(),
+                                               stream.cuda_stream)
+    t_end = time.perf_counter() + 0.3
+    while time.perf_counter() < t_end:
+        for _ in range(4):
+            if launch() != 0:
+                return None
+        torch.cuda.synchronize()
+    n = 10
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        if launch() != 0:
+            return None
+    e1.record(stream)
+    torch.cuda.synchronize()
+    avg = e0.elapsed_time(e1) * 1e-3 / n
+    c = clocks.cpu().view(workgroups, 2).double()
+    return {"value": round(flop / avg / 1e12, 2), "unit": "TFLOP/s",
+            "shader_clock_mhz": round((100.0 * c[:, 0] / c[:, 1]).mean().item(), 1),
+            "source": f"the library's {'FP32' if precision == 'fp32' else precision} matrix-core probe "
+                      "(register operands, 512 workgroups), right after the timed steps"}
+
+
 def cu_scaling():
     """The 256 x 256 MFMA kernel with one tile per busy CU: M = 256 .. 4096
     (16 .. 256 tiles), N = K = 4096.  The same work per CU at every M, so a
@@ -1083,6 +1127,13 @@ def main():
     }
     traffic = read_traffic() if (args.config == "c4_4096" and not share and kid == 40) else None
     out["roofline"]["traffic"] = traffic
+    if mfma:
+        # context beside the published peak: the rate the chip sustains for this
+        # type of matrix-core work, and this kernel's fraction of it
+        ceil = sustained_ceiling(lib, torch, dev, stream, args.precision if lowp else "fp32")
+        if ceil is not None:
+            ceil["frac"] = round(achieved / ceil["value"], 4)
+            out["roofline"]["sustained_ceiling"] = ceil
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on a sample of rows for ~{args.cpu_seconds:.0f} s")
         out["cpu_baseline"] = cpu_baseline(case, D_host, args.cpu_seconds,
