@@ -187,11 +187,10 @@ __global__ __launch_bounds__(Q::NT) void lp16_gemm_kernel(Lp16Args g)
     // once (measured on MI355X, GEMM pass alone on the 16-wavefront layout:
     // 4096^3 123.1-124.1 -> 120.8-121.4 us against bits 0 or 2 or none; with
     // 8 wavefronts of 64 x 128, bit 1 had taken the two-pass step from 867.5
-    // to 878.8 TFLOP/s).  The request
-    // still comes before the next wait, so the count of loads in flight there
-    // is unchanged.  The LDS-poisoning build poisons a stage with a barrier
-    // inside `issue`, which every wavefront must reach at the same point: it
-    // keeps one issue point.
+    // to 878.8 TFLOP/s).  The request still comes before the next wait, so
+    // the count of loads in flight there is unchanged.  The LDS-poisoning
+    // build poisons a stage with a barrier inside `issue`, which every
+    // wavefront must reach at the same point: it keeps one issue point.
     const bool late = !kPoisonLds && Q::NT == 1024 && (w & 8) != 0;
 #pragma unroll
     for (int st = 0; st < Q::S - 1; ++st)
@@ -375,8 +374,9 @@ __global__ __launch_bounds__(256) void lp16_round_transpose(const float *B, int6
 // 453.5, 16384 x 4096 x 1024 166.9 -> 154.0, 4096 x 4096 x 1024 44.5 -> 38.9,
 // 8192^3 level (884-905 us both).
 //
-// The 128 x 128 tile runs 8 wavefronts of 64 x 32 (two per SIMD; 2 workgroups
-// per CU) up to K = 3072 and 4 wavefronts of 64 x 64 above: measured on
+// The 128 x 128 tile runs 8 wavefronts of 64 x 32 (with two workgroups on a
+// CU, four wavefronts per SIMD) up to K = 3072 and 4 wavefronts of 64 x 64
+// above: measured on
 // MI355X (GEMM pass alone, bf16, same bits), 8 wavefronts took 2048 x 2048 x K
 // from 15.9 to 12.7 us at K = 512, 20.2 -> 17.3 at 1024, 24.1 -> 21.9 at 1536,
 // 28.2 -> 26.5 at 2048, 37.2 -> 35.3 at 3072, 1024^3 18.3 -> 15.2; level at
