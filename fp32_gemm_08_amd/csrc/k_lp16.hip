@@ -385,6 +385,7 @@ __global__ __launch_bounds__(256) void lp16_round_transpose(const float *B, int6
 typedef QGeo<256, 256, 4, 4, 4> QL;   // 16 wavefronts of 64 x 64, 4 stages (128 KB)
 typedef QGeo<128, 128, 2, 4, 4> QS8;  // 8 wavefronts of 64 x 32, 4 stages (64 KB): K <= kQs8MaxK
 typedef QGeo<128, 128, 2, 2, 4> QS;   // 4 wavefronts of 64 x 64, 4 stages (64 KB): longer K
+static_assert(QL::NT <= 1024 && QS8::NT <= 1024 && QS::NT <= 1024, "the plan's launch-size check");
 constexpr int64_t kQs8MaxK = 3072;    // padded K
 
 template <class Q>

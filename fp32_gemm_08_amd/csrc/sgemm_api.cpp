@@ -887,7 +887,7 @@ int run_lowp(int precision, int64_t M, int64_t N, int64_t K, float alpha, const 
 
 // Two-pass mixed precision with a caller workspace: the one-pass call's
 // validation and quick returns; the two passes only where they measured
-// faster, with 256 x 256 tiles when there are at least 128 of them, else
+// faster, with 256 x 256 tiles when there are more than 128 of them, else
 // 128 x 128.  `bytes` is what the workspace must hold.
 struct Lp16Plan {
     Plan base;
@@ -924,15 +924,18 @@ Lp16Plan make_lp16_plan(bool forced, int tile_req, int precision, int64_t M, int
     if (!forced && !(flops >= 1e10 || (flops >= 1e9 && ragged)))
         return lp;
     const bool bf16 = precision == SGEMM_PREC_BF16;
-    // 256 x 256 tiles once they keep at least half the CUs busy, else 128 x 128
-    // (2560^3: 483 against 346 TFLOP/s; 3000^3: 478 against 458)
+    // 256 x 256 tiles once they keep more than half the CUs busy, else 128 x 128
+    // (2560^3: 483 against 346 TFLOP/s; 3000^3: 478 against 458; with the
+    // 16-wavefront 256 x 256 GEMM, 144 tiles (3072^3) 93.4 against 105.5 us,
+    // but exactly 128 (4096 x 2048 x 2048) 67.2 against 57.6 us)
     const TileShape tl = lp16_tile_shape(true);
-    lp.large = tile_req == 0 ? ceil_div(M, tl.bm) * ceil_div(N, tl.bn) >= 128 : tile_req == 256;
+    lp.large = tile_req == 0 ? ceil_div(M, tl.bm) * ceil_div(N, tl.bn) > 128 : tile_req == 256;
     const TileShape t = lp16_tile_shape(lp.large);
     const int64_t tiles = ceil_div(M, t.bm) * ceil_div(N, t.bn);
     // the rounding transpose of op(B) = B launches ceil(K / 64) workgroup rows
     // (a grid's y extent is at most 65535)
-    if (tiles * (lp.large ? 512 : 256) > kMaxWorkItems || ceil_div(K, 32) * 32 > std::numeric_limits<int>::max() ||
+    // (no layout of the two-pass GEMM launches more than 1024 work-items a workgroup)
+    if (tiles * 1024 > kMaxWorkItems || ceil_div(K, 32) * 32 > std::numeric_limits<int>::max() ||
         ceil_div(K, 64) > 65535) {
         if (forced) {
             lp.base.status = SGEMM_ERR_INVALID_VALUE;

@@ -76,7 +76,9 @@ def test_precision_table():
 
 @pytest.mark.parametrize("shape,want", [
     ((4096, 4096, 4096), ("two", True, (16, 16))),    # >= 1e10 FLOPs, 256 tiles of 256
-    ((3000, 3000, 3000), ("two", True, (12, 12))),    # 144 tiles of 256: at least half the CUs
+    ((3000, 3000, 3000), ("two", True, (12, 12))),    # 144 tiles of 256: more than half the CUs
+    ((4096, 2048, 2048), ("two", False, (32, 16))),   # exactly 128 tiles of 256: the 128 x 128 tile
+    ((4096, 2064, 2048), ("two", True, (16, 9))),     # 144 tiles of 256
     ((2560, 2560, 2560), ("two", False, (20, 20))),   # 100: the 128 x 128 tile
     ((2048, 2048, 2048), ("two", False, (16, 16))),
     ((1000, 1017, 999), ("two", False, (8, 8))),      # 2e9 FLOPs with edges and a k tail
