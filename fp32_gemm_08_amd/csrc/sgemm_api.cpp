@@ -919,9 +919,15 @@ Lp16Plan make_lp16_plan(bool forced, int tile_req, int precision, int64_t M, int
     // and on smaller products with edge tiles or a k tail, which the rounding
     // pass pads away (1000 x 1017 x 999: 65 against 46); below, the pass costs
     // more than it saves (1024^3: 77 against 117).
+    // From 4e9 FLOPs they also win where K >= min(M, N): the one-pass kernel's
+    // small tile then runs long k-loops (measured with the current kernels:
+    // 1024 x 1024 x 4096 79.3 against 51.5 us, 2048 x 1024 x 2048 43.5 against
+    // 35.8, 1280^3 29.4 against 27.8), while shallow products stay faster in
+    // one pass (2048 x 2048 x 1024 27.8 against 29.2, x 512 17.9 against 20.9).
     const double flops = 2.0 * (double)M * (double)N * (double)K;
     const bool ragged = (M % 64) != 0 || (N % 64) != 0 || (K % 32) != 0;
-    if (!forced && !(flops >= 1e10 || (flops >= 1e9 && ragged)))
+    const bool deep = flops >= 4e9 && K >= (M < N ? M : N);
+    if (!forced && !(flops >= 1e10 || deep || (flops >= 1e9 && ragged)))
         return lp;
     const bool bf16 = precision == SGEMM_PREC_BF16;
     // 256 x 256 tiles once they keep more than half the CUs busy, else 128 x 128

@@ -323,8 +323,9 @@ int sgemm_f32_lowp_ws(int precision, int64_t M, int64_t N, int64_t K, float alph
 /* Host-only query for sgemm_f32_lowp_ws: the kernel id (64/65: fp16/bf16 with
  * 256 x 256 tiles, chosen when there are more than 128 of them; 66/67: 128 x
  * 128 tiles; otherwise the one-pass call's id: the two passes run for products
- * of at least 1e10 FLOPs, or 1e9 when M or N is not a multiple of 64 or K of
- * 32, where they measured faster, and K <= 64 * 65535 = 4,194,240; longer K
+ * of at least 1e10 FLOPs, of at least 4e9 FLOPs with K >= min(M, N), or of 1e9
+ * when M or N is not a multiple of 64 or K of 32, where they measured faster,
+ * and K <= 64 * 65535 = 4,194,240; longer K
  * runs the one-pass call), the output tiles and the workspace bytes (0 when
  * the one-pass call runs).  Output pointers may be NULL. */
 int sgemm_f32_lowp_ws_plan(int precision, int64_t M, int64_t N, int64_t K, int transB, int *kernel_id,

@@ -83,7 +83,12 @@ def test_precision_table():
     ((2048, 2048, 2048), ("two", False, (16, 16))),
     ((1000, 1017, 999), ("two", False, (8, 8))),      # 2e9 FLOPs with edges and a k tail
     ((1024, 1024, 1024), ("one", False, (16, 16))),   # aligned and small: the one-pass call
-    ((1536, 1536, 1536), ("one", False, (24, 24))),
+    ((1536, 1536, 1536), ("two", False, (12, 12))),   # 7.2e9 FLOPs with K >= min(M, N)
+    ((1280, 1280, 1280), ("two", False, (10, 10))),   # 4.2e9, K = M = N
+    ((1024, 1024, 4096), ("two", False, (8, 8))),
+    ((2048, 2048, 1024), ("one", False, (32, 32))),   # 8.6e9 but shallow: one pass
+    ((2048, 2048, 512), ("one", False, (32, 32))),
+    ((1024, 1024, 1856), ("one", False, (16, 16))),   # 3.9e9 < 4e9: one pass
     ((100, 100, 100), ("one", False, (2, 2))),
 ])
 @pytest.mark.parametrize("prec", [1, 2])
